@@ -1,0 +1,65 @@
+"""CPU oracle for the paged KV cache and paged decode attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code, header, table
+or helper with the HIP library in ``paged_kv_cache_392_amd``; the two meet
+only through the seeded inputs of ``workloads.py``.
+
+It is written to be plain and slow and to be read against the three source
+pages, which are cited as
+
+* [p1] "KV Cache / PagedAttention / Flash Attention" overview,
+  chanyi.net.cn/article/49, sections 一 to 六;
+* [p2] practitioner notes on KV cache and vLLM, lqnn.cn/news/235768,
+  sections 1 to 5.3;
+* [p3] course notes "9.1 推理优化：KV Cache、PagedAttention 与 vLLM",
+  hdu-wiki.cn/courses/inference-kvcache-vllm, Q1 to Q4.
+
+Floating point is fp64 (the pages fix no precision). Every function names the
+passage it follows. Where the pages are silent the reading taken is stated in
+the function's docstring.
+
+Modules
+-------
+sizes      KV-cache byte counts (the size formula and its table).
+allocator  block pool: free list, refcounts, block tables, fork, COW.
+cache      the paged K/V store: append, block copy, gather.
+attention  decode attention by definition (NumPy fp64) and by brute force.
+quant      int8 absmax quantiser with one scale per (block, KV head).
+
+Pinning status: every function here is pinned by a ``-m "not gpu"`` test
+against values printed on the pages, closed forms, invariants, brute force or
+a library routine, with one exception: the rounding of exact ties in the
+int8 quantiser (round-half-to-even) is a choice the pages do not fix, and is
+"parity unpinned".
+"""
+
+from .sizes import (
+    BLOCK_TOKENS,
+    kv_bytes_per_token,
+    kv_cache_bytes,
+    pool_bytes,
+)
+from .allocator import RefAllocator, NoBlocks, UnknownSeq
+from .cache import RefCache
+from .attention import decode, decode_seq_head, brute_decode, gather
+from .quant import quantize_block_int8, quantize_pool_int8, dequantize_int8
+
+__all__ = [
+    "BLOCK_TOKENS",
+    "kv_bytes_per_token",
+    "kv_cache_bytes",
+    "pool_bytes",
+    "RefAllocator",
+    "NoBlocks",
+    "UnknownSeq",
+    "RefCache",
+    "decode",
+    "decode_seq_head",
+    "brute_decode",
+    "gather",
+    "quantize_block_int8",
+    "quantize_pool_int8",
+    "dequantize_int8",
+]

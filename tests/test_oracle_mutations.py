@@ -1,0 +1,150 @@
+"""Planted mistakes: each test puts one plausible bug into the oracle (on the
+CPU, through monkeypatch) and checks that at least one pin catches it. This
+shows the pins constrain every part of the oracle, not only its happy path."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as att
+import oracle.allocator as alc
+import oracle.quant as qnt
+import oracle.sizes as sz
+import workloads
+from test_oracle_allocator import hand_trace, random_ops, check_invariants
+from test_oracle_decode import (check_against_brute, check_against_sdpa,
+                                check_gather_matches_contiguous,
+                                test_shared_prefix_equals_private_copy)
+from test_oracle_quant import check_error_bound
+from test_oracle_sizes import check_printed_sizes
+
+
+def _decode_with(mapping=None, scale_override=None, sign=1.0, swap_kv=False):
+    def decode(cache, q, block_tables, context_lens, layer=0, scale=None):
+        q = np.asarray(q)
+        B, Hq, D = q.shape
+        Hkv = cache.kv_heads
+        G = Hq // Hkv
+        sc = 1.0 / math.sqrt(D) if scale is None else scale
+        if scale_override is not None:
+            sc = scale_override
+        out = np.empty((B, Hq, D))
+        for b in range(B):
+            n = int(context_lens[b])
+            for h in range(Hq):
+                g = mapping(h, G, Hkv) if mapping else h // G
+                Kc = att.gather(cache.K, layer, block_tables[b], n, g, cache.scales, 0)
+                Vc = att.gather(cache.V, layer, block_tables[b], n, g, cache.scales, 1)
+                if swap_kv:
+                    Kc, Vc = Vc, Kc
+                s = sign * (Kc @ q[b, h].astype(np.float64)) * sc
+                e = np.exp(s - s.max())
+                out[b, h] = (e / e.sum()) @ Vc
+        return out
+    return decode
+
+
+def test_interleaved_head_mapping_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "decode", _decode_with(mapping=lambda h, G, Hkv: h % Hkv))
+    with pytest.raises(AssertionError):
+        check_against_sdpa(workloads.c1_tiny())
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "decode", _decode_with(scale_override=1.0))
+    with pytest.raises(AssertionError):
+        check_against_brute(workloads.c1_tiny())
+
+
+def test_sign_flip_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "decode", _decode_with(sign=-1.0))
+    with pytest.raises(AssertionError):
+        check_against_brute(workloads.c1_tiny())
+
+
+def test_swapped_k_and_v_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "decode", _decode_with(swap_kv=True))
+    with pytest.raises(AssertionError):
+        check_against_brute(workloads.c1_tiny())
+
+
+def test_gather_off_by_one_is_caught(monkeypatch):
+    real = att.gather
+
+    def shifted(store, layer, table, n, g, scales=None, which=0):
+        rows = real(store, layer, table, n + 1 if n % 16 else n, g, scales, which)
+        return rows[1:n + 1] if len(rows) > n else np.roll(rows, 1, axis=0)
+
+    monkeypatch.setattr(oracle, "gather", shifted)
+    with pytest.raises(AssertionError):
+        check_gather_matches_contiguous(0)
+
+
+def test_fifo_free_list_is_caught(monkeypatch):
+    def seq_free(self, sid):
+        self._check(sid)
+        for blk in reversed(self.tables[sid]):
+            self.ref[blk] -= 1
+            if self.ref[blk] == 0:
+                self.free.insert(0, blk)
+        del self.tables[sid]
+        del self.lens[sid]
+
+    monkeypatch.setattr(alc.RefAllocator, "seq_free", seq_free)
+    with pytest.raises(AssertionError):
+        hand_trace()
+
+
+def test_missing_copy_on_write_is_caught(monkeypatch):
+    def seq_reserve(self, sid, n):
+        self._check(sid)
+        table, length = self.tables[sid], self.lens[sid]
+        need = sum(1 for pos in range(length, length + n) if pos % 16 == 0)
+        if need > len(self.free):
+            raise oracle.NoBlocks(sid)
+        slots = []
+        for pos in range(length, length + n):
+            lblk, off = divmod(pos, 16)
+            if off == 0:
+                blk = self.free.pop()
+                self.ref[blk] = 1
+                table.append(blk)
+            slots.append(table[lblk] * 16 + off)
+        self.lens[sid] = length + n
+        return slots, []
+
+    monkeypatch.setattr(alc.RefAllocator, "seq_reserve", seq_reserve)
+    with pytest.raises(AssertionError):
+        test_shared_prefix_equals_private_copy()
+    with pytest.raises(AssertionError):
+        hand_trace()
+
+
+def test_leaked_block_on_free_is_caught(monkeypatch):
+    def seq_free(self, sid):
+        self._check(sid)
+        for blk in reversed(self.tables[sid][1:]):
+            self.ref[blk] -= 1
+            if self.ref[blk] == 0:
+                self.free.append(blk)
+        del self.tables[sid]
+        del self.lens[sid]
+
+    monkeypatch.setattr(alc.RefAllocator, "seq_free", seq_free)
+    with pytest.raises(AssertionError):
+        random_ops(oracle.RefAllocator(12, np.arange(12)), np.random.default_rng(1), 100)
+
+
+def test_floor_quantiser_is_caught(monkeypatch):
+    monkeypatch.setattr(qnt.np, "rint", np.floor)
+    with pytest.raises(AssertionError):
+        check_error_bound(1)
+
+
+def test_size_formula_without_factor_two_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "kv_cache_bytes",
+                        lambda L, H, D, E, n, B=1: L * H * D * E * n * B)
+    with pytest.raises(AssertionError):
+        check_printed_sizes(__import__("os").path.join(__import__("os").path.dirname(__file__), "golden"))

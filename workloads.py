@@ -1,0 +1,229 @@
+"""Seeded synthetic workloads for the paged KV cache.
+
+This module is the only source of randomness for tests and the benchmark and
+the only thing the HIP library and the CPU oracle have in common: it draws
+request lengths, physical-block orders, churn recipes and fp16 K/V/q values,
+and it contains none of the method's arithmetic (no attention, no block
+bookkeeping). Each workload is a script of steps that a driver replays
+against either implementation.
+
+Step kinds::
+
+    ("create", name)                 new empty sequence
+    ("prefill", name, k, v)          append len(k) tokens to one sequence
+    ("append", names, k, v)          append one token to each named sequence
+    ("fork", parent, child)          child shares parent's blocks
+    ("free", name)                   release a sequence
+    ("churn", Churn)                 alloc/free traffic of earlier requests
+    ("decode", names, q)             one decode step over the named sequences
+
+``k``/``v`` are ``[n, Hkv, D]`` fp16 and ``q`` is ``[B, Hq, D]`` fp16, drawn as
+``standard_normal(float32).astype(float16)``. Draws follow one fixed order:
+physical order / churn, then lengths, then K/V per sequence in order, then
+the new token's k/v, then q.
+"""
+
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+
+
+@dataclass
+class Churn:
+    """Alloc/free traffic of earlier requests that scrambles the free list.
+
+    Replayed by :func:`replay_churn`: request ``i`` asks for ``lengths[i]``
+    tokens; while the pool refuses it, a random live request is freed; after
+    each admission a coin (p = 0.5) may free one random live request; at the
+    end every live request is freed in random order. All random choices come
+    from the pre-drawn ``uniforms`` stream.
+    """
+
+    lengths: np.ndarray
+    uniforms: np.ndarray
+
+
+def replay_churn(churn, alloc, free):
+    """Drive ``alloc(tag, n) -> bool`` and ``free(tag)`` through the churn.
+
+    ``alloc`` returns False when the pool is out of blocks (and must then have
+    changed nothing)."""
+    it = iter(churn.uniforms)
+
+    def pick(live):
+        return live.pop(min(int(next(it) * len(live)), len(live) - 1))
+
+    live = []
+    for i, n in enumerate(churn.lengths):
+        while not alloc(i, int(n)):
+            if not live:
+                raise RuntimeError("request larger than the whole pool")
+            free(pick(live))
+        live.append(i)
+        if next(it) < 0.5 and live:
+            free(pick(live))
+    while live:
+        free(pick(live))
+
+
+@dataclass
+class Workload:
+    name: str
+    num_blocks: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str  # "f16" or "i8"
+    free_order: np.ndarray  # int32 permutation of the block ids
+    steps: list = field(default_factory=list)
+    seed: int = 0
+    layers: int = 1  # layers whose contents come from this script
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def group(self):
+        return self.num_q_heads // self.num_kv_heads
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+
+
+def _decode_batch(name, rng, N, Hq, Hkv, D, lens, free_order, dtype="f16", append=True):
+    """Shared shape of C1, C2, C5 and the headline: B sequences prefilled to
+    ``lens``, one appended token each (unless ``append`` is False), then one
+    decode step."""
+    w = Workload(name, N, Hq, Hkv, D, dtype, free_order)
+    names = [f"s{i}" for i in range(len(lens))]
+    for s in names:
+        w.steps.append(("create", s))
+    for s, n in zip(names, lens):
+        w.steps.append(("prefill", s, _normal(rng, (n, Hkv, D)), _normal(rng, (n, Hkv, D))))
+    if append:
+        B = len(lens)
+        w.steps.append(("append", names, _normal(rng, (B, Hkv, D)), _normal(rng, (B, Hkv, D))))
+    w.steps.append(("decode", names, _normal(rng, (len(lens), Hq, D))))
+    return w
+
+
+def c1_tiny(seed=1):
+    """Tiny one-layer case: 4 sequences at {5,17,33,64} tokens, 4 q heads,
+    2 KV heads, head_dim 64, a 64-block pool in random physical order; one
+    appended token each, then decode over {6,18,34,65}."""
+    rng = np.random.default_rng(seed)
+    N = 64
+    order = rng.permutation(N).astype(np.int32)
+    w = _decode_batch("c1_tiny", rng, N, 4, 2, 64, [5, 17, 33, 64], order)
+    w.seed = seed
+    return w
+
+
+def c2_llama_b8(seed=2):
+    """Llama-7B-shaped layer (32 q / 8 KV heads, d128): batch 8 at 1024
+    tokens, pool of exactly 8 * ceil(1025/16) = 520 blocks in random order,
+    one appended token, decode over 1025."""
+    rng = np.random.default_rng(seed)
+    N = 8 * 65
+    order = rng.permutation(N).astype(np.int32)
+    w = _decode_batch("c2_llama_b8", rng, N, 32, 8, 128, [1024] * 8, order)
+    w.seed = seed
+    return w
+
+
+def c3_mixed(seed=3, batch=16, churn_requests=200):
+    """Continuous-batching mix: 16 sequences of U[128, 8192] tokens, pool
+    scrambled by 200 earlier requests of U[1, 8192] tokens."""
+    rng = np.random.default_rng(seed)
+    N = 16 * 513
+    churn = Churn(lengths=rng.integers(1, 8193, churn_requests),
+                  uniforms=rng.random(8 * churn_requests + 64))
+    lens = rng.integers(128, 8193, batch).tolist()
+    w = Workload("c3_mixed", N, 32, 8, 128, "f16", np.arange(N, dtype=np.int32))
+    w.steps.append(("churn", churn))
+    names = [f"s{i}" for i in range(batch)]
+    for s in names:
+        w.steps.append(("create", s))
+    for s, n in zip(names, lens):
+        w.steps.append(("prefill", s, _normal(rng, (n, 8, 128)), _normal(rng, (n, 8, 128))))
+    w.steps.append(("append", names, _normal(rng, (batch, 8, 128)), _normal(rng, (batch, 8, 128))))
+    w.steps.append(("decode", names, _normal(rng, (batch, 32, 128))))
+    w.seed = seed
+    return w
+
+
+def c4_prefix(seed=4, sharers=32, prefix=2048):
+    """Copy-on-write prefix sharing: one 2048-token prefix shared by 32
+    sequences, private suffixes of U[64, 1024] tokens, one decode step; then
+    the lowest-index sequence whose length is not a multiple of 16 forks, the
+    child appends one token (into the shared partial tail block) and
+    [parent, child] decode."""
+    rng = np.random.default_rng(seed)
+    N = 2304
+    order = rng.permutation(N).astype(np.int32)
+    suffix = rng.integers(64, 1025, sharers).tolist()
+    w = Workload("c4_prefix", N, 32, 8, 128, "f16", order)
+    names = [f"s{i}" for i in range(sharers)]
+    w.steps.append(("create", names[0]))
+    w.steps.append(("prefill", names[0], _normal(rng, (prefix, 8, 128)), _normal(rng, (prefix, 8, 128))))
+    for s in names[1:]:
+        w.steps.append(("fork", names[0], s))
+    for s, n in zip(names, suffix):
+        w.steps.append(("prefill", s, _normal(rng, (n, 8, 128)), _normal(rng, (n, 8, 128))))
+    w.steps.append(("append", names, _normal(rng, (sharers, 8, 128)), _normal(rng, (sharers, 8, 128))))
+    w.steps.append(("decode", names, _normal(rng, (sharers, 32, 128))))
+    lengths = [prefix + n + 1 for n in suffix]
+    parent = next(i for i, n in enumerate(lengths) if n % 16)
+    w.steps.append(("fork", names[parent], "child"))
+    w.steps.append(("append", ["child"], _normal(rng, (1, 8, 128)), _normal(rng, (1, 8, 128))))
+    w.steps.append(("decode", [names[parent], "child"], _normal(rng, (2, 32, 128))))
+    w.seed = seed
+    return w
+
+
+def c5_int8(seed=5, batch=16, ctx=8192):
+    """Long-context int8 KV: 16 sequences at 8192 tokens of N(0,1) fp16 data
+    stored as int8 with one fp16 scale per (block, KV head); decode only."""
+    rng = np.random.default_rng(seed)
+    N = batch * (-(-ctx // 16))
+    order = rng.permutation(N).astype(np.int32)
+    w = _decode_batch("c5_int8", rng, N, 32, 8, 128, [ctx] * batch, order, dtype="i8", append=False)
+    w.seed = seed
+    return w
+
+
+def headline(seed=6, batch=16, ctx=8192, spare_blocks=0):
+    """The 32q/8kv d128 fp16 decode step at batch 16 and 8K context: 16
+    sequences prefilled to 8192 tokens, one appended token each, decode over
+    8193. Pool: 16 * 513 blocks (+ ``spare_blocks`` for longer runs)."""
+    rng = np.random.default_rng(seed)
+    N = batch * (-(-(ctx + 1) // 16)) + spare_blocks
+    order = rng.permutation(N).astype(np.int32)
+    w = _decode_batch("headline_b16_ctx8k", rng, N, 32, 8, 128, [ctx] * batch, order)
+    w.seed = seed
+    return w
+
+
+def tiny_random(seed, B=3, Hq=4, Hkv=2, D=64, max_len=40, N=None, dtype="f16"):
+    """Small random shapes for brute-force and edge-case checks."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, max_len + 1, B).tolist()
+    if N is None:
+        N = sum(-(-(n + 1) // 16) for n in lens) + 4
+    order = rng.permutation(N).astype(np.int32)
+    w = _decode_batch(f"tiny_{seed}", rng, N, Hq, Hkv, D, lens, order, dtype=dtype)
+    w.seed = seed
+    return w
+
+
+CONFIGS = {
+    "c1": c1_tiny,
+    "c2": c2_llama_b8,
+    "c3": c3_mixed,
+    "c4": c4_prefix,
+    "c5": c5_int8,
+    "headline": headline,
+}
