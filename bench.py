@@ -1,0 +1,362 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV cache decode step on one MI355X.
+
+Workload (seeded, synthetic): the 32-query-head / 8-KV-head, head_dim 128,
+fp16 decode step at batch 16 and 8K context over 32 layer pools -- every
+sequence prefilled to 8192 tokens ([p2] lqnn.cn/news/235768 §2.3 table, the
+8192 x 16 row: 16 GB of K/V). One step is the whole hot path for one new
+token per sequence: host slot reservation and block-table packing, their
+upload, then for each of the 32 layers the KV append and the paged decode
+(split-K kernel + log-sum-exp merge). The context grows by one token per
+step, as in serving.
+
+Printed: one JSON line. ``value`` is whole-step throughput in GB/s of
+algorithmic bytes (K/V read by decode, q, tables, out, appended K/V read and
+written); ``decode_tok_s`` is batch / step time (attention only);
+``roofline`` is the split-K decode kernel's algorithmic bytes per launch
+over its average duration, timed with HIP events recorded around that
+kernel alone on its own stream; ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+B, HQ, HKV, D, CTX = 16, 32, 8, 128, 8192
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "paged_kv_cache_392_amd", "csrc", "kernels.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(src_hash, bytes_per_launch):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "paged_decode_headline_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the paged decode path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    sys.path.insert(0, ROOT)
+    import paged_kv_cache_392_amd as pkv
+    from paged_kv_cache_392_amd import _capi as C
+    import workloads
+
+    dev = torch.device("cuda:0")
+    K, W, L = args.steps, args.warmup, args.layers
+    total_steps = K + W
+    spare = B * (-(-(total_steps + 1) // 16))
+    w = workloads.headline(spare_blocks=spare)
+    N = w.num_blocks
+    max_blocks = -(-(CTX + total_steps + 1) // 16)
+
+    cache = pkv.PagedKVCache(L, N, HKV, D, "f16", w.free_order, dev)
+    lib = C.load()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    print(f"[bench] pool {cache.nbytes / 2**30:.2f} GiB, {L} layers, {N} blocks", file=sys.stderr, flush=True)
+
+    # --- build the cache: layer 0 from the seeded workload through the
+    # library's append, layers 1.. with seeded device noise (timing only)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    for layer in range(1, L):
+        cache.region(0, layer).normal_(generator=gen)
+        cache.region(1, layer).normal_(generator=gen)
+    seqs, first_k, first_v, first_q = [], None, None, None
+    for step in w.steps:
+        if step[0] == "create":
+            seqs.append(cache.create_seq())
+        elif step[0] == "prefill":
+            _, name, k, v = step
+            s = seqs[int(name[1:])]
+            slots, cow = cache.reserve([s], [len(k)])
+            sd = torch.from_numpy(slots).to(dev)
+            cache.write(0, torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), sd)
+        elif step[0] == "append":
+            first_k, first_v = step[2], step[3]
+        elif step[0] == "decode":
+            first_q = step[2]
+    torch.cuda.synchronize()
+
+    # per-layer new-token k/v and q; step 0 of layer 0 uses the workload's own
+    knew = torch.empty((total_steps, L, B, HKV, D), dtype=torch.float16, device=dev).normal_(generator=gen)
+    vnew = torch.empty_like(knew).normal_(generator=gen)
+    qall = torch.empty((L, B, HQ, D), dtype=torch.float16, device=dev).normal_(generator=gen)
+    knew[0, 0].copy_(torch.from_numpy(first_k))
+    vnew[0, 0].copy_(torch.from_numpy(first_v))
+    qall[0].copy_(torch.from_numpy(first_q))
+    out = torch.empty((L, B, HQ, D), dtype=torch.float16, device=dev)
+    max_ctx_final = CTX + total_steps
+    ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, HQ, max_ctx_final, args.partition_tokens)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    # per-step pinned upload buffers (a step's buffer is never reused while its
+    # copy may still be queued)
+    slots_h = torch.empty((total_steps, B), dtype=torch.int32).pin_memory()
+    tables_h = torch.empty((total_steps, B, max_blocks), dtype=torch.int32).pin_memory()
+    lens_h = torch.empty((total_steps, B), dtype=torch.int32).pin_memory()
+    slots_d = torch.empty((B,), dtype=torch.int32, device=dev)
+    tables_d = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
+    lens_d = torch.empty((B,), dtype=torch.int32, device=dev)
+    seq_arr = np.array(seqs, np.int64)
+
+    # prebuilt decode argument blocks, one per layer
+    argv = []
+    for layer in range(L):
+        a = C.pkv_decode_args()
+        a.cfg = ctypes.pointer(cache.cfg)
+        a.pool_dev = cache.pool.data_ptr()
+        a.layer = layer
+        a.q_dev = qall[layer].data_ptr()
+        a.num_seqs = B
+        a.num_q_heads = HQ
+        a.block_tables_dev = tables_d.data_ptr()
+        a.max_blocks = max_blocks
+        a.ctx_lens_dev = lens_d.data_ptr()
+        a.out_dev = out[layer].data_ptr()
+        a.scale = 1.0 / math.sqrt(D)
+        a.workspace_dev = ws.data_ptr()
+        a.workspace_bytes = ws.numel()
+        a.partition_tokens = args.partition_tokens
+        a.timing_events = None
+        argv.append(a)
+
+    # timing events around the split kernel and the merge kernel of every
+    # timed decode (recorded once so each owns a HIP event)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K * L)]
+    for group in ev:
+        for e in group:
+            e.record()
+    ev_arrays = [(ctypes.c_void_p * 4)(*[e.cuda_event for e in group]) for group in ev]
+    ev_ptrs = [ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)) for arr in ev_arrays]
+    torch.cuda.synchronize()
+
+    lib_reserve = lib.pkv_seq_reserve
+    slot1 = np.empty(1, np.int32)
+    cow = np.empty((1, 2), np.int32)
+    ncow = ctypes.c_int32()
+    step_lens = []
+
+    def one_step(i, timed_index):
+        # a1: reserve one slot per sequence (host allocator)
+        sl = slots_h[i].numpy()
+        for b in range(B):
+            st = lib_reserve(cache.handle, int(seq_arr[b]), 1, C._i32p(slot1), C._i32p(cow), 1, ctypes.byref(ncow))
+            if st != 0 or ncow.value:
+                raise RuntimeError(f"reserve failed ({st}) or unexpected copy-on-write")
+            sl[b] = slot1[0]
+        # a2: pack and upload the tables, lengths and slots
+        th, lh = tables_h[i].numpy(), lens_h[i].numpy()
+        C._check(lib.pkv_build_block_tables(cache.handle, seq_arr.ctypes.data_as(C._p_i64), B, max_blocks,
+                                            C._i32p(th), C._i32p(lh)))
+        step_lens.append(lh.copy())
+        slots_d.copy_(slots_h[i], non_blocking=True)
+        tables_d.copy_(tables_h[i], non_blocking=True)
+        lens_d.copy_(lens_h[i], non_blocking=True)
+        mc = int(lh.max())
+        for layer in range(L):
+            # a4: append the new token's K/V; a5 + a6: paged decode
+            C._check(lib.pkv_append_kv(ctypes.byref(cache.cfg), cache.pool.data_ptr(), layer,
+                                       knew[i, layer].data_ptr(), vnew[i, layer].data_ptr(),
+                                       slots_d.data_ptr(), B, sp))
+            a = argv[layer]
+            a.max_context = mc
+            a.ctx_lens_host = C._i32p(lh)
+            a.timing_events = ev_ptrs[timed_index * L + layer] if timed_index is not None else None
+            C._check(lib.pkv_paged_decode(ctypes.byref(a), sp))
+
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for i in range(W):
+        one_step(i, None)
+        if i == 0:
+            torch.cuda.synchronize()
+            first_out = out[0].float().cpu().numpy()
+            first_tables = tables_h[0].numpy().copy()
+            first_lens = lens_h[0].numpy().copy()
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(K):
+        one_step(W + i, i)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / K
+
+    split_ms = np.array([g[0].elapsed_time(g[1]) for g in ev])
+    merge_ms = np.array([g[2].elapsed_time(g[3]) for g in ev])
+    timed_lens = step_lens[W:]
+
+    # algorithmic bytes
+    kv_tok = 2 * HKV * D * 2  # K and V of one token, one layer, fp16
+    def decode_bytes(lens, with_out=True):
+        """K/V rows read + q + table entries + lengths (+ out) of one decode."""
+        lens = np.asarray(lens, np.int64)
+        nb = len(lens)
+        nblk = (lens + 15) // 16
+        b = int(lens.sum()) * kv_tok + nb * HQ * D * 2 + int(nblk.sum()) * 4 + nb * 4
+        return b + (nb * HQ * D * 2 if with_out else 0)
+    append_bytes = 2 * (B * HKV * D * 2) * 2 + B * 4  # k, v read and written; slots
+    upload_bytes = B * max_blocks * 4 + 2 * B * 4
+    step_bytes = [L * (decode_bytes(l) + append_bytes) + upload_bytes for l in timed_lens]
+    split_bytes = np.repeat([decode_bytes(l, with_out=False) for l in timed_lens], L)
+    value = float(np.sum(step_bytes) / (total_ms * 1e-3) / 1e9)
+    split_gbps = float(np.mean(split_bytes) / (np.mean(split_ms) * 1e-3) / 1e9)
+    decode_gbps = float(np.mean(split_bytes + B * HQ * D * 2) / (np.mean(split_ms + merge_ms) * 1e-3) / 1e9)
+
+    # HBM probe: a plain coalesced read in the same run
+    probe = None
+    if not args.no_probe:
+        nbytes = min(cache.nbytes, 8 * 2**30)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        C.pkv_probe_stream_read(cache.pool.data_ptr(), nbytes, sink.data_ptr(), sp)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        torch.cuda.synchronize()
+        p0.record()
+        for _ in range(reps):
+            C.pkv_probe_stream_read(cache.pool.data_ptr(), nbytes, sink.data_ptr(), sp)
+        p1.record()
+        torch.cuda.synchronize()
+        probe = nbytes * reps / (p0.elapsed_time(p1) * 1e-3) / 1e9
+
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic(src_hash, float(np.mean(split_bytes)))
+    result = {
+        "metric": "paged decode HBM GB/s (% of peak) + decode tok/s, 32q/8kv d128 fp16",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode step, batch 16, context 8192 (+1 token per step), 32 q heads / 8 KV heads, "
+                        "head_dim 128, fp16 K/V in 16-token blocks, 32 layer pools",
+            "batch": B, "context": CTX, "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "layers": L,
+            "block_tokens": 16, "pool_blocks_per_layer": N,
+            "partition_tokens": args.partition_tokens or "auto",
+        },
+        "decode_tok_s": round(B / (ms_per_step * 1e-3), 1),
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 2),
+        "decode_kernels_GBps": round(decode_gbps, 1),
+        "split_kernel_us": round(float(np.mean(split_ms)) * 1e3, 2),
+        "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2),
+        "probe_read_GBps": None if probe is None else round(probe, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged_decode_kernel<128,4,f16> (split-K)",
+            "achieved": round(split_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(split_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": int(np.mean(split_bytes)),
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, first_out, first_tables, first_lens, args.cpu_seconds,
+                                              decode_bytes)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, gpu_out, gpu_tables, gpu_lens, budget_s, decode_bytes):
+    """Time the CPU oracle (fp64 NumPy, as it stands) on whole sequences of
+    layer 0 of the first decode step until about ``budget_s`` seconds of CPU
+    work; report GB/s of the same algorithmic bytes and, for information, the
+    GPU's max abs error on that sample."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from oracle_driver import OracleRun
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = None
+    o = OracleRun(w).run(decode=False)
+    rec = o.decodes[0]
+    assert np.array_equal(rec["tables"], gpu_tables[:, :rec["tables"].shape[1]])
+    assert np.array_equal(rec["lens"], gpu_lens)
+    done, err, t_total = 0, 0.0, 0.0
+    for b in range(B):
+        t = time.perf_counter()
+        ref = oracle.decode(o.cache, rec["q"][b:b + 1], rec["tables"][b:b + 1], rec["lens"][b:b + 1], 0, w.scale)
+        t_total += time.perf_counter() - t
+        err = max(err, float(np.abs(gpu_out[b].astype(np.float64) - ref[0]).max()))
+        done += 1
+        if t_total >= budget_s:
+            break
+    lens = rec["lens"][:done]
+    nbytes = decode_bytes(lens, True)
+    return {
+        "value": round(nbytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": blas,
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "seconds": round(t_total, 2),
+        "sample": f"layer 0 of 32, {done} of {B} sequences at context {int(lens[0])}, all 32 q heads "
+                  f"(fp64 NumPy gather + softmax(qK^T/sqrt(d))V)",
+        "gpu_max_abs_err_on_sample": err,
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * pkv.h -- C ABI of libpkv: a paged KV cache and paged decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source pages cited below:
+ *   [p1] KV Cache / PagedAttention / Flash Attention overview,
+ *        chanyi.net.cn/article/49, sections 一 to 六
+ *   [p2] practitioner notes on KV cache and vLLM, lqnn.cn/news/235768,
+ *        sections 1 to 5.3
+ *   [p3] course notes "9.1 推理优化：KV Cache、PagedAttention 与 vLLM",
+ *        hdu-wiki.cn/courses/inference-kvcache-vllm
+ *
+ * Conventions
+ *   - Every call returns an int status (PKV_OK = 0, negative on error) unless
+ *     stated otherwise. No C++ exception crosses this boundary. On error,
+ *     pkv_last_error() returns a message for the calling thread.
+ *   - The library owns host metadata only. All device memory (the pool, the
+ *     tables, q, out, the workspace) belongs to the caller; device calls are
+ *     asynchronous on the caller's stream and never allocate.
+ *   - A pkv_pool handle is not thread-safe: the caller serialises calls on
+ *     one handle.
+ *   - Streams are passed as void* and must be a hipStream_t (NULL = the
+ *     default stream).
+ *
+ * Device pool layout (one allocation of pkv_pool_bytes() bytes):
+ *   K region   [L][N][Hkv][16][D] elements (fp16 or int8)
+ *   V region   same shape, right after K
+ *   scales     int8 pools only: [L][N][Hkv][2] fp16 (0 = K scale, 1 = V)
+ * One (layer, block, KV head) tile is 16 consecutive token rows of D
+ * elements: each block holds a short contiguous run of K/V and blocks need
+ * not be contiguous with each other ([p2] §3.2).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PKV_OK 0
+#define PKV_ERR_INVALID_ARG (-1) /* bad pointer, size, shape or value          */
+#define PKV_ERR_NO_BLOCKS (-2)   /* pool exhausted; nothing changed ([p2] §5.2) */
+#define PKV_ERR_UNKNOWN_SEQ (-3) /* sequence id not live                        */
+#define PKV_ERR_REFCOUNT (-4)    /* block refcount inconsistency                */
+#define PKV_ERR_UNSUPPORTED (-5) /* head_dim / dtype / group size not built     */
+#define PKV_ERR_HIP (-6)         /* a HIP runtime call failed                   */
+
+/* ---- element types ------------------------------------------------------ */
+#define PKV_F16 0 /* IEEE binary16 K/V                                          */
+#define PKV_I8 1  /* int8 K/V with one fp16 scale per (block, KV head), [p2] §4.1 */
+
+#define PKV_BLOCK_TOKENS 16 /* tokens per block: the page size of [p1] §三, [p2] §3.2 */
+
+/* Shape of one pool. Validated by every call that takes it:
+ * num_layers >= 1, num_blocks >= 1, block_size == 16, num_kv_heads >= 1,
+ * head_dim in {64, 128}, dtype in {PKV_F16, PKV_I8}. */
+typedef struct pkv_config {
+  int32_t num_layers;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+} pkv_config;
+
+typedef struct pkv_pool pkv_pool;
+
+/* Bytes of device memory the pool needs: N*16 token slots of
+ * 2*L*Hkv*D*elem_bytes each (the per-token size of [p2] §2.3), plus
+ * N*L*Hkv*2 fp16 scales for int8. Returns < 0 (a status) on a bad config. */
+int64_t pkv_pool_bytes(const pkv_config* cfg);
+
+/* ---- host block allocator ([p1] §三, [p2] §3.2) --------------------------- */
+
+/* Create the host metadata of a pool of cfg->num_blocks blocks.
+ * free_order: a permutation of 0..N-1 giving the order in which blocks are
+ * handed out (NULL = 0,1,2,...); n must equal N when free_order is given.
+ * The free list is a LIFO stack: a freed sequence pushes its blocks in
+ * reverse logical order, and the next allocation takes the last one pushed.
+ * *out receives the handle. The library allocates no device memory. */
+int pkv_pool_create(const pkv_config* cfg, const int32_t* free_order, int32_t n, pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+
+/* A new, empty sequence. Ids count up from 1 in creation order. */
+int pkv_seq_create(pkv_pool* pool, int64_t* seq);
+/* Release a finished request: each of its blocks loses a reference and a
+ * block that reaches zero returns to the free list at once ([p1] §三,
+ * [p2] §3.2). */
+int pkv_seq_free(pkv_pool* pool, int64_t seq);
+/* A new sequence sharing all of parent's blocks (refcount + 1 each); blocks
+ * are copied only when one sharer later writes into a shared block, as with
+ * Unix fork() ([p1] §三). */
+int pkv_seq_fork(pkv_pool* pool, int64_t parent, int64_t* child);
+
+/* Reserve slots for n new tokens appended at the tail of seq ([p2] §2.2).
+ * slots_out[n] receives slot = physical_block*16 + offset for each token in
+ * order. A token at offset 0 opens a new block. A token written at a
+ * non-zero offset of a block shared with another sequence first moves the
+ * writer to a fresh block (copy-on-write): the (src, dst) block pair is
+ * appended to cow_pairs_out (int32 [cow_cap][2]) and *n_cow counts them; the
+ * caller copies those blocks with pkv_copy_blocks before writing.
+ * All or nothing: on PKV_ERR_NO_BLOCKS (or INVALID_ARG for cow_cap too small)
+ * no state changes, so the caller may queue the request ([p2] §5.2).
+ * slots_out may be NULL only when n == 0. */
+int pkv_seq_reserve(pkv_pool* pool, int64_t seq, int32_t n, int32_t* slots_out,
+                    int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow);
+
+/* ---- introspection (host) ------------------------------------------------- */
+int pkv_seq_len(const pkv_pool* pool, int64_t seq, int32_t* len);
+/* Logical -> physical block map of seq; *n = number of blocks. cap < *n is
+ * INVALID_ARG (and *n still reports the size). */
+int pkv_seq_block_table(const pkv_pool* pool, int64_t seq, int32_t* out, int32_t cap, int32_t* n);
+int pkv_block_refcount(const pkv_pool* pool, int32_t block, int32_t* ref);
+int pkv_num_free(const pkv_pool* pool, int32_t* n);
+/* Free blocks, the next to be handed out first. */
+int pkv_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* Pack the tables of B sequences into host buffers for upload:
+ * tables_host int32 [B][max_blocks] (unused entries = -1) and
+ * ctx_lens_host int32 [B] (tokens held by each sequence). INVALID_ARG if a
+ * table is wider than max_blocks. The decode walks these rows in logical
+ * order instead of gathering blocks into contiguous memory ([p2] §3.2). */
+int pkv_build_block_tables(const pkv_pool* pool, const int64_t* seqs, int32_t B, int32_t max_blocks,
+                           int32_t* tables_host, int32_t* ctx_lens_host);
+
+/* ---- device operations (asynchronous on `stream`) ------------------------ */
+
+/* Copy-on-write block copy ([p1] §三): for each of the n (src, dst) pairs in
+ * pairs_dev (int32 [n][2], device), copy the whole block -- every layer, K
+ * and V, and the int8 scales -- from src to dst. Pairs with an id outside
+ * [0, N) are skipped. n == 0 is a no-op. */
+int pkv_copy_blocks(const pkv_config* cfg, void* pool_dev, const int32_t* pairs_dev, int32_t n,
+                    void* stream);
+
+/* Append ([p2] §2.2 pseudocode: the new token's k and v go to the cache
+ * tail; cached K/V are never modified afterwards, [p1] §二): for token i,
+ * write k_dev[i] and v_dev[i] (fp16, contiguous [n_tokens][Hkv][D], device)
+ * into slot slots_dev[i] (int32, device) of `layer`. Bit-exact copy. Slots
+ * outside [0, 16N) are skipped. fp16 pools only (UNSUPPORTED for int8). */
+int pkv_append_kv(const pkv_config* cfg, void* pool_dev, int32_t layer, const void* k_dev,
+                  const void* v_dev, const int32_t* slots_dev, int32_t n_tokens, void* stream);
+
+/* Arguments of one paged decode step over a batch ([p2] §1.2 attention of
+ * the new token's query over all cached tokens; [p2] §3.2 walk through the
+ * block table). */
+typedef struct pkv_decode_args {
+  const pkv_config* cfg;
+  const void* pool_dev;           /* the pool, layout above                       */
+  int32_t layer;                  /* 0 <= layer < L                               */
+  const void* q_dev;              /* fp16 [B][Hq][D]                              */
+  int32_t num_seqs;               /* B >= 1                                       */
+  int32_t num_q_heads;            /* Hq, a multiple of Hkv; G = Hq/Hkv in {1,2,4,8} */
+  const int32_t* block_tables_dev;/* int32 [B][max_blocks], -1 padded             */
+  int32_t max_blocks;             /* row stride of the tables                     */
+  const int32_t* ctx_lens_dev;    /* int32 [B], tokens attended (>= 1)            */
+  const int32_t* ctx_lens_host;   /* optional host copy, validated if non-NULL    */
+  int32_t max_context;            /* >= every ctx_len; sizes the grid             */
+  void* out_dev;                  /* fp16 [B][Hq][D], written by the call         */
+  float scale;                    /* softmax scale, usually 1/sqrt(D)             */
+  void* workspace_dev;            /* split-K partials, caller owned               */
+  int64_t workspace_bytes;        /* >= pkv_decode_workspace_bytes(...)           */
+  int32_t partition_tokens;       /* tokens per split-K partition, a multiple of
+                                     16 in [16, 4096]; 0 = automatic             */
+  void* const* timing_events;     /* optional (NULL = none): 4 hipEvent_t recorded
+                                     around the split kernel ([0] start, [1] stop)
+                                     and the merge kernel ([2], [3]; untouched if
+                                     the merge is not needed). Instrumentation
+                                     only; the result does not depend on it.     */
+} pkv_decode_args;
+
+/* Workspace bytes pkv_paged_decode needs for these sizes (0 is possible).
+ * Returns < 0 (a status) on bad arguments. partition_tokens 0 = the same
+ * automatic choice pkv_paged_decode makes. */
+int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_context, int32_t partition_tokens);
+
+/* Paged decode: out[b][h] = softmax(q[b][h] . K_b^T * scale) . V_b over the
+ * ctx_lens[b] tokens of sequence b, read in place through its block table
+ * (no gather), with query head h using KV head h / (Hq/Hkv). Split-K: the
+ * context is cut into partitions of partition_tokens (a multiple of 16);
+ * each partition runs an online softmax ([p1] §四) and a second kernel
+ * merges the partitions by log-sum-exp. Accumulation is fp32 and the output
+ * is rounded to fp16 (nearest even). The result depends only on logical
+ * token order, not on physical block ids. Slots past ctx_len in a tail
+ * block are never used. Block ids outside [0, N) are treated as empty.
+ * INVALID_ARG: null pointers, ctx_len == 0 or > 16*max_blocks or >
+ * max_context (host copy), workspace too small, partition_tokens not a
+ * multiple of 16. UNSUPPORTED: head_dim/group size not built. */
+int pkv_paged_decode(const pkv_decode_args* args, void* stream);
+
+/* ---- measurement helper ------------------------------------------------------ */
+
+/* Plain coalesced read of `bytes` (>= 16) bytes at buf_dev (16-byte aligned),
+ * the reference for achievable HBM read bandwidth on this device. sink_dev
+ * must point to 4 writable device bytes (practically never written). */
+int pkv_probe_stream_read(const void* buf_dev, int64_t bytes, void* sink_dev, void* stream);
+
+/* ---- errors ---------------------------------------------------------------- */
+const char* pkv_strerror(int status);
+const char* pkv_last_error(void); /* thread-local; "" if none */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

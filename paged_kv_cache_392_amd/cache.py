@@ -1,0 +1,233 @@
+"""PagedKVCache: the Python face of libpkv.
+
+torch provides the device memory (one uint8 tensor holds the whole pool) and
+the stream (the current torch stream); every step of the path runs in the
+library: block bookkeeping in its C++ allocator, copies, appends and decode
+in its HIP kernels. Nothing here computes attention or touches cache
+contents.
+
+The calls follow the pages' statement of the problem: a pool of fixed
+16-token blocks with a block table per sequence, blocks allocated on demand
+and returned when a sequence ends ([p1] chanyi.net.cn/article/49 §三; [p2]
+lqnn.cn/news/235768 §3.2), copy-on-write prefix sharing through fork ([p1]
+§三), append of the new token's K/V at the tail ([p2] §2.2) and a decode that
+reads the blocks in table order ([p2] §3.2).
+"""
+
+import math
+
+import numpy as np
+import torch
+
+from . import _capi as C
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev_i32(a, device):
+    t = torch.from_numpy(np.ascontiguousarray(a, np.int32))
+    if t.numel() == 0:
+        return torch.empty(t.shape, dtype=torch.int32, device=device)
+    return t.pin_memory().to(device, non_blocking=True)
+
+
+class PagedKVCache:
+    """A pool of ``num_blocks`` blocks for ``num_layers`` layers.
+
+    ``dtype`` is ``"f16"`` or ``"i8"`` (int8 K/V with one fp16 scale per
+    (layer, block, KV head) for K and for V). ``free_order`` fixes the order
+    in which blocks are handed out (a permutation of the block ids).
+    """
+
+    def __init__(self, num_layers, num_blocks, num_kv_heads, head_dim, dtype="f16",
+                 free_order=None, device="cuda"):
+        self.cfg = C.make_config(num_layers, num_blocks, num_kv_heads, head_dim, dtype)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.num_layers, self.num_blocks = num_layers, num_blocks
+        self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
+        self.nbytes = C.pkv_pool_bytes(self.cfg)
+        self.pool = torch.empty(self.nbytes, dtype=torch.uint8, device=self.device)
+        self.handle = C.pkv_pool_create(self.cfg, free_order)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            C.pkv_pool_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- views of the device pool (for tests and bulk fills) ---------------
+    def _region_bytes(self):
+        e = 1 if self.dtype == "i8" else 2
+        return self.num_layers * self.num_blocks * self.num_kv_heads * 16 * self.head_dim * e
+
+    def region(self, which, layer=None):
+        """K (``which=0``) or V (1) region as ``[L, N, Hkv, 16, D]`` (or one layer)."""
+        rb = self._region_bytes()
+        raw = self.pool[which * rb:(which + 1) * rb]
+        t = raw.view(torch.int8 if self.dtype == "i8" else torch.float16)
+        t = t.view(self.num_layers, self.num_blocks, self.num_kv_heads, 16, self.head_dim)
+        return t if layer is None else t[layer]
+
+    def scales(self):
+        """int8 scales ``[L, N, Hkv, 2]`` fp16 (0 = K, 1 = V)."""
+        if self.dtype != "i8":
+            raise ValueError("fp16 pools have no scales")
+        rb = self._region_bytes()
+        raw = self.pool[2 * rb:]
+        return raw.view(torch.float16).view(self.num_layers, self.num_blocks, self.num_kv_heads, 2)
+
+    # ---- sequences (host) -------------------------------------------------------
+    def create_seq(self):
+        return C.pkv_seq_create(self.handle)
+
+    def free_seq(self, seq):
+        C.pkv_seq_free(self.handle, seq)
+
+    def fork(self, parent):
+        return C.pkv_seq_fork(self.handle, parent)
+
+    def seq_len(self, seq):
+        return C.pkv_seq_len(self.handle, seq)
+
+    def block_table(self, seq):
+        return C.pkv_seq_block_table(self.handle, seq)
+
+    def num_free(self):
+        return C.pkv_num_free(self.handle)
+
+    def free_list(self):
+        return C.pkv_free_list(self.handle)
+
+    def refcount(self, block):
+        return C.pkv_block_refcount(self.handle, block)
+
+    def reserve(self, seqs, counts):
+        """Reserve ``counts[i]`` token slots for ``seqs[i]``, in order.
+
+        Returns ``(slots int32[sum(counts)], cow_pairs int32[k, 2])``. A
+        NoBlocksError leaves the sequence that failed (and every later one)
+        untouched; earlier sequences in the list keep their reservation."""
+        all_slots, all_cow = [], []
+        for s, n in zip(seqs, counts):
+            slots, cow = C.pkv_seq_reserve(self.handle, s, int(n), cow_cap=1)
+            all_slots.append(slots)
+            all_cow.append(cow)
+        slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int32)
+        cow = np.concatenate(all_cow) if all_cow else np.empty((0, 2), np.int32)
+        return slots, cow
+
+    # ---- device steps -------------------------------------------------------------
+    def copy_blocks(self, pairs):
+        """Copy-on-write block copies (host pairs ``[k, 2]``), all layers."""
+        pairs = np.ascontiguousarray(pairs, np.int32).reshape(-1, 2)
+        if len(pairs) == 0:
+            return
+        dev = _dev_i32(pairs, self.device)
+        C.pkv_copy_blocks(self.cfg, self.pool.data_ptr(), dev.data_ptr(), len(pairs), _stream())
+
+    def write(self, layer, k, v, slots_dev):
+        """Write fp16 ``k, v [n, Hkv, D]`` (device, contiguous) of one layer
+        into the reserved device slots."""
+        k = k.contiguous()
+        v = v.contiguous()
+        if k.dtype != torch.float16 or v.dtype != torch.float16:
+            raise TypeError("k and v must be float16")
+        n = k.shape[0]
+        if tuple(k.shape) != (n, self.num_kv_heads, self.head_dim) or v.shape != k.shape:
+            raise ValueError(f"k, v must be [n, {self.num_kv_heads}, {self.head_dim}]")
+        if slots_dev.numel() != n:
+            raise ValueError("one slot per token")
+        C.pkv_append_kv(self.cfg, self.pool.data_ptr(), layer, k.data_ptr(), v.data_ptr(),
+                        slots_dev.data_ptr(), n, _stream())
+
+    def append_kv(self, seq, k, v):
+        """Append new tokens' K/V at the tail ([p2] §2.2).
+
+        ``seq`` is one sequence id with ``k, v [n, Hkv, D]`` (n tokens), or a
+        list of B ids with ``k, v [B, Hkv, D]`` (one token each). With a
+        leading layer axis ``[L, ...]`` every layer is written; without it
+        the pool must have one layer. Returns the device slot tensor."""
+        seqs = [seq] if isinstance(seq, (int, np.integer)) else list(seq)
+        per_layer = k.dim() == 4
+        n = k.shape[1] if per_layer else k.shape[0]
+        counts = [n] if len(seqs) == 1 and isinstance(seq, (int, np.integer)) else [1] * len(seqs)
+        if sum(counts) != n:
+            raise ValueError("token count does not match the sequences")
+        if not per_layer and self.num_layers != 1:
+            raise ValueError("pass k, v with a leading layer axis for a multi-layer pool")
+        slots, cow = self.reserve(seqs, counts)
+        self.copy_blocks(cow)
+        slots_dev = _dev_i32(slots, self.device)
+        if per_layer:
+            for layer in range(k.shape[0]):
+                self.write(layer, k[layer], v[layer], slots_dev)
+        else:
+            self.write(0, k, v, slots_dev)
+        return slots_dev
+
+    def block_tables(self, seqs, max_blocks=None):
+        """Host ``(tables int32[B, max_blocks], ctx_lens int32[B])`` for the
+        decode, padded with -1."""
+        if max_blocks is None:
+            max_blocks = max(len(self.block_table(s)) for s in seqs)
+        return C.pkv_build_block_tables(self.handle, seqs, max_blocks)
+
+    def paged_decode(self, q, block_tables, context_lens, layer=0, out=None, scale=None,
+                     context_lens_host=None, max_context=None, workspace=None, partition_tokens=0):
+        """``out[b, h] = softmax(q[b, h] K_b^T * scale) V_b`` over the
+        ``context_lens[b]`` tokens of each sequence, read in place through
+        ``block_tables`` (device int32 ``[B, max_blocks]``)."""
+        return paged_decode(self, q, block_tables, context_lens, layer, out, scale,
+                            context_lens_host, max_context, workspace, partition_tokens)
+
+
+def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=None,
+                 context_lens_host=None, max_context=None, workspace=None, partition_tokens=0):
+    if q.dtype != torch.float16 or q.dim() != 3:
+        raise TypeError("q must be float16 [B, Hq, D]")
+    q = q.contiguous()
+    B, Hq, D = q.shape
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    block_tables = block_tables.contiguous()
+    context_lens = context_lens.contiguous()
+    max_blocks = block_tables.shape[1]
+    host = None
+    if context_lens_host is not None:
+        host = np.ascontiguousarray(context_lens_host, np.int32)
+    if max_context is None:
+        max_context = int(host.max()) if host is not None else max_blocks * 16
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, Hq, max_context, partition_tokens)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    args = C.pkv_decode_args()
+    args.cfg = C.ctypes.pointer(cache.cfg)
+    args.pool_dev = cache.pool.data_ptr()
+    args.layer = layer
+    args.q_dev = q.data_ptr()
+    args.num_seqs = B
+    args.num_q_heads = Hq
+    args.block_tables_dev = block_tables.data_ptr()
+    args.max_blocks = max_blocks
+    args.ctx_lens_dev = context_lens.data_ptr()
+    args.ctx_lens_host = host.ctypes.data_as(C._p_i32) if host is not None else None
+    args.max_context = max_context
+    args.out_dev = out.data_ptr()
+    args.scale = scale
+    args.workspace_dev = workspace.data_ptr()
+    args.workspace_bytes = workspace.numel()
+    args.partition_tokens = partition_tokens
+    C.pkv_paged_decode(args, _stream())
+    return out

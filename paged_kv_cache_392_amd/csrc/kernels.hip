@@ -1,0 +1,726 @@
+// gfx950 kernels of libpkv and their C-ABI launchers: KV append, block copy,
+// paged decode (split-K, fp16 or int8 K/V) and the log-sum-exp merge.
+//
+// Paged decode follows the pages' statement of the problem: one new query
+// token per sequence attends, softmax(q K^T / sqrt(d)) V ([p2]
+// lqnn.cn/news/235768 §1.2), over every cached token, the one just appended
+// included ([p2] §2.2 pseudocode); the cached K/V sit in fixed 16-token blocks
+// reached through a per-sequence block table and are read in place, in table
+// order, never gathered into contiguous memory ([p2] §3.2); several query heads
+// share one KV head ([p1] chanyi.net.cn/article/49 §二, [p2] §4.2); the scores
+// never go to HBM: each work-group runs a tiled online softmax over its part of
+// the context, the Flash Attention idea of [p1] §四. Decode is bound by reading
+// the cache ([p2] §1.3, §5.1), so the design target is HBM bandwidth, not
+// arithmetic.
+//
+// Work decomposition (one work-group of 4 wave64s per (partition, KV head,
+// sequence)):
+//   * the partition's blocks are dealt round-robin to the 4 waves; each wave
+//     streams its K and V tiles (16 rows x D) straight from HBM into VGPRs
+//     with 16-byte loads, double-buffered so the next tile is in flight
+//     while the current one is used; the loaded K tile serves all G query
+//     heads of the group;
+//   * scores: lane (t = lane/4, kq = lane%4) holds row t and one quarter of
+//     the head dimension, does fp16 pair dot products into fp32
+//     (v_dot2_f32_f16) and a 2-step DPP quad reduction;
+//   * softmax: base-2 online softmax with a wave-uniform running max that is
+//     raised only when a score exceeds it by more than 8 (in log2 units), so
+//     the rescale of the accumulators is a rare, wave-uniform branch;
+//   * values: probabilities go through 256 bytes of LDS to a second lane
+//     mapping in which each load instruction covers whole 256-byte rows and
+//     each lane accumulates D/16 (fp16) output dims for all G heads;
+//   * the 4 waves merge in LDS; a work-group writes one (m, l, o[D]) partial
+//     per query head, or the final fp16 row when the sequence has a single
+//     partition; a second kernel merges partitions by log-sum-exp.
+// The reduction order depends only on logical token positions, so the result
+// is bitwise independent of where the blocks live.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "pkv_internal.h"
+
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int BT = PKV_BLOCK_TOKENS;  // tokens per block
+constexpr int WAVES = 4;              // waves per decode work-group
+constexpr float LAZY_MAX = 8.0f;      // rescale only when a score beats the max by 2^8
+constexpr float LOG2E = 1.4426950408889634f;
+// A wave keeps its tiles' block ids one per lane: at most 64 tiles per wave.
+constexpr int MAX_PARTITION_TOKENS = 64 * WAVES * PKV_BLOCK_TOKENS;
+
+// ---------------------------------------------------------------------------
+// small device helpers
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 4 lanes of a quad; every lane ends with the same bits.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += dpp<0xB1>(x);  // quad_perm(1,0,3,2)
+  x += dpp<0x4E>(x);  // quad_perm(2,3,0,1)
+  return x;
+}
+
+__device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Max over the 16 quads (all 64 lanes) of a quad-uniform value.
+__device__ __forceinline__ float quads_max(float x) {
+  x = fmaxf(x, xor_shfl(x, 4));
+  x = fmaxf(x, xor_shfl(x, 8));
+  x = fmaxf(x, xor_shfl(x, 16));
+  x = fmaxf(x, xor_shfl(x, 32));
+  return x;
+}
+
+// Sum over the 16 quads of a quad-uniform value (butterfly: same bits in all lanes).
+__device__ __forceinline__ float quads_sum(float x) {
+  x += xor_shfl(x, 4);
+  x += xor_shfl(x, 8);
+  x += xor_shfl(x, 16);
+  x += xor_shfl(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float lo_half(uint32_t w) {
+  return float(__builtin_bit_cast(half2_t, w).x);
+}
+__device__ __forceinline__ float hi_half(uint32_t w) {
+  return float(__builtin_bit_cast(half2_t, w).y);
+}
+
+// Four int8 codes in one dword -> two fp16 pairs holding the exact integers.
+// The bytes are biased to unsigned u = x + 128, placed in the low byte of
+// fp16 1024 (whose ulp is 1) and the bias 1152 subtracted: exact for all
+// codes.
+__device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const half2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) - bias);
+  hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, b) - bias);
+}
+
+// ---------------------------------------------------------------------------
+// append / copy
+
+// Token i, KV head h: copy the D-element rows k[i][h], v[i][h] into slot
+// slots[i] of one layer. One thread moves 16 bytes.
+__global__ __launch_bounds__(256) void append_kv_f16_kernel(uint4* __restrict__ Kl, uint4* __restrict__ Vl,
+                                                            const uint4* __restrict__ k,
+                                                            const uint4* __restrict__ v,
+                                                            const int32_t* __restrict__ slots, int n,
+                                                            int Hkv, int D, int num_blocks) {
+  const int per_row = D / 8;  // 16-byte pieces per row
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = int64_t(n) * Hkv * per_row;
+  if (idx >= total) return;
+  const int c = int(idx % per_row);
+  const int64_t th = idx / per_row;
+  const int h = int(th % Hkv);
+  const int64_t i = th / Hkv;
+  const int32_t slot = slots[i];
+  if (slot < 0 || slot >= num_blocks * BT) return;
+  const int64_t blk = slot / BT, off = slot % BT;
+  const int64_t dst = ((blk * Hkv + h) * BT + off) * per_row + c;
+  const int64_t src = (i * Hkv + h) * per_row + c;
+  Kl[dst] = k[src];
+  Vl[dst] = v[src];
+}
+
+// Copy-on-write: blockIdx = (pair, layer, region); region 0 = K, 1 = V,
+// 2 = int8 scales. Copies the whole (layer, block) slab: Hkv tiles.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ pool, const int32_t* __restrict__ pairs,
+                                                          int num_blocks, int64_t slab_bytes,
+                                                          int64_t layer_bytes, int64_t region_bytes,
+                                                          int64_t scale_slab_bytes, int has_scales) {
+  const int pair = blockIdx.x, layer = blockIdx.y, region = blockIdx.z;
+  const int32_t src = pairs[2 * pair], dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  if (region == 2) {
+    if (!has_scales) return;
+    const int64_t base = 2 * region_bytes + int64_t(layer) * num_blocks * scale_slab_bytes;
+    const char* s = pool + base + src * scale_slab_bytes;
+    char* d = pool + base + dst * scale_slab_bytes;
+    for (int64_t i = threadIdx.x; i < scale_slab_bytes; i += blockDim.x) d[i] = s[i];
+    return;
+  }
+  const int64_t base = region * region_bytes + layer * layer_bytes;
+  const uint4* s = reinterpret_cast<const uint4*>(pool + base + src * slab_bytes);
+  uint4* d = reinterpret_cast<uint4*>(pool + base + dst * slab_bytes);
+  for (int64_t i = threadIdx.x; i < slab_bytes / 16; i += blockDim.x) d[i] = s[i];
+}
+
+// ---------------------------------------------------------------------------
+// paged decode
+
+struct DecodeParams {
+  const void* K;  // this layer's K region: [N][Hkv][16][D]
+  const void* V;
+  const _Float16* scales;  // int8: this layer's [N][Hkv][2]; else null
+  const _Float16* q;       // [B][Hq][D]
+  const int32_t* tables;
+  const int32_t* ctx_lens;
+  float* part_m;  // [B][Hq][max_parts]
+  float* part_l;
+  float* part_o;  // [B][Hq][max_parts][D]
+  _Float16* out;    // [B][Hq][D]
+  int max_blocks;
+  int num_blocks;
+  int Hkv;
+  int part_blocks;
+  int max_parts;
+  int max_context;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+__device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int max_context) {
+  return min(ctx, min(max_blocks * BT, max_context));
+}
+
+template <int D, int G, bool I8>
+struct Shape {
+  static constexpr int E = I8 ? 1 : 2;   // bytes per element
+  static constexpr int CE = 16 / E;      // elements per 16-byte chunk
+  static constexpr int NC = D / CE / 4;  // K chunks per lane (lane quarter kq)
+  static constexpr int QW = CE / 8;      // uint4 of fp16 q per K chunk
+  static constexpr int LPR = D / CE;     // V lanes per row
+  static constexpr int RPI = 64 / LPR;   // V rows per load instruction
+  static constexpr int NI = BT / RPI;    // V load instructions per tile
+  static constexpr int TILE = BT * D * E;  // bytes per (block, head) tile
+};
+
+template <int D, int G, bool I8>
+__global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
+  using S = Shape<D, G, I8>;
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int Hkv = prm.Hkv, Hq = Hkv * G;
+  const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+
+  if (ctx <= 0) {  // rejected on the host when lengths are given; never NaN
+    if (p == 0)
+      for (int i = tid; i < G * D; i += 256) prm.out[(int64_t(b) * Hq + g * G) * D + i] = _Float16(0.0f);
+    return;
+  }
+  const int nblk = (ctx + BT - 1) / BT;
+  const int nparts = (nblk + prm.part_blocks - 1) / prm.part_blocks;
+  if (p >= nparts) return;
+  const int jb = p * prm.part_blocks, je = min(nblk, jb + prm.part_blocks);
+
+  // K lane mapping: row kt, quarter kq; V lane mapping: row group vt, dims vd.
+  const int kt = lane >> 2, kq = lane & 3;
+  const int vt = lane / S::LPR, vd = lane % S::LPR;
+
+  // q for the G heads: the dims of this lane's K chunks {kq + 4i}.
+  uint4 qr[G][S::NC][S::QW];
+  {
+    const _Float16* qb = prm.q + (int64_t(b) * Hq + g * G) * D;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < S::NC; ++i)
+#pragma unroll
+        for (int w = 0; w < S::QW; ++w)
+          qr[h][i][w] = *reinterpret_cast<const uint4*>(qb + h * D + (kq + 4 * i) * S::CE + 8 * w);
+  }
+
+  float m[G], l[G], o[G][S::CE];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < S::CE; ++e) o[h][e] = 0.0f;
+  }
+
+  __shared__ float p_lds[WAVES][BT][G];
+  __shared__ float merge_o[WAVES][G][D];
+  __shared__ float merge_ml[WAVES][G][2];
+
+  const int32_t* trow = prm.tables + int64_t(b) * prm.max_blocks;
+  const char* Kc = static_cast<const char*>(prm.K);
+  const char* Vc = static_cast<const char*>(prm.V);
+  const int64_t head_off = int64_t(g) * S::TILE;
+  const int64_t blk_stride = int64_t(Hkv) * S::TILE;
+
+  struct Tile {
+    uint4 k[S::NC];
+    uint4 v[S::NI];
+    int blk;
+  };
+
+  // Block ids of this wave's tiles (it-th tile = logical block
+  // jb + wave + 4*it) sit one per lane in a VGPR, loaded once; each tile reads
+  // its id with readlane, so the id never waits on the vector memory queue.
+  const int first = jb + wave;
+  const int n_my = first < je ? (je - first + WAVES - 1) / WAVES : 0;  // <= 64
+  const int blk_lane = lane < n_my ? trow[first + WAVES * lane] : -1;
+
+  // A bad id (outside the pool) still loads block 0, which exists; compute()
+  // then masks every row of that tile.
+  auto load = [&](int it, Tile& t) {
+    const int blk = __builtin_amdgcn_readlane(blk_lane, it);
+    t.blk = blk;
+    const int safe = unsigned(blk) < unsigned(prm.num_blocks) ? blk : 0;
+    const char* kb = Kc + safe * blk_stride + head_off;
+    const char* vb = Vc + safe * blk_stride + head_off;
+#pragma unroll
+    for (int i = 0; i < S::NC; ++i)
+      t.k[i] = *reinterpret_cast<const uint4*>(kb + kt * (D * S::E) + (kq + 4 * i) * 16);
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i)
+      t.v[i] = *reinterpret_cast<const uint4*>(vb + (vt + S::RPI * i) * (D * S::E) + vd * 16);
+  };
+
+  auto compute = [&](int j, Tile& t) {
+    const bool blk_ok = unsigned(t.blk) < unsigned(prm.num_blocks);
+    float kscale = prm.scale_log2, vscale = 1.0f;
+    if constexpr (I8) {
+      if (blk_ok) {
+        const _Float16* sc = prm.scales + (int64_t(t.blk) * Hkv + g) * 2;
+        kscale *= float(sc[0]);
+        vscale = float(sc[1]);
+      }
+    }
+    // scores of row kt for the G heads
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < S::NC; ++i) {
+        if constexpr (I8) {
+          const uint32_t w4[4] = {t.k[i].x, t.k[i].y, t.k[i].z, t.k[i].w};
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t lo, hi;
+            i8x4_to_f16x4(w4[w], lo, hi);
+            const uint4& qq = qr[h][i][w >> 1];
+            const uint32_t qa = (w & 1) ? qq.z : qq.x, qb2 = (w & 1) ? qq.w : qq.y;
+            acc = dot2(qa, lo, acc);
+            acc = dot2(qb2, hi, acc);
+          }
+        } else {
+          acc = dot2(qr[h][i][0].x, t.k[i].x, acc);
+          acc = dot2(qr[h][i][0].y, t.k[i].y, acc);
+          acc = dot2(qr[h][i][0].z, t.k[i].z, acc);
+          acc = dot2(qr[h][i][0].w, t.k[i].w, acc);
+        }
+      }
+      s[h] = quad_sum(acc) * kscale;
+    }
+    const bool tvalid = blk_ok && (j * BT + kt) < ctx;
+    bool need = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s[h] = tvalid ? s[h] : -INFINITY;
+      need |= s[h] > m[h] + LAZY_MAX;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first tile
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = fmaxf(m[h], quads_max(s[h]));
+        const float alpha = (m[h] == -INFINITY) ? 0.0f : exp2_fast(m[h] - mn);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < S::CE; ++e) o[h][e] *= alpha;
+        m[h] = mn;
+      }
+    }
+    float pr[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      pr[h] = tvalid ? exp2_fast(s[h] - m[h]) : 0.0f;
+      l[h] += pr[h];
+    }
+    // hand the probabilities to the V lane mapping through LDS
+#pragma unroll
+    for (int h = kq; h < G; h += 4) p_lds[wave][kt][h] = pr[h];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float pv[S::NI][G];
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i)
+#pragma unroll
+      for (int h = 0; h < G; ++h) pv[i][h] = p_lds[wave][vt + S::RPI * i][h] * vscale;
+    // rows past the context (stale or poisoned) must contribute exact zeros
+    const bool tail = !blk_ok || (j + 1) * BT > ctx;
+    if (tail) {
+#pragma unroll
+      for (int i = 0; i < S::NI; ++i)
+        if (!blk_ok || j * BT + vt + S::RPI * i >= ctx) t.v[i] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < S::NI; ++i) {
+      const uint32_t w4[4] = {t.v[i].x, t.v[i].y, t.v[i].z, t.v[i].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (I8) {
+          uint32_t lo, hi;
+          i8x4_to_f16x4(w4[w], lo, hi);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            o[h][4 * w + 0] = fmaf(pv[i][h], lo_half(lo), o[h][4 * w + 0]);
+            o[h][4 * w + 1] = fmaf(pv[i][h], hi_half(lo), o[h][4 * w + 1]);
+            o[h][4 * w + 2] = fmaf(pv[i][h], lo_half(hi), o[h][4 * w + 2]);
+            o[h][4 * w + 3] = fmaf(pv[i][h], hi_half(hi), o[h][4 * w + 3]);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            o[h][2 * w + 0] = fmaf(pv[i][h], lo_half(w4[w]), o[h][2 * w + 0]);
+            o[h][2 * w + 1] = fmaf(pv[i][h], hi_half(w4[w]), o[h][2 * w + 1]);
+          }
+        }
+      }
+    }
+  };
+
+  // Double-buffered stream over this wave's tiles: in the steady state the
+  // next tile's loads are always issued before the current tile is used, so
+  // the wait before compute covers only the older tile.
+  if (n_my > 0) {
+    Tile ta, tb;
+    int it = 0;
+    load(0, ta);
+    for (; it + 2 < n_my; it += 2) {
+      load(it + 1, tb);
+      compute(first + WAVES * it, ta);
+      load(it + 2, ta);
+      compute(first + WAVES * (it + 1), tb);
+    }
+    if (it + 1 < n_my) {
+      load(it + 1, tb);
+      compute(first + WAVES * it, ta);
+      compute(first + WAVES * (it + 1), tb);
+    } else {
+      compute(first + WAVES * it, ta);
+    }
+  }
+
+  // wave totals: l over the 16 quads, o over the row groups
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l[h] = quads_sum(l[h]);
+#pragma unroll
+    for (int e = 0; e < S::CE; ++e)
+#pragma unroll
+      for (int mask = S::LPR; mask < 64; mask <<= 1) o[h][e] += xor_shfl(o[h][e], mask);
+  }
+  if (vt == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < S::CE; ++e) merge_o[wave][h][vd * S::CE + e] = o[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      merge_ml[wave][h][0] = m[h];
+      merge_ml[wave][h][1] = l[h];
+    }
+  }
+  __syncthreads();
+
+  // merge the 4 waves (fixed order) and write the partial or the final row
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) M = fmaxf(M, merge_ml[w][h][0]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      const float mw = merge_ml[w][h][0];
+      const float wt = (mw == -INFINITY) ? 0.0f : exp2_fast(mw - M);
+      L += merge_ml[w][h][1] * wt;
+      O += merge_o[w][h][d] * wt;
+    }
+    const int64_t row = int64_t(b) * Hq + g * G + h;
+    if (nparts == 1) {
+      prm.out[row * D + d] = (_Float16)(L > 0.0f ? O / L : 0.0f);
+    } else {
+      const int64_t pi = row * prm.max_parts + p;
+      prm.part_o[pi * D + d] = O;
+      if (d == 0) {
+        prm.part_m[pi] = M;
+        prm.part_l[pi] = L;
+      }
+    }
+  }
+}
+
+// Merge the partitions of one (sequence, query head) by log-sum-exp:
+// M = max m_p, out = sum o_p 2^(m_p - M) / sum l_p 2^(m_p - M). One thread per
+// output dim. Sequences with a single partition were finished by the split
+// kernel.
+__global__ __launch_bounds__(128) void lse_reduce_kernel(const float* __restrict__ part_m,
+                                                         const float* __restrict__ part_l,
+                                                         const float* __restrict__ part_o,
+                                                         const int32_t* __restrict__ ctx_lens,
+                                                         _Float16* __restrict__ out, int max_blocks,
+                                                         int max_context, int part_blocks, int max_parts,
+                                                         int D) {
+  const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
+  const int d = threadIdx.x;
+  const int ctx = clamp_ctx(ctx_lens[b], max_blocks, max_context);
+  if (ctx <= 0 || d >= D) return;
+  const int nblk = (ctx + BT - 1) / BT;
+  const int nparts = (nblk + part_blocks - 1) / part_blocks;
+  if (nparts <= 1) return;
+  const int64_t base = (int64_t(b) * Hq + h) * max_parts;
+  float M = -INFINITY;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, part_m[base + p]);
+  float L = 0.0f, O = 0.0f;
+  for (int p = 0; p < nparts; ++p) {
+    const float mp = part_m[base + p];
+    const float wt = (mp == -INFINITY) ? 0.0f : exp2_fast(mp - M);
+    L += part_l[base + p] * wt;
+    O += part_o[(base + p) * D + d] * wt;
+  }
+  out[(int64_t(b) * Hq + h) * D + d] = (_Float16)(L > 0.0f ? O / L : 0.0f);
+}
+
+// Plain coalesced read of a buffer, for an achievable-bandwidth reference.
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ buf, int64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    const uint4 v = buf[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never taken
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return pkv::fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Tokens per split-K partition: explicit, from PKV_PARTITION_TOKENS, or
+// chosen so that about 2048 work-groups (8 per CU) are in flight, with at
+// least 4 blocks (one per wave) per partition.
+int choose_part_blocks(const pkv_config& c, int B, int max_context, int partition_tokens) {
+  if (partition_tokens == 0) {
+    if (const char* env = std::getenv("PKV_PARTITION_TOKENS")) partition_tokens = std::atoi(env);
+  }
+  if (partition_tokens > 0) return std::min(partition_tokens, MAX_PARTITION_TOKENS) / BT;
+  const int nblk = (max_context + BT - 1) / BT;
+  const int64_t groups = int64_t(B) * c.num_kv_heads;
+  int64_t want_parts = (2048 + groups - 1) / groups;
+  if (want_parts < 1) want_parts = 1;
+  int pb = int((nblk + want_parts - 1) / want_parts);
+  if (pb < 4) pb = 4;
+  return std::min(pb, MAX_PARTITION_TOKENS / BT);
+}
+
+int max_parts_for(int max_context, int part_blocks) {
+  const int nblk = (max_context + BT - 1) / BT;
+  return (nblk + part_blocks - 1) / part_blocks;
+}
+
+typedef void (*decode_fn)(DecodeParams);
+
+template <int D, bool I8>
+decode_fn pick_g(int G) {
+  switch (G) {
+    case 1: return paged_decode_kernel<D, 1, I8>;
+    case 2: return paged_decode_kernel<D, 2, I8>;
+    case 4: return paged_decode_kernel<D, 4, I8>;
+    case 8: return paged_decode_kernel<D, 8, I8>;
+    default: return nullptr;
+  }
+}
+
+decode_fn pick_kernel(int D, int G, bool i8) {
+  if (D == 128) return i8 ? pick_g<128, true>(G) : pick_g<128, false>(G);
+  if (D == 64) return i8 ? pick_g<64, true>(G) : pick_g<64, false>(G);
+  return nullptr;
+}
+
+int check_partition_tokens(int partition_tokens) {
+  if (partition_tokens < 0 || partition_tokens % BT || partition_tokens > MAX_PARTITION_TOKENS)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "partition_tokens must be a multiple of 16 in [0, %d] (got %d)",
+                     MAX_PARTITION_TOKENS, partition_tokens);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_copy_blocks(const pkv_config* cfg, void* pool_dev, const int32_t* pairs_dev, int32_t n, void* stream) {
+  int st = pkv::validate_config(cfg);
+  if (st != PKV_OK) return st;
+  if (n < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "n must be >= 0");
+  if (n == 0) return PKV_OK;
+  if (!pool_dev || !pairs_dev) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned16(pool_dev)) return pkv::fail(PKV_ERR_INVALID_ARG, "pool must be 16-byte aligned");
+  if (n > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "at most 65535 pairs per call");
+  const int64_t E = pkv::elem_bytes(cfg->dtype);
+  const int64_t slab = int64_t(cfg->num_kv_heads) * pkv::tile_elems(*cfg) * E;
+  const int64_t layer_bytes = pkv::layer_elems(*cfg) * E;
+  dim3 grid(n, cfg->num_layers, 3);
+  hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<char*>(pool_dev), pairs_dev, cfg->num_blocks, slab, layer_bytes,
+                     pkv::region_bytes(*cfg), int64_t(cfg->num_kv_heads) * 2 * 2, cfg->dtype == PKV_I8 ? 1 : 0);
+  return hip_status(hipGetLastError(), "copy_blocks launch");
+}
+
+int pkv_append_kv(const pkv_config* cfg, void* pool_dev, int32_t layer, const void* k_dev, const void* v_dev,
+                  const int32_t* slots_dev, int32_t n_tokens, void* stream) {
+  int st = pkv::validate_config(cfg);
+  if (st != PKV_OK) return st;
+  if (cfg->dtype != PKV_F16) return pkv::fail(PKV_ERR_UNSUPPORTED, "append_kv writes fp16 pools only");
+  if (layer < 0 || layer >= cfg->num_layers) return pkv::fail(PKV_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (n_tokens < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (n_tokens == 0) return PKV_OK;
+  if (!pool_dev || !k_dev || !v_dev || !slots_dev) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned16(pool_dev) || !aligned16(k_dev) || !aligned16(v_dev))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "pool, k and v must be 16-byte aligned");
+  const int64_t layer_bytes = pkv::layer_elems(*cfg) * 2;
+  char* base = static_cast<char*>(pool_dev);
+  uint4* Kl = reinterpret_cast<uint4*>(base + layer * layer_bytes);
+  uint4* Vl = reinterpret_cast<uint4*>(base + pkv::region_bytes(*cfg) + layer * layer_bytes);
+  const int64_t threads = int64_t(n_tokens) * cfg->num_kv_heads * (cfg->head_dim / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "too many tokens in one call");
+  hipLaunchKernelGGL(append_kv_f16_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     Kl, Vl, static_cast<const uint4*>(k_dev), static_cast<const uint4*>(v_dev), slots_dev,
+                     n_tokens, cfg->num_kv_heads, cfg->head_dim, cfg->num_blocks);
+  return hip_status(hipGetLastError(), "append_kv launch");
+}
+
+int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t max_context, int32_t partition_tokens) {
+  int st = pkv::validate_config(cfg);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 1 || num_q_heads < 1 || max_context < 1)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_seqs, num_q_heads and max_context must be >= 1");
+  st = check_partition_tokens(partition_tokens);
+  if (st != PKV_OK) return st;
+  const int pb = choose_part_blocks(*cfg, num_seqs, max_context, partition_tokens);
+  const int mp = max_parts_for(max_context, pb);
+  if (mp <= 1) return 0;
+  return int64_t(num_seqs) * num_q_heads * mp * (cfg->head_dim + 2) * int64_t(sizeof(float));
+}
+
+int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  int st = pkv::validate_config(a->cfg);
+  if (st != PKV_OK) return st;
+  const pkv_config& c = *a->cfg;
+  if (!a->pool_dev || !a->q_dev || !a->block_tables_dev || !a->ctx_lens_dev || !a->out_dev)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned16(a->pool_dev) || !aligned16(a->q_dev))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "pool and q must be 16-byte aligned");
+  if (a->layer < 0 || a->layer >= c.num_layers)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "layer %d out of range", a->layer);
+  if (a->num_seqs < 1 || a->num_seqs > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "num_seqs must be in [1, 65535]");
+  if (a->num_q_heads < 1 || a->num_q_heads % c.num_kv_heads)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", a->num_q_heads,
+                     c.num_kv_heads);
+  if (a->max_blocks < 1 || a->max_context < 1)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks and max_context must be >= 1");
+  st = check_partition_tokens(a->partition_tokens);
+  if (st != PKV_OK) return st;
+  const int G = a->num_q_heads / c.num_kv_heads;
+  decode_fn fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8);
+  if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", G);
+  if (c.num_kv_heads > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
+  if (a->ctx_lens_host) {
+    const int64_t cap = std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context);
+    for (int b = 0; b < a->num_seqs; ++b) {
+      const int32_t n = a->ctx_lens_host[b];
+      if (n < 1 || n > cap)
+        return pkv::fail(PKV_ERR_INVALID_ARG, "context_len[%d] = %d outside [1, %lld]", b, n, (long long)cap);
+    }
+  }
+  const int pb = choose_part_blocks(c, a->num_seqs, a->max_context, a->partition_tokens);
+  const int mp = max_parts_for(a->max_context, pb);
+  const int64_t need = mp <= 1 ? 0 : int64_t(a->num_seqs) * a->num_q_heads * mp * (c.head_dim + 2) * 4;
+  if (need > 0 && (!a->workspace_dev || a->workspace_bytes < need))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "workspace too small: need %lld bytes", (long long)need);
+
+  const int64_t E = pkv::elem_bytes(c.dtype);
+  const int64_t layer_bytes = pkv::layer_elems(c) * E;
+  const char* base = static_cast<const char*>(a->pool_dev);
+  DecodeParams prm;
+  prm.K = base + a->layer * layer_bytes;
+  prm.V = base + pkv::region_bytes(c) + a->layer * layer_bytes;
+  prm.scales = c.dtype == PKV_I8
+                   ? reinterpret_cast<const _Float16*>(base + 2 * pkv::region_bytes(c) +
+                                                     int64_t(a->layer) * c.num_blocks * c.num_kv_heads * 2 * 2)
+                   : nullptr;
+  prm.q = static_cast<const _Float16*>(a->q_dev);
+  prm.tables = a->block_tables_dev;
+  prm.ctx_lens = a->ctx_lens_dev;
+  const int64_t rows = int64_t(a->num_seqs) * a->num_q_heads * mp;
+  float* ws = static_cast<float*>(a->workspace_dev);
+  prm.part_m = need ? ws : nullptr;
+  prm.part_l = need ? ws + rows : nullptr;
+  prm.part_o = need ? ws + 2 * rows : nullptr;
+  prm.out = static_cast<_Float16*>(a->out_dev);
+  prm.max_blocks = a->max_blocks;
+  prm.num_blocks = c.num_blocks;
+  prm.Hkv = c.num_kv_heads;
+  prm.part_blocks = pb;
+  prm.max_parts = mp;
+  prm.max_context = a->max_context;
+  prm.scale_log2 = a->scale * LOG2E;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  if (a->timing_events)
+    for (int i = 0; i < 4; ++i) ev[i] = static_cast<hipEvent_t>(a->timing_events[i]);
+  const dim3 grid(mp, c.num_kv_heads, a->num_seqs);
+  if (ev[0] && ev[1])
+    hipExtLaunchKernelGGL(fn, grid, dim3(256), 0, s, ev[0], ev[1], 0, prm);
+  else
+    hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, prm);
+  st = hip_status(hipGetLastError(), "paged_decode launch");
+  if (st != PKV_OK || mp <= 1) return st;
+  const dim3 rgrid(a->num_q_heads, a->num_seqs);
+  if (ev[2] && ev[3])
+    hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, ev[2], ev[3], 0, prm.part_m,
+                          prm.part_l, prm.part_o, a->ctx_lens_dev, prm.out, a->max_blocks, a->max_context, pb,
+                          mp, c.head_dim);
+  else
+    hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, prm.part_m, prm.part_l, prm.part_o,
+                       a->ctx_lens_dev, prm.out, a->max_blocks, a->max_context, pb, mp, c.head_dim);
+  return hip_status(hipGetLastError(), "lse_reduce launch");
+}
+
+int pkv_probe_stream_read(const void* buf_dev, int64_t bytes, void* sink_dev, void* stream) {
+  if (!buf_dev || !sink_dev || bytes < 16 || !aligned16(buf_dev))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "bad probe arguments");
+  hipLaunchKernelGGL(stream_read_kernel, dim3(256 * 16), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(buf_dev), bytes / 16, static_cast<uint32_t*>(sink_dev));
+  return hip_status(hipGetLastError(), "stream_read launch");
+}
+
+}  // extern "C"

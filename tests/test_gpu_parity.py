@@ -1,0 +1,332 @@
+"""Parity of the HIP path with the CPU oracle, on an MI355X.
+
+Bars: every stored byte, table, length, slot and copy-on-write pair
+bit-exact; fp16 decode output within 2e-3 max abs of the fp64 oracle; int8
+within 2e-2 of the fp64 oracle on the dequantised values. Each test prints
+the case it runs before touching the GPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_392_amd as pkv
+import workloads
+from lib_driver import LibRun
+from oracle_driver import OracleRun
+
+pytestmark = pytest.mark.gpu
+
+F16_TOL = 2e-3
+I8_TOL = 2e-2
+DEV = "cuda:0"
+
+
+def announce(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+def live_slots(o):
+    """(block, offset) of every token held by a live sequence of the oracle run."""
+    out = set()
+    for sid, table in o.alloc.tables.items():
+        n = o.alloc.lens[sid]
+        for t in range(n):
+            out.add((table[t // 16], t % 16))
+    return out
+
+
+def check_stored_bytes(lib, o):
+    K = lib.cache.region(0, 0).cpu().numpy()
+    V = lib.cache.region(1, 0).cpu().numpy()
+    for blk, off in sorted(live_slots(o)):
+        assert np.array_equal(K[blk, :, off].view(np.uint16), o.cache.K[0, blk, :, off].view(np.uint16)), (blk, off)
+        assert np.array_equal(V[blk, :, off].view(np.uint16), o.cache.V[0, blk, :, off].view(np.uint16)), (blk, off)
+
+
+def check_host_records(lib, o):
+    assert len(lib.reserves) == len(o.reserves)
+    for a, b in zip(lib.reserves, o.reserves):
+        assert a == b
+    for a, b in zip(lib.decodes, o.decodes):
+        np.testing.assert_array_equal(a["tables"], b["tables"])
+        np.testing.assert_array_equal(a["lens"], b["lens"])
+
+
+def max_err(lib, o):
+    errs = []
+    for a, b in zip(lib.decodes, o.decodes):
+        assert a["out"].dtype == np.float16
+        assert np.isfinite(a["out"]).all()
+        errs.append(float(np.abs(a["out"].astype(np.float64) - b["out"]).max()))
+    return max(errs)
+
+
+def run_pair(w, poison=True, **kw):
+    announce(f"{w.name} seed={w.seed} B-shape Hq={w.num_q_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
+             f"N={w.num_blocks} dtype={w.dtype} {kw}")
+    o = OracleRun(w).run()
+    lib = LibRun(w, device=DEV, poison=poison, quantised=o.q8).run(**kw)
+    return lib, o
+
+
+# ---------------------------------------------------------------------------
+# append + decode parity on the configs
+
+def test_c1_append_bitwise_and_decode():
+    lib, o = run_pair(workloads.c1_tiny())
+    check_host_records(lib, o)
+    check_stored_bytes(lib, o)
+    assert max_err(lib, o) <= F16_TOL
+    lib.close()
+
+
+def test_c2_exact_fit_pool():
+    lib, o = run_pair(workloads.c2_llama_b8())
+    check_host_records(lib, o)
+    check_stored_bytes(lib, o)
+    assert pkv.pkv_num_free(lib.handle) == 0
+    assert max_err(lib, o) <= F16_TOL
+    lib.close()
+
+
+def test_c3_fragmented_mixed_lengths():
+    lib, o = run_pair(workloads.c3_mixed())
+    check_host_records(lib, o)
+    check_stored_bytes(lib, o)
+    assert max_err(lib, o) <= F16_TOL
+    lib.close()
+
+
+def test_c4_prefix_sharing_and_cow():
+    w = workloads.c4_prefix()
+    lib, o = run_pair(w)
+    check_host_records(lib, o)
+    # the copy-on-write block copy and the child's append, byte for byte
+    check_stored_bytes(lib, o)
+    assert max_err(lib, o) <= F16_TOL
+    lib.close()
+
+
+def test_c5_int8():
+    w = workloads.c5_int8()
+    lib, o = run_pair(w)
+    check_host_records(lib, o)
+    err = max_err(lib, o)
+    announce(f"c5 int8 max abs err vs dequantised oracle {err:.3g}")
+    assert err <= I8_TOL
+    lib.close()
+
+
+@pytest.mark.parametrize("seed,Hq,Hkv,D", [
+    (1, 4, 2, 64), (2, 4, 4, 64), (3, 8, 1, 64), (4, 8, 2, 128), (5, 32, 8, 128),
+    (6, 16, 2, 128), (7, 3, 3, 128), (8, 8, 4, 64),
+])
+def test_tiny_shapes(seed, Hq, Hkv, D):
+    w = workloads.tiny_random(700 + seed, B=5, Hq=Hq, Hkv=Hkv, D=D, max_len=300)
+    lib, o = run_pair(w)
+    check_host_records(lib, o)
+    check_stored_bytes(lib, o)
+    assert max_err(lib, o) <= F16_TOL
+    lib.close()
+
+
+@pytest.mark.parametrize("seed,Hq,Hkv,D", [(1, 4, 2, 64), (2, 32, 8, 128), (3, 8, 1, 128)])
+def test_tiny_int8(seed, Hq, Hkv, D):
+    w = workloads.tiny_random(800 + seed, B=4, Hq=Hq, Hkv=Hkv, D=D, max_len=200, dtype="i8")
+    lib, o = run_pair(w)
+    assert max_err(lib, o) <= I8_TOL
+    lib.close()
+
+
+@pytest.mark.parametrize("ptok", [16, 64, 128, 256, 512, 4096])
+def test_partition_size_within_tolerance(ptok):
+    w = workloads.tiny_random(901, B=6, Hq=8, Hkv=2, D=128, max_len=1500)
+    lib, o = run_pair(w, partition_tokens=ptok)
+    assert max_err(lib, o) <= F16_TOL
+    lib.close()
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU
+
+def test_physical_permutation_is_bitwise_invariant():
+    outs = []
+    for k in range(3):
+        w = workloads.tiny_random(1001, B=5, Hq=8, Hkv=2, D=128, max_len=700)
+        if k:
+            w.free_order = np.random.default_rng(k).permutation(w.num_blocks).astype(np.int32)
+        announce(f"permutation {k}")
+        lib = LibRun(w, device=DEV, poison=True).run()
+        outs.append((lib.decodes[0]["tables"], lib.decodes[0]["out"]))
+        lib.close()
+    assert not np.array_equal(outs[0][0], outs[1][0])
+    for t, out in outs[1:]:
+        assert np.array_equal(out.view(np.uint16), outs[0][1].view(np.uint16))
+
+
+def test_run_to_run_bitwise_determinism():
+    w = workloads.tiny_random(1002, B=4, Hq=32, Hkv=8, D=128, max_len=3000)
+    announce("determinism")
+    lib = LibRun(w, device=DEV).run()
+    first = lib.decodes[0]["out"]
+    rec = lib.decodes[0]
+    td = torch.from_numpy(rec["tables"]).to(DEV)
+    ld = torch.from_numpy(rec["lens"]).to(DEV)
+    qd = torch.from_numpy(rec["q"]).to(DEV)
+    for _ in range(5):
+        out = lib.cache.paged_decode(qd, td, ld, context_lens_host=rec["lens"]).cpu().numpy()
+        assert np.array_equal(out.view(np.uint16), first.view(np.uint16))
+    lib.close()
+
+
+def test_shared_prefix_equals_private_copy_bitwise():
+    rng = np.random.default_rng(77)
+    Hkv, D, Hq = 8, 128, 32
+    prefix = 700
+    pk = rng.standard_normal((prefix, Hkv, D), dtype=np.float32).astype(np.float16)
+    pv = rng.standard_normal((prefix, Hkv, D), dtype=np.float32).astype(np.float16)
+    suf = [(rng.standard_normal((n, Hkv, D), dtype=np.float32).astype(np.float16),
+            rng.standard_normal((n, Hkv, D), dtype=np.float32).astype(np.float16)) for n in (5, 300)]
+    q = torch.from_numpy(rng.standard_normal((2, Hq, D), dtype=np.float32).astype(np.float16)).to(DEV)
+    announce("shared prefix vs private copy")
+    outs = []
+    for shared in (True, False):
+        c = pkv.PagedKVCache(1, 200, Hkv, D, free_order=rng.permutation(200).astype(np.int32), device=DEV)
+        c.pool.view(torch.float16).fill_(float("nan"))
+        if shared:
+            p = c.create_seq()
+            c.append_kv(p, torch.from_numpy(pk).to(DEV), torch.from_numpy(pv).to(DEV))
+            seqs = [p, c.fork(p)]
+        else:
+            seqs = [c.create_seq(), c.create_seq()]
+            for s in seqs:
+                c.append_kv(s, torch.from_numpy(pk).to(DEV), torch.from_numpy(pv).to(DEV))
+        for s, (k, v) in zip(seqs, suf):
+            c.append_kv(s, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV))
+        tables, lens = c.block_tables(seqs)
+        out = c.paged_decode(q, torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV),
+                             context_lens_host=lens)
+        outs.append(out.cpu().numpy())
+        c.close()
+    assert np.isfinite(outs[0]).all()
+    assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+
+
+def test_single_token_returns_its_value_exactly():
+    rng = np.random.default_rng(5)
+    c = pkv.PagedKVCache(1, 4, 2, 128, device=DEV)
+    c.pool.view(torch.float16).fill_(float("nan"))
+    s = c.create_seq()
+    k = torch.from_numpy(rng.standard_normal((1, 2, 128), dtype=np.float32).astype(np.float16)).to(DEV)
+    v = torch.from_numpy(rng.standard_normal((1, 2, 128), dtype=np.float32).astype(np.float16)).to(DEV)
+    announce("single token")
+    c.append_kv(s, k, v)
+    tables, lens = c.block_tables([s])
+    q = torch.from_numpy(rng.standard_normal((1, 8, 128), dtype=np.float32).astype(np.float16)).to(DEV)
+    out = c.paged_decode(q, torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV),
+                         context_lens_host=lens).cpu()
+    # p = 2^0 = 1 for the only token: the output is V_0 bit for bit
+    for h in range(8):
+        assert torch.equal(out[0, h], v[0, h // 4].cpu())
+    c.close()
+
+
+def test_zero_query_gives_mean():
+    rng = np.random.default_rng(6)
+    n = 1000
+    c = pkv.PagedKVCache(1, 70, 1, 64, device=DEV)
+    s = c.create_seq()
+    k = rng.standard_normal((n, 1, 64), dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal((n, 1, 64), dtype=np.float32).astype(np.float16)
+    announce("zero query")
+    c.append_kv(s, torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV))
+    tables, lens = c.block_tables([s])
+    q = torch.zeros((1, 4, 64), dtype=torch.float16, device=DEV)
+    out = c.paged_decode(q, torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV),
+                         context_lens_host=lens).cpu().numpy().astype(np.float64)
+    mean = v[:, 0].astype(np.float64).mean(0)
+    for h in range(4):
+        assert np.abs(out[0, h] - mean).max() <= F16_TOL
+    c.close()
+
+
+@pytest.mark.parametrize("lens", [[1], [16], [17], [15, 16, 17, 31, 32, 33], [4096], [4097, 1, 2]])
+def test_edge_lengths(lens):
+    rng = np.random.default_rng(sum(lens))
+    Hkv, D, Hq = 2, 128, 8
+    N = sum(-(-n // 16) for n in lens) + 2
+    w = workloads.Workload("edge", N, Hq, Hkv, D, "f16", rng.permutation(N).astype(np.int32))
+    names = [f"s{i}" for i in range(len(lens))]
+    for s in names:
+        w.steps.append(("create", s))
+    for s, n in zip(names, lens):
+        k = rng.standard_normal((n, Hkv, D), dtype=np.float32).astype(np.float16)
+        w.steps.append(("prefill", s, k, rng.standard_normal((n, Hkv, D), dtype=np.float32).astype(np.float16)))
+    w.steps.append(("decode", names, rng.standard_normal((len(lens), Hq, D), dtype=np.float32).astype(np.float16)))
+    for ptok in (0, 16, 256):
+        lib, o = run_pair(w, partition_tokens=ptok)
+        check_stored_bytes(lib, o)
+        assert max_err(lib, o) <= F16_TOL
+        lib.close()
+
+
+def test_copy_blocks_all_layers_and_scales():
+    rng = np.random.default_rng(9)
+    for dtype in ("f16", "i8"):
+        c = pkv.PagedKVCache(3, 6, 2, 64, dtype=dtype, device=DEV)
+        src = torch.from_numpy(rng.integers(0, 256, c.nbytes, dtype=np.uint8)).to(DEV)
+        c.pool.copy_(src)
+        announce(f"copy_blocks {dtype}")
+        c.copy_blocks(np.array([[1, 4], [2, 0]], np.int32))
+        torch.cuda.synchronize()
+        for which in (0, 1):
+            r = c.region(which).cpu().numpy()
+            before = src.cpu().numpy()
+            rb = c._region_bytes()
+            e = 1 if dtype == "i8" else 2
+            orig = before[which * rb:(which + 1) * rb].view(np.int8 if e == 1 else np.float16).reshape(r.shape)
+            expect = orig.copy()
+            expect[:, 4] = orig[:, 1]
+            expect[:, 0] = orig[:, 2]
+            assert np.array_equal(r.view(np.uint8), expect.view(np.uint8))
+        if dtype == "i8":
+            s = c.scales().cpu().numpy()
+            rb = c._region_bytes()
+            orig = src.cpu().numpy()[2 * rb:].view(np.float16).reshape(s.shape)
+            expect = orig.copy()
+            expect[:, 4] = orig[:, 1]
+            expect[:, 0] = orig[:, 2]
+            assert np.array_equal(s.view(np.uint16), expect.view(np.uint16))
+        c.close()
+
+
+# ---------------------------------------------------------------------------
+# the headline workload at full size, in the benchmark's launch configuration
+
+def test_headline_full_size_sampled():
+    w = workloads.headline()
+    announce("headline B16 ctx 8192+1, 32q/8kv d128 fp16 (auto partitions)")
+    o = OracleRun(w).run(decode=False)
+    lib = LibRun(w, device=DEV, poison=True).run()
+    check_host_records(lib, o)
+    rec = lib.decodes[0]
+    out = rec["out"]
+    assert np.isfinite(out).all()
+    rng = np.random.default_rng(0)
+    cache = o.cache
+    errs = []
+    for b in range(16):
+        for h in rng.choice(32, 4, replace=False):
+            g = h // 4
+            n = int(rec["lens"][b])
+            Kc = oracle.gather(cache.K, 0, rec["tables"][b], n, g)
+            Vc = oracle.gather(cache.V, 0, rec["tables"][b], n, g)
+            ref = oracle.decode_seq_head(Kc, Vc, rec["q"][b, h], w.scale)
+            errs.append(np.abs(out[b, h].astype(np.float64) - ref).max())
+    announce(f"headline sampled max abs err {max(errs):.3g}")
+    assert max(errs) <= F16_TOL
+    lib.close()
