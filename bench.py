@@ -46,7 +46,26 @@ def parse():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB three times (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain elementwise copy kernel (x * 1) of exactly 2**30 bytes in and
+    2**30 bytes out, three times, on cuda:0: under rocprofv3 --pmc its
+    FETCH_SIZE and WRITE_SIZE per dispatch give the factor between the
+    counters and true HBM bytes. (An elementwise kernel rather than
+    Tensor.copy_, which may become a DMA transfer that the counters miss.)"""
+    import torch
+    n = 2**30
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 3}), flush=True)
 
 
 def kernel_source_hash():
@@ -78,6 +97,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
