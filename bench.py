@@ -14,9 +14,10 @@ Printed: one JSON line. ``value`` is whole-step throughput in GB/s of
 algorithmic bytes (K/V read by decode, q, tables, out, appended K/V read and
 written); ``decode_tok_s`` is batch / step time (attention only);
 ``roofline`` is the split-K decode kernel's algorithmic bytes per launch
-over its average duration, timed with HIP events recorded around that
-kernel alone on its own stream; ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same workload.
+over its average duration, from HIP events recorded around that kernel on
+its launch stream for one decode per timed step (the layer rotating with the
+step); ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload.
 """
 
 import argparse
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every layer directly instead of replaying layers 1.. as one HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -110,7 +113,7 @@ def main():
 
     dev = torch.device("cuda:0")
     K, W, L = args.steps, args.warmup, args.layers
-    total_steps = K + W
+    total_steps = K + W + 1
     spare = B * (-(-(total_steps + 1) // 16))
     w = workloads.headline(spare_blocks=spare)
     N = w.num_blocks
@@ -153,19 +156,17 @@ def main():
     vnew[0, 0].copy_(torch.from_numpy(first_v))
     qall[0].copy_(torch.from_numpy(first_q))
     out = torch.empty((L, B, HQ, D), dtype=torch.float16, device=dev)
-    max_ctx_final = CTX + total_steps
-    ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, HQ, max_ctx_final, args.partition_tokens)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, HQ, max_blocks * 16, args.partition_tokens)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     # per-step pinned upload buffers (a step's buffer is never reused while its
     # copy may still be queued)
-    slots_h = torch.empty((total_steps, B), dtype=torch.int32).pin_memory()
     tables_h = torch.empty((total_steps, B, max_blocks), dtype=torch.int32).pin_memory()
     lens_h = torch.empty((total_steps, B), dtype=torch.int32).pin_memory()
-    slots_d = torch.empty((B,), dtype=torch.int32, device=dev)
     tables_d = torch.empty((B, max_blocks), dtype=torch.int32, device=dev)
     lens_d = torch.empty((B,), dtype=torch.int32, device=dev)
     seq_arr = np.array(seqs, np.int64)
+    cap = max_blocks * 16  # table width in tokens: the graph's max_context
 
     # prebuilt decode argument blocks, one per layer
     argv = []
@@ -188,9 +189,10 @@ def main():
         a.timing_events = None
         argv.append(a)
 
-    # timing events around the split kernel and the merge kernel of every
-    # timed decode (recorded once so each owns a HIP event)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K * L)]
+    # timing events around the split and merge kernels of layer 0's decode in
+    # every timed step (an event pair costs a few µs of queue time, so the
+    # other decodes run without); recorded once so each owns a HIP event
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     for group in ev:
         for e in group:
             e.record()
@@ -204,37 +206,42 @@ def main():
     ncow = ctypes.c_int32()
     step_lens = []
 
-    def one_step(i, timed_index):
-        # a1: reserve one slot per sequence (host allocator)
-        sl = slots_h[i].numpy()
+    def prepare(i):
+        """a1: reserve one slot per sequence (host allocator; the kernel finds
+        the slot through the table); a2: pack and upload tables and lengths."""
         for b in range(B):
             st = lib_reserve(cache.handle, int(seq_arr[b]), 1, C._i32p(slot1), C._i32p(cow), 1, ctypes.byref(ncow))
             if st != 0 or ncow.value:
                 raise RuntimeError(f"reserve failed ({st}) or unexpected copy-on-write")
-            sl[b] = slot1[0]
-        # a2: pack and upload the tables, lengths and slots
         th, lh = tables_h[i].numpy(), lens_h[i].numpy()
         C._check(lib.pkv_build_block_tables(cache.handle, seq_arr.ctypes.data_as(C._p_i64), B, max_blocks,
                                             C._i32p(th), C._i32p(lh)))
         step_lens.append(lh.copy())
-        slots_d.copy_(slots_h[i], non_blocking=True)
-        tables_d.copy_(tables_h[i], non_blocking=True)
-        lens_d.copy_(lens_h[i], non_blocking=True)
+        # uploaded by the library's kernel, on the compute queue
+        C._check(lib.pkv_upload(tables_d.data_ptr(), tables_h[i].data_ptr(), tables_d.numel() * 4, sp))
+        C._check(lib.pkv_upload(lens_d.data_ptr(), lens_h[i].data_ptr(), B * 4, sp))
+        return lh
+
+    def launch(layer, i, lh, max_context, events=None, stream_handle=None):
+        """a4 + a5 (+ a6): one decode launch with the new token's K/V appended
+        inside it, and the merge kernel."""
+        a = argv[layer]
+        a.max_context = max_context
+        a.ctx_lens_host = C._i32p(lh)
+        a.k_new_dev = knew[i, layer].data_ptr()
+        a.v_new_dev = vnew[i, layer].data_ptr()
+        a.timing_events = events
+        C._check(lib.pkv_paged_decode(ctypes.byref(a), sp if stream_handle is None else stream_handle))
+
+    def eager_step(i, events=None):
+        lh = prepare(i)
         mc = int(lh.max())
         for layer in range(L):
-            # a4: append the new token's K/V; a5 + a6: paged decode
-            C._check(lib.pkv_append_kv(ctypes.byref(cache.cfg), cache.pool.data_ptr(), layer,
-                                       knew[i, layer].data_ptr(), vnew[i, layer].data_ptr(),
-                                       slots_d.data_ptr(), B, sp))
-            a = argv[layer]
-            a.max_context = mc
-            a.ctx_lens_host = C._i32p(lh)
-            a.timing_events = ev_ptrs[timed_index * L + layer] if timed_index is not None else None
-            C._check(lib.pkv_paged_decode(ctypes.byref(a), sp))
+            launch(layer, i, lh, mc, events if layer == 0 else None)
 
     print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
     for i in range(W):
-        one_step(i, None)
+        eager_step(i)
         if i == 0:
             torch.cuda.synchronize()
             first_out = out[0].float().cpu().numpy()
@@ -242,21 +249,60 @@ def main():
             first_lens = lens_h[0].numpy().copy()
     torch.cuda.synchronize()
 
-    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    graph = None
+    if not args.eager:
+        # layers 1..L-1 of a step as one HIP graph: grids sized for the table
+        # width, lengths and tables read from the device buffers at replay;
+        # the appended rows come from step 0's buffers (values do not matter
+        # for timing; layer 0, which carries the seeded workload, stays eager)
+        graph = torch.cuda.CUDAGraph()
+        lh_cap = lens_h[W - 1].numpy()
+        with torch.cuda.graph(graph):
+            cs = torch.cuda.current_stream().cuda_stream
+            for layer in range(1, L):
+                launch(layer, 0, lh_cap, cap, stream_handle=cs)
+        torch.cuda.synchronize()
+
+    def graph_step(i, events=None):
+        lh = prepare(i)
+        launch(0, i, lh, int(lh.max()), events)
+        graph.replay()
+
+    step_fn = eager_step if graph is None else graph_step
+    step_fn(W)  # one untimed step in the timed mode (first graph replay)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {K} steps ({'eager' if graph is None else 'layer 0 eager + graph'})",
+          file=sys.stderr, flush=True)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
+    h0 = time.perf_counter()
     for i in range(K):
-        one_step(W + i, i)
+        step_fn(W + 1 + i, ev_ptrs[i])
+    host_ms = (time.perf_counter() - h0) * 1e3 / K
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
     ms_per_step = total_ms / K
 
+    # the last graph step's outputs against eager launches of the same layers
+    # (the appended rows are rewritten with the same bytes)
+    graph_matches_eager = None
+    if graph is not None:
+        lh = lens_h[W + K].numpy()
+        check_layers = [1, L // 2, L - 1] if L > 2 else list(range(1, L))
+        got = {l: out[l].clone() for l in check_layers}
+        for l in check_layers:
+            launch(l, 0, lh, int(lh.max()))
+        torch.cuda.synchronize()
+        graph_matches_eager = all(torch.equal(got[l].view(torch.int16), out[l].view(torch.int16))
+                                  for l in check_layers)
+
     split_ms = np.array([g[0].elapsed_time(g[1]) for g in ev])
     merge_ms = np.array([g[2].elapsed_time(g[3]) for g in ev])
-    timed_lens = step_lens[W:]
+    timed_lens = step_lens[W + 1:]
 
     # algorithmic bytes
     kv_tok = 2 * HKV * D * 2  # K and V of one token, one layer, fp16
@@ -267,13 +313,12 @@ def main():
         nblk = (lens + 15) // 16
         b = int(lens.sum()) * kv_tok + nb * HQ * D * 2 + int(nblk.sum()) * 4 + nb * 4
         return b + (nb * HQ * D * 2 if with_out else 0)
-    append_bytes = 2 * (B * HKV * D * 2) * 2 + B * 4  # k, v read and written; slots
-    upload_bytes = B * max_blocks * 4 + 2 * B * 4
+    append_bytes = 2 * (B * HKV * D * 2) * 2  # the new k and v rows, read and written
+    upload_bytes = B * max_blocks * 4 + B * 4  # tables and lengths
     step_bytes = [L * (decode_bytes(l) + append_bytes) + upload_bytes for l in timed_lens]
-    split_bytes = np.repeat([decode_bytes(l, with_out=False) for l in timed_lens], L)
+    split_bytes = np.array([decode_bytes(l, with_out=False) for l in timed_lens])
     value = float(np.sum(step_bytes) / (total_ms * 1e-3) / 1e9)
     split_gbps = float(np.mean(split_bytes) / (np.mean(split_ms) * 1e-3) / 1e9)
-    decode_gbps = float(np.mean(split_bytes + B * HQ * D * 2) / (np.mean(split_ms + merge_ms) * 1e-3) / 1e9)
 
     # HBM probe: a plain coalesced read in the same run
     probe = None
@@ -315,13 +360,21 @@ def main():
         },
         "decode_tok_s": round(B / (ms_per_step * 1e-3), 1),
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBPS, 2),
-        "decode_kernels_GBps": round(decode_gbps, 1),
         "split_kernel_us": round(float(np.mean(split_ms)) * 1e3, 2),
+        "split_kernel_us_p10_p90": [round(float(np.percentile(split_ms, 10)) * 1e3, 2),
+                                    round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
         "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2),
+        "timed_launch_samples": int(len(split_ms)),
+        "execution": ("per step: host slot reservation and table packing, table upload, layer 0 "
+                      "launched directly (timing events), " +
+                      ("layers 1.. directly" if graph is None else f"layers 1..{L - 1} as one HIP graph replay") +
+                      "; the append runs inside the decode kernel"),
+        "graph_matches_eager_bitwise": graph_matches_eager,
+        "host_issue_ms_per_step": round(host_ms, 4),
         "probe_read_GBps": None if probe is None else round(probe, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel<128,4,f16> (split-K)",
+            "kernel": "paged_decode_kernel<128,4,f16> (split-K decode)",
             "achieved": round(split_gbps, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

@@ -148,7 +148,8 @@ int pkv_append_kv(const pkv_config* cfg, void* pool_dev, int32_t layer, const vo
  * block table). */
 typedef struct pkv_decode_args {
   const pkv_config* cfg;
-  const void* pool_dev;           /* the pool, layout above                       */
+  const void* pool_dev;           /* the pool, layout above (written only by the
+                                     fused append below)                         */
   int32_t layer;                  /* 0 <= layer < L                               */
   const void* q_dev;              /* fp16 [B][Hq][D]                              */
   int32_t num_seqs;               /* B >= 1                                       */
@@ -164,6 +165,15 @@ typedef struct pkv_decode_args {
   int64_t workspace_bytes;        /* >= pkv_decode_workspace_bytes(...)           */
   int32_t partition_tokens;       /* tokens per split-K partition, a multiple of
                                      16 in [16, 4096]; 0 = automatic             */
+  const void* k_new_dev;          /* optional fused append (NULL = none, the
+                                     default): fp16 [B][Hkv][D] k and v of one new
+                                     token per sequence, stored first at logical
+                                     position ctx_lens[b] - 1 of sequence b (the
+                                     slot pkv_seq_reserve gave that token; any
+                                     copy-on-write pairs already copied), then
+                                     attended like every other token. Same bytes
+                                     as pkv_append_kv. fp16 pools only.          */
+  const void* v_new_dev;
   void* const* timing_events;     /* optional (NULL = none): 4 hipEvent_t recorded
                                      around the split kernel ([0] start, [1] stop)
                                      and the merge kernel ([2], [3]; untouched if
@@ -171,25 +181,52 @@ typedef struct pkv_decode_args {
                                      only; the result does not depend on it.     */
 } pkv_decode_args;
 
-/* Workspace bytes pkv_paged_decode needs for these sizes (0 is possible).
- * Returns < 0 (a status) on bad arguments. partition_tokens 0 = the same
- * automatic choice pkv_paged_decode makes. */
+/* Workspace bytes pkv_paged_decode needs for these sizes (0 when every
+ * sequence fits one partition). Returns < 0 (a status) on bad arguments.
+ * partition_tokens 0 = the same automatic choice pkv_paged_decode makes.
+ * Layout: fp32 partials m [B][Hq][P], l [B][Hq][P], o [B][Hq][P][D]. */
 int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_context, int32_t partition_tokens);
 
 /* Paged decode: out[b][h] = softmax(q[b][h] . K_b^T * scale) . V_b over the
  * ctx_lens[b] tokens of sequence b, read in place through its block table
- * (no gather), with query head h using KV head h / (Hq/Hkv). Split-K: the
- * context is cut into partitions of partition_tokens (a multiple of 16);
- * each partition runs an online softmax ([p1] §四) and a second kernel
- * merges the partitions by log-sum-exp. Accumulation is fp32 and the output
- * is rounded to fp16 (nearest even). The result depends only on logical
- * token order, not on physical block ids. Slots past ctx_len in a tail
- * block are never used. Block ids outside [0, N) are treated as empty.
+ * (no gather), with query head h using KV head h / (Hq/Hkv) ([p2] §1.2,
+ * §3.2, §4.2). Split-K: the context is cut into partitions of
+ * partition_tokens (a multiple of 16); each partition runs an online
+ * softmax ([p1] §四) and writes a (max, sum, weighted-V) partial, and a
+ * second kernel merges the partials by log-sum-exp in partition order
+ * (skipped when every sequence fits one partition). Accumulation is fp32 and
+ * the output is rounded to fp16 (nearest even). The result depends only on
+ * logical token order, not on physical block ids, and is bitwise
+ * reproducible. Slots past ctx_len in a tail block are never used. Block ids
+ * outside [0, N) are treated as empty.
+ *
+ * Workspace: device memory of at least pkv_decode_workspace_bytes() bytes,
+ * 16-byte aligned, scratch owned by the caller (no initial contents needed;
+ * contents after the call unspecified). Calls sharing one workspace must be
+ * ordered on one stream.
+ *
+ * With k_new_dev/v_new_dev set, the call also performs the append step of
+ * [p2] §2.2 for every sequence (one token each) before attending: the
+ * decode step of the pages in one launch. pool_dev is then written.
+ *
  * INVALID_ARG: null pointers, ctx_len == 0 or > 16*max_blocks or >
- * max_context (host copy), workspace too small, partition_tokens not a
- * multiple of 16. UNSUPPORTED: head_dim/group size not built. */
+ * max_context (host copy), workspace too small or misaligned,
+ * partition_tokens not a multiple of 16, only one of k_new/v_new given.
+ * UNSUPPORTED: head_dim/group size not built, fused append on int8. */
 int pkv_paged_decode(const pkv_decode_args* args, void* stream);
+
+/* Upload host metadata for the next step (block tables, lengths: the
+ * per-step upload of [p2] §3.3's batch that changes every step) from pinned
+ * host memory to device memory, with a kernel on `stream` that reads the
+ * host buffer through its device mapping. The copy stays on the compute
+ * queue: no hand-off to a copy engine between kernels. src_host must be
+ * pinned host memory allocated for the device (hipHostMalloc, torch
+ * pin_memory); it is read when the kernel runs, so the caller keeps it
+ * unchanged until then. dst_dev must be device memory. Both 16-byte aligned.
+ * INVALID_ARG (no launch): bytes < 0, null or misaligned pointers, src not
+ * pinned host memory, dst not device memory. bytes == 0 is a no-op. */
+int pkv_upload(void* dst_dev, const void* src_host, int64_t bytes, void* stream);
 
 /* ---- measurement helper ------------------------------------------------------ */
 

@@ -50,7 +50,8 @@ class pkv_decode_args(ctypes.Structure):
                 ("block_tables_dev", _vp), ("max_blocks", _c_i32), ("ctx_lens_dev", _vp),
                 ("ctx_lens_host", _p_i32), ("max_context", _c_i32), ("out_dev", _vp),
                 ("scale", ctypes.c_float), ("workspace_dev", _vp), ("workspace_bytes", _c_i64),
-                ("partition_tokens", _c_i32), ("timing_events", ctypes.POINTER(_vp))]
+                ("partition_tokens", _c_i32), ("k_new_dev", _vp), ("v_new_dev", _vp),
+                ("timing_events", ctypes.POINTER(_vp))]
 
 
 class PkvError(RuntimeError):
@@ -81,6 +82,7 @@ _SIGS = {
     "pkv_append_kv": (ctypes.c_int, [ctypes.POINTER(pkv_config), _vp, _c_i32, _vp, _vp, _vp, _c_i32, _vp]),
     "pkv_decode_workspace_bytes": (_c_i64, [ctypes.POINTER(pkv_config), _c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_paged_decode": (ctypes.c_int, [ctypes.POINTER(pkv_decode_args), _vp]),
+    "pkv_upload": (ctypes.c_int, [_vp, _vp, _c_i64, _vp]),
     "pkv_probe_stream_read": (ctypes.c_int, [_vp, _c_i64, _vp, _vp]),
     "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_last_error": (ctypes.c_char_p, []),
@@ -256,6 +258,10 @@ def pkv_decode_workspace_bytes(cfg, num_seqs, num_q_heads, max_context, partitio
 
 def pkv_paged_decode(args, stream):
     _check(load().pkv_paged_decode(ctypes.byref(args), stream))
+
+
+def pkv_upload(dst_dev, src_host, nbytes, stream):
+    _check(load().pkv_upload(dst_dev, src_host, nbytes, stream))
 
 
 def pkv_probe_stream_read(buf_dev, nbytes, sink_dev, stream):

@@ -63,6 +63,15 @@ class PagedKVCache:
         except Exception:
             pass
 
+    def decode_workspace(self, nbytes):
+        """A device workspace of at least ``nbytes`` for pkv_paged_decode,
+        kept and reused by later calls (calls on one cache share one stream)."""
+        ws = getattr(self, "_workspace", None)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self._workspace = ws
+        return ws
+
     # ---- views of the device pool (for tests and bulk fills) ---------------
     def _region_bytes(self):
         e = 1 if self.dtype == "i8" else 2
@@ -173,6 +182,18 @@ class PagedKVCache:
             self.write(0, k, v, slots_dev)
         return slots_dev
 
+    def upload(self, dst, src_pinned):
+        """Copy a pinned host tensor into a device tensor of the same size
+        with the library's upload kernel on the current stream (no copy
+        engine): the per-step block tables and lengths."""
+        if not src_pinned.is_pinned() or dst.device.type != "cuda" or not dst.is_contiguous() \
+                or not src_pinned.is_contiguous():
+            raise ValueError("upload needs a contiguous pinned host source and a contiguous device target")
+        n = src_pinned.numel() * src_pinned.element_size()
+        if dst.numel() * dst.element_size() != n:
+            raise ValueError("source and target sizes differ")
+        C.pkv_upload(dst.data_ptr(), src_pinned.data_ptr(), n, _stream())
+
     def block_tables(self, seqs, max_blocks=None):
         """Host ``(tables int32[B, max_blocks], ctx_lens int32[B])`` for the
         decode, padded with -1."""
@@ -181,16 +202,21 @@ class PagedKVCache:
         return C.pkv_build_block_tables(self.handle, seqs, max_blocks)
 
     def paged_decode(self, q, block_tables, context_lens, layer=0, out=None, scale=None,
-                     context_lens_host=None, max_context=None, workspace=None, partition_tokens=0):
+                     context_lens_host=None, max_context=None, workspace=None, partition_tokens=0,
+                     k_new=None, v_new=None):
         """``out[b, h] = softmax(q[b, h] K_b^T * scale) V_b`` over the
         ``context_lens[b]`` tokens of each sequence, read in place through
-        ``block_tables`` (device int32 ``[B, max_blocks]``)."""
+        ``block_tables`` (device int32 ``[B, max_blocks]``). With ``k_new,
+        v_new`` (fp16 ``[B, Hkv, D]``) the kernel first stores them as the
+        last token of each sequence (the slot already reserved), so append
+        and attention run in one launch."""
         return paged_decode(self, q, block_tables, context_lens, layer, out, scale,
-                            context_lens_host, max_context, workspace, partition_tokens)
+                            context_lens_host, max_context, workspace, partition_tokens, k_new, v_new)
 
 
 def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=None,
-                 context_lens_host=None, max_context=None, workspace=None, partition_tokens=0):
+                 context_lens_host=None, max_context=None, workspace=None, partition_tokens=0,
+                 k_new=None, v_new=None):
     if q.dtype != torch.float16 or q.dim() != 3:
         raise TypeError("q must be float16 [B, Hq, D]")
     q = q.contiguous()
@@ -211,7 +237,7 @@ def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=
         out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
     ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, Hq, max_context, partition_tokens)
     if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+        workspace = cache.decode_workspace(ws_bytes)
     args = C.pkv_decode_args()
     args.cfg = C.ctypes.pointer(cache.cfg)
     args.pool_dev = cache.pool.data_ptr()
@@ -229,5 +255,15 @@ def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=
     args.workspace_dev = workspace.data_ptr()
     args.workspace_bytes = workspace.numel()
     args.partition_tokens = partition_tokens
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        k_new, v_new = k_new.contiguous(), v_new.contiguous()
+        shape = (B, cache.num_kv_heads, D)
+        if k_new.dtype != torch.float16 or tuple(k_new.shape) != shape or tuple(v_new.shape) != shape \
+                or v_new.dtype != torch.float16:
+            raise ValueError(f"k_new, v_new must be float16 {list(shape)}")
+        args.k_new_dev = k_new.data_ptr()
+        args.v_new_dev = v_new.data_ptr()
     C.pkv_paged_decode(args, _stream())
     return out

@@ -67,32 +67,7 @@ __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over the 4 lanes of a quad; every lane ends with the same bits.
-__device__ __forceinline__ float quad_sum(float x) {
-  x += dpp<0xB1>(x);  // quad_perm(1,0,3,2)
-  x += dpp<0x4E>(x);  // quad_perm(2,3,0,1)
-  return x;
-}
-
 __device__ __forceinline__ float xor_shfl(float x, int mask) { return __shfl_xor(x, mask, 64); }
-
-// Max over the 16 quads (all 64 lanes) of a quad-uniform value.
-__device__ __forceinline__ float quads_max(float x) {
-  x = fmaxf(x, xor_shfl(x, 4));
-  x = fmaxf(x, xor_shfl(x, 8));
-  x = fmaxf(x, xor_shfl(x, 16));
-  x = fmaxf(x, xor_shfl(x, 32));
-  return x;
-}
-
-// Sum over the 16 quads of a quad-uniform value (butterfly: same bits in all lanes).
-__device__ __forceinline__ float quads_sum(float x) {
-  x += xor_shfl(x, 4);
-  x += xor_shfl(x, 8);
-  x += xor_shfl(x, 16);
-  x += xor_shfl(x, 32);
-  return x;
-}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -184,12 +159,14 @@ struct DecodeParams {
   const void* V;
   const _Float16* scales;  // int8: this layer's [N][Hkv][2]; else null
   const _Float16* q;       // [B][Hq][D]
+  const uint4* k_new;      // optional fused append: fp16 [B][Hkv][D] (null = none)
+  const uint4* v_new;
   const int32_t* tables;
   const int32_t* ctx_lens;
   float* part_m;  // [B][Hq][max_parts]
   float* part_l;
   float* part_o;  // [B][Hq][max_parts][D]
-  _Float16* out;    // [B][Hq][D]
+  _Float16* out;  // [B][Hq][D]
   int max_blocks;
   int num_blocks;
   int Hkv;
@@ -203,18 +180,60 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int max_contex
   return min(ctx, min(max_blocks * BT, max_context));
 }
 
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
 template <int D, int G, bool I8>
 struct Shape {
-  static constexpr int E = I8 ? 1 : 2;   // bytes per element
-  static constexpr int CE = 16 / E;      // elements per 16-byte chunk
-  static constexpr int NC = D / CE / 4;  // K chunks per lane (lane quarter kq)
-  static constexpr int QW = CE / 8;      // uint4 of fp16 q per K chunk
-  static constexpr int LPR = D / CE;     // V lanes per row
-  static constexpr int RPI = 64 / LPR;   // V rows per load instruction
-  static constexpr int NI = BT / RPI;    // V load instructions per tile
+  static constexpr int E = I8 ? 1 : 2;     // bytes per element
+  static constexpr int NCH = D / 32;       // MFMA k-chunks of 32 dims
+  static constexpr int KL = D * E / 64;    // K 16-byte loads per lane per tile
+  static constexpr int CE = 16 / E;        // V elements per 16-byte chunk
+  static constexpr int LPR = D / CE;       // V lanes per row
+  static constexpr int RPI = 64 / LPR;     // V rows per load instruction
+  static constexpr int NI = BT / RPI;      // V load instructions per tile
   static constexpr int TILE = BT * D * E;  // bytes per (block, head) tile
+  // First of the 8 head dims that k-slot group j (lanes 16j..16j+15) holds in
+  // MFMA chunk c. K load i of lane (n, j) reads bytes [16(4i + j), +16) of
+  // row n: 8 fp16 dims (chunk i) or 16 int8 dims (chunks 2i and 2i + 1); q
+  // is loaded with the same assignment, so the contraction pairs equal dims.
+  static __device__ __forceinline__ int dim_base(int c, int j) {
+    return I8 ? 64 * (c >> 1) + 16 * j + 8 * (c & 1) : 32 * c + 8 * j;
+  }
 };
 
+// Max / sum over the 16 lanes of a DPP row. Every lane gets a result; lane 0
+// of the row always combines in the same order.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm(1,0,3,2)
+  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm(2,3,0,1)
+  x = fmaxf(x, dpp<0x124>(x));  // row_ror:4
+  x = fmaxf(x, dpp<0x128>(x));  // row_ror:8
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x124>(x);
+  x += dpp<0x128>(x);
+  return x;
+}
+__device__ __forceinline__ float read_lane(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// One work-group (4 wave64s) per (partition p, KV head g, sequence b).
+//
+// Scores on the matrix cores: per tile, S[r][n] = sum_k Q[r][k] K[n][k] with
+// v_mfma_f32_16x16x32_f16 over D/32 chunks. A-row r holds query head r % G of
+// the group (rows repeat when G < 16), B-column n is token n of the tile.
+// Lane (n = lane % 16, j = lane / 16) feeds token n's K dims of k-slot group
+// j and receives rows 4j..4j+3 of column n: the scores of heads
+// (4j + e) % G, e = 0..3, for its token, already fully reduced.
+//
+// After its last tile the work-group writes one (m, l, o[D]) partial per
+// query head for the merge kernel, or the final fp16 row when the sequence
+// has a single partition.
 template <int D, int G, bool I8>
 __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   using S = Shape<D, G, I8>;
@@ -234,31 +253,29 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   if (p >= nparts) return;
   const int jb = p * prm.part_blocks, je = min(nblk, jb + prm.part_blocks);
 
-  // K lane mapping: row kt, quarter kq; V lane mapping: row group vt, dims vd.
-  const int kt = lane >> 2, kq = lane & 3;
-  const int vt = lane / S::LPR, vd = lane % S::LPR;
+  const int kn = lane & 15, kj = lane >> 4;  // score mapping: token, k-slot group
+  const int vt = lane / S::LPR, vd = lane % S::LPR;  // V mapping: row group, dims
+  const bool odd = (kj & 1) != 0;  // G == 8: this lane's score rows are heads 4..7
 
-  // q for the G heads: the dims of this lane's K chunks {kq + 4i}.
-  uint4 qr[G][S::NC][S::QW];
+  // q as the MFMA A operand: head (kn % G), the dims of group kj per chunk
+  half8_t qa[S::NCH];
   {
-    const _Float16* qb = prm.q + (int64_t(b) * Hq + g * G) * D;
+    const _Float16* qh = prm.q + (int64_t(b) * Hq + g * G + kn % G) * D;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < S::NC; ++i)
-#pragma unroll
-        for (int w = 0; w < S::QW; ++w)
-          qr[h][i][w] = *reinterpret_cast<const uint4*>(qb + h * D + (kq + 4 * i) * S::CE + 8 * w);
+    for (int c = 0; c < S::NCH; ++c) qa[c] = *reinterpret_cast<const half8_t*>(qh + S::dim_base(c, kj));
   }
 
-  float m[G], l[G], o[G][S::CE];
+  // mh: running max per head (wave-uniform); lrow: this lane's share of the
+  // softmax denominator per score row; o: V accumulators, D/16 dims x G heads
+  float mh[G], o[G][S::CE], lrow[4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
+    mh[h] = -INFINITY;
 #pragma unroll
     for (int e = 0; e < S::CE; ++e) o[h][e] = 0.0f;
   }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lrow[e] = 0.0f;
 
   __shared__ float p_lds[WAVES][BT][G];
   __shared__ float merge_o[WAVES][G][D];
@@ -270,8 +287,30 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   const int64_t head_off = int64_t(g) * S::TILE;
   const int64_t blk_stride = int64_t(Hkv) * S::TILE;
 
+  // Fused append (fp16 pools): the new token is the last of the context, at
+  // logical position ctx - 1, in this sequence's last partition. That
+  // work-group stores its k and v rows for head g into the slot the table
+  // gives, then reads them back with the rest of the tile; no other
+  // work-group reads that slot in this launch (a slot written at a non-zero
+  // offset of a shared block was moved to a private block by copy-on-write).
+  if constexpr (!I8) {
+    if (prm.k_new && p == nparts - 1) {
+      constexpr int PIECES = D / 8;  // 16-byte pieces per fp16 row
+      const int t = ctx - 1;
+      const int blk = trow[t / BT];
+      if (tid < 2 * PIECES && unsigned(blk) < unsigned(prm.num_blocks)) {
+        const int c = tid % PIECES;
+        const uint4* src = (tid < PIECES ? prm.k_new : prm.v_new) + (int64_t(b) * Hkv + g) * PIECES + c;
+        char* dst = const_cast<char*>(tid < PIECES ? Kc : Vc) + blk * blk_stride + head_off + (t % BT) * (D * 2);
+        reinterpret_cast<uint4*>(dst)[c] = *src;
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      __syncthreads();
+    }
+  }
+
   struct Tile {
-    uint4 k[S::NC];
+    uint4 k[S::KL];
     uint4 v[S::NI];
     int blk;
   };
@@ -292,9 +331,15 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
     const char* kb = Kc + safe * blk_stride + head_off;
     const char* vb = Vc + safe * blk_stride + head_off;
 #pragma unroll
-    for (int i = 0; i < S::NC; ++i) t.k[i] = load_nt(kb + kt * (D * S::E) + (kq + 4 * i) * 16);
+    for (int i = 0; i < S::KL; ++i) t.k[i] = load_nt(kb + kn * (D * S::E) + (4 * i + kj) * 16);
 #pragma unroll
     for (int i = 0; i < S::NI; ++i) t.v[i] = load_nt(vb + (vt + S::RPI * i) * (D * S::E) + vd * 16);
+  };
+
+  // running max of the head of score row e of this lane
+  auto mrow = [&](int e) -> float {
+    if constexpr (G == 8) return odd ? mh[4 + e] : mh[e];
+    else return mh[e % G];
   };
 
   auto compute = [&](int j, Tile& t) {
@@ -307,60 +352,72 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
         vscale = float(sc[1]);
       }
     }
-    // scores of row kt for the G heads
-    float s[G];
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float acc = 0.0f;
-#pragma unroll
-      for (int i = 0; i < S::NC; ++i) {
-        if constexpr (I8) {
-          const uint32_t w4[4] = {t.k[i].x, t.k[i].y, t.k[i].z, t.k[i].w};
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            uint32_t lo, hi;
-            i8x4_to_f16x4(w4[w], lo, hi);
-            const uint4& qq = qr[h][i][w >> 1];
-            const uint32_t qa = (w & 1) ? qq.z : qq.x, qb2 = (w & 1) ? qq.w : qq.y;
-            acc = dot2(qa, lo, acc);
-            acc = dot2(qb2, hi, acc);
-          }
-        } else {
-          acc = dot2(qr[h][i][0].x, t.k[i].x, acc);
-          acc = dot2(qr[h][i][0].y, t.k[i].y, acc);
-          acc = dot2(qr[h][i][0].z, t.k[i].z, acc);
-          acc = dot2(qr[h][i][0].w, t.k[i].w, acc);
-        }
+    for (int c = 0; c < S::NCH; ++c) {
+      half8_t kb;
+      if constexpr (I8) {
+        const uint4& w = t.k[c >> 1];
+        uint32_t a0, a1, a2, a3;
+        i8x4_to_f16x4((c & 1) ? w.z : w.x, a0, a1);
+        i8x4_to_f16x4((c & 1) ? w.w : w.y, a2, a3);
+        kb = __builtin_bit_cast(half8_t, make_uint4(a0, a1, a2, a3));
+      } else {
+        kb = __builtin_bit_cast(half8_t, t.k[c]);
       }
-      s[h] = quad_sum(acc) * kscale;
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kb, acc, 0, 0, 0);
     }
-    const bool tvalid = blk_ok && (j * BT + kt) < ctx;
+    // A score of a row past the context (stale or poisoned) only reaches its
+    // own column, and is replaced by -inf here.
+    const bool tvalid = blk_ok && (j * BT + kn) < ctx;
+    float s[4];
     bool need = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s[h] = tvalid ? s[h] : -INFINITY;
-      need |= s[h] > m[h] + LAZY_MAX;
+    for (int e = 0; e < 4; ++e) {
+      s[e] = tvalid ? acc[e] * kscale : -INFINITY;
+      need |= s[e] > mrow(e) + LAZY_MAX;
     }
     if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first tile
+      float mx[G];
+#pragma unroll
+      for (int e = 0; e < 4 && e < G; ++e) {
+        const float r = row16_max(s[e]);
+        mx[e] = read_lane(r, 0);
+        if constexpr (G == 8) mx[4 + e] = read_lane(r, 16);
+      }
+      float alpha[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m[h], quads_max(s[h]));
-        const float alpha = (m[h] == -INFINITY) ? 0.0f : exp2_fast(m[h] - mn);
-        l[h] *= alpha;
+        const float mn = fmaxf(mh[h], mx[h]);
+        alpha[h] = (mh[h] == -INFINITY) ? 0.0f : exp2_fast(mh[h] - mn);
+        mh[h] = mn;
 #pragma unroll
-        for (int e = 0; e < S::CE; ++e) o[h][e] *= alpha;
-        m[h] = mn;
+        for (int e = 0; e < S::CE; ++e) o[h][e] *= alpha[h];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (G == 8) lrow[e] *= odd ? alpha[4 + e] : alpha[e];
+        else lrow[e] *= alpha[e % G];
       }
     }
-    float pr[G];
+    float pr[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      pr[h] = tvalid ? exp2_fast(s[h] - m[h]) : 0.0f;
-      l[h] += pr[h];
+    for (int e = 0; e < 4; ++e) {
+      pr[e] = tvalid ? exp2_fast(s[e] - mrow(e)) : 0.0f;
+      lrow[e] += pr[e];
     }
     // hand the probabilities to the V lane mapping through LDS
+    if constexpr (G == 8) {
+      if (lane < 32) {
 #pragma unroll
-    for (int h = kq; h < G; h += 4) p_lds[wave][kt][h] = pr[h];
+        for (int e = 0; e < 4; ++e) p_lds[wave][kn][4 * kj + e] = pr[e];
+      }
+    } else {
+      if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < G && e < 4; ++e) p_lds[wave][kn][e] = pr[e];
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -400,6 +457,8 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
         }
       }
     }
+    // the next tile rewrites p_lds: its writes stay behind these reads
+    __builtin_amdgcn_wave_barrier();
   };
 
   // Double-buffered stream over this wave's tiles: in the steady state the
@@ -424,15 +483,20 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
     }
   }
 
-  // wave totals: l over the 16 quads, o over the row groups
+  // wave totals: l over the 16 tokens of each score row, o over the V row groups
+  float lh[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l[h] = quads_sum(l[h]);
+  for (int e = 0; e < 4 && e < G; ++e) {
+    const float r = row16_sum(lrow[e]);
+    lh[e] = read_lane(r, 0);
+    if constexpr (G == 8) lh[4 + e] = read_lane(r, 16);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < S::CE; ++e)
 #pragma unroll
       for (int mask = S::LPR; mask < 64; mask <<= 1) o[h][e] += xor_shfl(o[h][e], mask);
-  }
   if (vt == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -442,13 +506,13 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      merge_ml[wave][h][0] = m[h];
-      merge_ml[wave][h][1] = l[h];
+      merge_ml[wave][h][0] = mh[h];
+      merge_ml[wave][h][1] = lh[h];
     }
   }
   __syncthreads();
 
-  // merge the 4 waves (fixed order) and write the partial or the final row
+  // merge the 4 waves (fixed order); write the final row or this partition's partial
   for (int idx = tid; idx < G * D; idx += 256) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
@@ -477,9 +541,12 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
 }
 
 // Merge the partitions of one (sequence, query head) by log-sum-exp:
-// M = max m_p, out = sum o_p 2^(m_p - M) / sum l_p 2^(m_p - M). One thread per
-// output dim. Sequences with a single partition were finished by the split
-// kernel.
+// M = max_p m_p, out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), in
+// partition order. One thread per output dim. The partials are read 16
+// partitions at a time, all loads of a group in flight together; across
+// groups the running max is raised as in the split kernel (a sequence of up
+// to 16 partitions is one group, exactly the two-pass formula above).
+// Sequences with a single partition were finished by the split kernel.
 __global__ __launch_bounds__(128) void lse_reduce_kernel(const float* __restrict__ part_m,
                                                          const float* __restrict__ part_l,
                                                          const float* __restrict__ part_o,
@@ -487,6 +554,7 @@ __global__ __launch_bounds__(128) void lse_reduce_kernel(const float* __restrict
                                                          _Float16* __restrict__ out, int max_blocks,
                                                          int max_context, int part_blocks, int max_parts,
                                                          int D) {
+  constexpr int CH = 16;
   const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
   const int d = threadIdx.x;
   const int ctx = clamp_ctx(ctx_lens[b], max_blocks, max_context);
@@ -495,16 +563,47 @@ __global__ __launch_bounds__(128) void lse_reduce_kernel(const float* __restrict
   const int nparts = (nblk + part_blocks - 1) / part_blocks;
   if (nparts <= 1) return;
   const int64_t base = (int64_t(b) * Hq + h) * max_parts;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, part_m[base + p]);
-  float L = 0.0f, O = 0.0f;
-  for (int p = 0; p < nparts; ++p) {
-    const float mp = part_m[base + p];
-    const float wt = (mp == -INFINITY) ? 0.0f : exp2_fast(mp - M);
-    L += part_l[base + p] * wt;
-    O += part_o[(base + p) * D + d] * wt;
+  float M = -INFINITY, L = 0.0f, O = 0.0f;
+  for (int p0 = 0; p0 < nparts; p0 += CH) {
+    float mv[CH], lv[CH], ov[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const bool ok = p0 + u < nparts;
+      const int64_t pi = base + (ok ? p0 + u : 0);
+      mv[u] = ok ? part_m[pi] : -INFINITY;
+      lv[u] = ok ? part_l[pi] : 0.0f;
+      ov[u] = ok ? part_o[pi * D + d] : 0.0f;
+    }
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) cm = fmaxf(cm, mv[u]);
+    if (cm != M) {  // raise the running max (always on the first group)
+      const float a = (M == -INFINITY) ? 0.0f : exp2_fast(M - cm);
+      L *= a;
+      O *= a;
+      M = cm;
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const float wt = (mv[u] == -INFINITY) ? 0.0f : exp2_fast(mv[u] - M);
+      L += lv[u] * wt;
+      O += ov[u] * wt;
+    }
   }
   out[(int64_t(b) * Hq + h) * D + d] = (_Float16)(L > 0.0f ? O / L : 0.0f);
+}
+
+// Host -> device staging of small host metadata (block tables, lengths): one
+// thread per 16 bytes reads the pinned host buffer through its device mapping
+// and writes device memory; the last thread copies a ragged tail byte-wise.
+__global__ __launch_bounds__(256) void upload_kernel(char* __restrict__ dst, const char* __restrict__ src,
+                                                     int64_t bytes) {
+  const int64_t n16 = bytes / 16;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    for (int64_t i = n16 * 16; i < bytes; ++i) dst[i] = src[i];
 }
 
 // Coalesced streaming read of a buffer, for an achievable-bandwidth
@@ -578,6 +677,13 @@ decode_fn pick_kernel(int D, int G, bool i8) {
   return nullptr;
 }
 
+// Split-K workspace: m [B][Hq][P], l [B][Hq][P], o [B][Hq][P][D] (fp32); none
+// when every sequence fits one partition.
+int64_t workspace_bytes_for(const pkv_config& c, int B, int Hq, int max_parts) {
+  if (max_parts <= 1) return 0;
+  return int64_t(B) * Hq * max_parts * (c.head_dim + 2) * int64_t(sizeof(float));
+}
+
 int check_partition_tokens(int partition_tokens) {
   if (partition_tokens < 0 || partition_tokens % BT || partition_tokens > MAX_PARTITION_TOKENS)
     return pkv::fail(PKV_ERR_INVALID_ARG, "partition_tokens must be a multiple of 16 in [0, %d] (got %d)",
@@ -640,9 +746,7 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
   st = check_partition_tokens(partition_tokens);
   if (st != PKV_OK) return st;
   const int pb = choose_part_blocks(*cfg, num_seqs, max_context, partition_tokens);
-  const int mp = max_parts_for(max_context, pb);
-  if (mp <= 1) return 0;
-  return int64_t(num_seqs) * num_q_heads * mp * (cfg->head_dim + 2) * int64_t(sizeof(float));
+  return workspace_bytes_for(*cfg, num_seqs, num_q_heads, max_parts_for(max_context, pb));
 }
 
 int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
@@ -664,6 +768,12 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
     return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks and max_context must be >= 1");
   st = check_partition_tokens(a->partition_tokens);
   if (st != PKV_OK) return st;
+  if ((a->k_new_dev == nullptr) != (a->v_new_dev == nullptr))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "k_new and v_new must both be given or both be NULL");
+  if (a->k_new_dev && c.dtype != PKV_F16)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "the fused append writes fp16 pools only");
+  if (a->k_new_dev && (!aligned16(a->k_new_dev) || !aligned16(a->v_new_dev)))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
   const int G = a->num_q_heads / c.num_kv_heads;
   decode_fn fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8);
   if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", G);
@@ -678,9 +788,11 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   }
   const int pb = choose_part_blocks(c, a->num_seqs, a->max_context, a->partition_tokens);
   const int mp = max_parts_for(a->max_context, pb);
-  const int64_t need = mp <= 1 ? 0 : int64_t(a->num_seqs) * a->num_q_heads * mp * (c.head_dim + 2) * 4;
+  const int64_t need = workspace_bytes_for(c, a->num_seqs, a->num_q_heads, mp);
   if (need > 0 && (!a->workspace_dev || a->workspace_bytes < need))
     return pkv::fail(PKV_ERR_INVALID_ARG, "workspace too small: need %lld bytes", (long long)need);
+  if (need > 0 && !aligned16(a->workspace_dev))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
 
   const int64_t E = pkv::elem_bytes(c.dtype);
   const int64_t layer_bytes = pkv::layer_elems(c) * E;
@@ -693,6 +805,8 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
                                                      int64_t(a->layer) * c.num_blocks * c.num_kv_heads * 2 * 2)
                    : nullptr;
   prm.q = static_cast<const _Float16*>(a->q_dev);
+  prm.k_new = static_cast<const uint4*>(a->k_new_dev);
+  prm.v_new = static_cast<const uint4*>(a->v_new_dev);
   prm.tables = a->block_tables_dev;
   prm.ctx_lens = a->ctx_lens_dev;
   const int64_t rows = int64_t(a->num_seqs) * a->num_q_heads * mp;
@@ -729,6 +843,33 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
     hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, prm.part_m, prm.part_l, prm.part_o,
                        a->ctx_lens_dev, prm.out, a->max_blocks, a->max_context, pb, mp, c.head_dim);
   return hip_status(hipGetLastError(), "lse_reduce launch");
+}
+
+int pkv_upload(void* dst_dev, const void* src_host, int64_t bytes, void* stream) {
+  if (bytes < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "bytes must be >= 0");
+  if (bytes == 0) return PKV_OK;
+  if (!dst_dev || !src_host) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(dst_dev) || !aligned16(src_host))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "dst and src must be 16-byte aligned");
+  // The kernel reads src through the device mapping of pinned host memory:
+  // anything else (pageable memory, device memory) is refused here, before
+  // any launch.
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, src_host) != hipSuccess || attr.type != hipMemoryTypeHost ||
+      attr.devicePointer == nullptr) {
+    (void)hipGetLastError();  // clear the sticky error of a failed query
+    return pkv::fail(PKV_ERR_INVALID_ARG, "src_host is not pinned host memory mapped for the device");
+  }
+  hipPointerAttribute_t dattr;
+  if (hipPointerGetAttributes(&dattr, dst_dev) != hipSuccess || dattr.type != hipMemoryTypeDevice) {
+    (void)hipGetLastError();
+    return pkv::fail(PKV_ERR_INVALID_ARG, "dst_dev is not device memory");
+  }
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n16 + 255) / 256, 1024));
+  hipLaunchKernelGGL(upload_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<char*>(dst_dev), static_cast<const char*>(attr.devicePointer), bytes);
+  return hip_status(hipGetLastError(), "upload launch");
 }
 
 int pkv_probe_stream_read(const void* buf_dev, int64_t bytes, void* sink_dev, void* stream) {

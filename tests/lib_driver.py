@@ -13,12 +13,19 @@ from workloads import replay_churn
 
 
 class LibRun:
-    def __init__(self, w, device=None, layers=1, quantised=None, poison=False):
+    def __init__(self, w, device=None, layers=1, quantised=None, poison=False, fused_append=False):
         """``quantised``: for an int8 workload, the oracle's quantised store
         (``RefCache`` with K, V, scales), uploaded into the pool before each
-        decode; the pool has no int8 write path of its own yet."""
+        decode; the pool has no int8 write path of its own yet.
+        ``fused_append``: an append step of one token per sequence followed by
+        a decode of exactly those sequences writes the tokens inside the
+        decode launch (k_new/v_new) instead of a separate append call."""
         self.w = w
         self.device = device
+        self.fused_append = fused_append
+        self.pending = None  # (names, slots, k, v) of an append not yet written
+        if fused_append and layers != 1:
+            raise ValueError("fused append runs on one-layer pools")
         self.cfg = pkv.make_config(layers, w.num_blocks, w.num_kv_heads, w.head_dim, w.dtype)
         self.quantised = quantised
         if device is None:
@@ -67,6 +74,8 @@ class LibRun:
     def run(self, decode=True, **decode_kw):
         for idx, step in enumerate(self.w.steps):
             kind = step[0]
+            if self.pending is not None and kind not in ("append", "decode"):
+                self._flush_pending()  # a pending append is written before any other step
             if kind == "create":
                 self.seq[step[1]] = pkv.pkv_seq_create(self.handle)
             elif kind == "prefill":
@@ -75,12 +84,19 @@ class LibRun:
                 self._write(slots, cow, k, v)
             elif kind == "append":
                 _, names, k, v = step
+                if self.pending is not None:
+                    self._flush_pending()
                 all_slots, all_cow = [], []
                 for name in names:
                     slots, cow = self._reserve(idx, name, 1)
                     all_slots.append(slots)
                     all_cow.append(cow)
-                self._write(np.concatenate(all_slots), np.concatenate(all_cow), k, v)
+                slots, cow = np.concatenate(all_slots), np.concatenate(all_cow)
+                if self.fused_append and self.cache is not None and self.w.dtype == "f16" and decode:
+                    self.cache.copy_blocks(cow)
+                    self.pending = (list(names), slots, k, v)
+                else:
+                    self._write(slots, cow, k, v)
             elif kind == "fork":
                 self.seq[step[2]] = pkv.pkv_seq_fork(self.handle, self.seq[step[1]])
             elif kind == "free":
@@ -91,6 +107,8 @@ class LibRun:
                 self._decode(step[1], step[2], decode, decode_kw)
             else:
                 raise ValueError(kind)
+        if self.pending is not None:
+            self._flush_pending()
         return self
 
     def _churn(self, churn):
@@ -122,11 +140,24 @@ class LibRun:
             self.cache.region(1, layer).copy_(torch.from_numpy(q8.V[0]))
             self.cache.scales()[layer].copy_(torch.from_numpy(q8.scales[0]))
 
+    def _flush_pending(self):
+        names, slots, k, v = self.pending
+        self.pending = None
+        self._write(slots, np.empty((0, 2), np.int32), k, v)
+
     def _decode(self, names, q, compute, kw):
+        fused = None
+        if self.pending is not None:
+            if self.pending[0] == list(names):
+                fused = self.pending
+                self.pending = None
+            else:
+                self._flush_pending()
         sids = [self.seq[n] for n in names]
         max_blocks = max(len(pkv.pkv_seq_block_table(self.handle, s)) for s in sids)
         tables, lens = pkv.pkv_build_block_tables(self.handle, sids, max_blocks)
-        rec = {"names": list(names), "tables": tables.copy(), "lens": lens.copy(), "q": q, "out": None}
+        rec = {"names": list(names), "tables": tables.copy(), "lens": lens.copy(), "q": q, "out": None,
+               "fused": fused is not None}
         if compute and self.cache is not None:
             import torch
             if self.w.dtype == "i8":
@@ -135,9 +166,13 @@ class LibRun:
             qd = torch.from_numpy(np.ascontiguousarray(q)).to(dev)
             td = torch.from_numpy(tables).to(dev)
             ld = torch.from_numpy(lens).to(dev)
+            extra = {}
+            if fused is not None:
+                extra["k_new"] = torch.from_numpy(np.ascontiguousarray(fused[2])).to(dev)
+                extra["v_new"] = torch.from_numpy(np.ascontiguousarray(fused[3])).to(dev)
             out = self.cache.paged_decode(qd, td, ld, layer=kw.get("layer", 0), context_lens_host=lens,
                                           scale=self.w.scale,
-                                          partition_tokens=kw.get("partition_tokens", 0))
+                                          partition_tokens=kw.get("partition_tokens", 0), **extra)
             torch.cuda.synchronize()
             rec["out"] = out.cpu().numpy()
         self.decodes.append(rec)

@@ -150,6 +150,86 @@ def test_partition_size_within_tolerance(ptok):
     lib.close()
 
 
+def test_workspace_reused_across_shapes_and_partitions():
+    """One workspace serves decodes of different batches, lengths and
+    partition sizes in a row (stale partials of the previous call in it):
+    each result matches the oracle."""
+    w = workloads.tiny_random(903, B=7, Hq=32, Hkv=8, D=128, max_len=2500)
+    lib, o = run_pair(w)
+    assert max_err(lib, o) <= F16_TOL
+    rec, ref = lib.decodes[0], o.decodes[0]["out"]
+    td = torch.from_numpy(rec["tables"]).to(DEV)
+    ld = torch.from_numpy(rec["lens"]).to(DEV)
+    qd = torch.from_numpy(rec["q"]).to(DEV)
+    for ptok, rows in [(16, 7), (512, 7), (64, 3), (4096, 7), (128, 1), (0, 5)]:
+        announce(f"workspace reuse ptok={ptok} rows={rows}")
+        out = lib.cache.paged_decode(qd[:rows], td[:rows], ld[:rows], context_lens_host=rec["lens"][:rows],
+                                     partition_tokens=ptok)
+        torch.cuda.synchronize()
+        err = float(np.abs(out.cpu().numpy().astype(np.float64) - ref[:rows]).max())
+        assert err <= F16_TOL, (ptok, rows, err)
+    lib.close()
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "tiny"])
+def test_fused_append_matches_oracle_and_two_call_path(name):
+    """Append inside the decode launch (k_new/v_new): the stored bytes match
+    the oracle bit for bit, the output matches the oracle within tolerance
+    and the two-call path (append kernel, then decode) bit for bit. c4
+    includes a copy-on-write fork whose child appends into a shared block."""
+    w = workloads.tiny_random(905, B=5, Hq=8, Hkv=2, D=128, max_len=600) if name == "tiny" \
+        else workloads.CONFIGS[name]()
+    announce(f"fused append {w.name}")
+    o = OracleRun(w).run()
+    fused = LibRun(w, device=DEV, poison=True, fused_append=True).run()
+    assert any(r["fused"] for r in fused.decodes)
+    check_host_records(fused, o)
+    check_stored_bytes(fused, o)
+    assert max_err(fused, o) <= F16_TOL
+    plain = LibRun(w, device=DEV, poison=True).run()
+    for a, b in zip(fused.decodes, plain.decodes):
+        assert np.array_equal(a["out"].view(np.uint16), b["out"].view(np.uint16))
+    fused.close()
+    plain.close()
+
+
+def test_graph_replay_matches_eager():
+    """A decode with the append fused in, captured into a HIP graph and
+    replayed several times with eager work and synchronisations between the
+    replays, gives the eager result bit for bit on every replay."""
+    w = workloads.tiny_random(907, B=4, Hq=32, Hkv=8, D=128, max_len=1200)
+    announce("graph capture + replay of fused append + decode")
+    lib = LibRun(w, device=DEV, fused_append=True).run()
+    rec = lib.decodes[0]
+    append = next(st for st in w.steps if st[0] == "append")
+    kd = torch.from_numpy(np.ascontiguousarray(append[2])).to(DEV)
+    vd = torch.from_numpy(np.ascontiguousarray(append[3])).to(DEV)
+    td = torch.from_numpy(rec["tables"]).to(DEV)
+    ld = torch.from_numpy(rec["lens"]).to(DEV)
+    qd = torch.from_numpy(rec["q"]).to(DEV)
+    q2 = torch.flip(qd, dims=[1]).contiguous()
+    cache = lib.cache
+    ws_bytes = pkv.pkv_decode_workspace_bytes(cache.cfg, 4, 32, int(rec["lens"].max()))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=DEV)
+    eager = cache.paged_decode(qd, td, ld, context_lens_host=rec["lens"], workspace=ws, k_new=kd, v_new=vd)
+    torch.cuda.synchronize()
+    assert np.array_equal(eager.cpu().numpy().view(np.uint16), rec["out"].view(np.uint16))
+    out = torch.empty_like(eager)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cache.paged_decode(qd, td, ld, context_lens_host=rec["lens"], out=out, workspace=ws, k_new=kd, v_new=vd)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.zero_()
+        other = cache.paged_decode(q2, td, ld, context_lens_host=rec["lens"], workspace=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), eager.cpu().numpy().view(np.uint16)), r
+        assert not torch.equal(other, out)
+    lib.close()
+
+
 # ---------------------------------------------------------------------------
 # invariants on the GPU
 
@@ -330,3 +410,28 @@ def test_headline_full_size_sampled():
     announce(f"headline sampled max abs err {max(errs):.3g}")
     assert max(errs) <= F16_TOL
     lib.close()
+
+
+def test_upload_kernel_copies_pinned_host_bytes():
+    """pkv_upload copies pinned host bytes to device memory bit for bit
+    (sizes with and without a ragged tail, interior offsets of a pinned
+    buffer) and refuses pageable or device sources before any launch."""
+    announce("upload kernel")
+    stream = torch.cuda.current_stream().cuda_stream
+    rng = np.random.default_rng(11)
+    src = torch.from_numpy(rng.integers(0, 256, 1 << 20, dtype=np.uint8)).pin_memory()
+    for n, off in [(4, 0), (16, 0), (100, 16), (33088, 64), ((1 << 20) - 48, 32), (1, 0)]:
+        dst = torch.full((n + 32,), 0xAB, dtype=torch.uint8, device=DEV)
+        pkv.pkv_upload(dst.data_ptr(), src.data_ptr() + off, n, stream)
+        torch.cuda.synchronize()
+        got = dst.cpu().numpy()
+        assert np.array_equal(got[:n], src.numpy()[off:off + n]), (n, off)
+        assert (got[n:] == 0xAB).all(), (n, off)
+    pageable = np.zeros(4096, np.uint8)
+    dst = torch.empty(4096, dtype=torch.uint8, device=DEV)
+    for bad_src in (pageable.ctypes.data, dst.data_ptr()):
+        with pytest.raises(pkv.PkvError):
+            pkv.pkv_upload(dst.data_ptr(), bad_src, 4096, stream)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_upload(src.data_ptr(), src.data_ptr(), 4096, stream)  # host target
+    torch.cuda.synchronize()

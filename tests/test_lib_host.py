@@ -258,7 +258,9 @@ def test_strerror():
 def test_workspace_bytes():
     cfg = pkv.make_config(1, 16, 8, 128)
     assert pkv.pkv_decode_workspace_bytes(cfg, 16, 32, 100, 128) == 0  # one partition: no partials
+    # m, l, o[128] partials of 16 x 32 heads x 17 partitions
     assert pkv.pkv_decode_workspace_bytes(cfg, 16, 32, 8193, 512) == 16 * 32 * 17 * 130 * 4
+    assert pkv.pkv_decode_workspace_bytes(cfg, 1, 32, 8193, 512) == 32 * 17 * 130 * 4
     for bad in (8, -16, 4097 * 16):
         with pytest.raises(pkv.PkvError):
             pkv.pkv_decode_workspace_bytes(cfg, 16, 32, 8193, bad)
@@ -318,5 +320,17 @@ def test_device_calls_validate_before_launch():
     assert status(lambda: pkv.pkv_paged_decode(args(layer=2), None)) == C.PKV_ERR_INVALID_ARG
     assert status(lambda: pkv.pkv_paged_decode(args(q_dev=None), None)) == C.PKV_ERR_INVALID_ARG
     assert status(lambda: pkv.pkv_paged_decode(args(partition_tokens=24), None)) == C.PKV_ERR_INVALID_ARG
+    # upload: sizes and pointers checked before any query or launch
+    assert status(lambda: pkv.pkv_upload(fake, fake, -1, None)) == C.PKV_ERR_INVALID_ARG
+    assert status(lambda: pkv.pkv_upload(0, fake, 16, None)) == C.PKV_ERR_INVALID_ARG
+    assert status(lambda: pkv.pkv_upload(fake, fake + 4, 16, None)) == C.PKV_ERR_INVALID_ARG
+    pkv.pkv_upload(fake, fake, 0, None)  # no-op
+    # fused append: both rows or neither; fp16 pools only
+    assert status(lambda: pkv.pkv_paged_decode(args(k_new_dev=fake), None)) == C.PKV_ERR_INVALID_ARG
+    assert status(lambda: pkv.pkv_paged_decode(args(k_new_dev=fake, v_new_dev=fake + 8), None)) == \
+        C.PKV_ERR_INVALID_ARG
+    i8dec = pkv.make_config(2, 16, 2, 64, "i8")
+    assert status(lambda: pkv.pkv_paged_decode(args(cfg=C.ctypes.pointer(i8dec), k_new_dev=fake, v_new_dev=fake),
+                                               None)) == C.PKV_ERR_UNSUPPORTED
     assert status(lambda: pkv.pkv_paged_decode(args(max_blocks=300, max_context=4800, workspace_bytes=10,
                                                     partition_tokens=64), None)) == C.PKV_ERR_INVALID_ARG
