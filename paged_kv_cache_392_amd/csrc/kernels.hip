@@ -239,9 +239,31 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   using S = Shape<D, G, I8>;
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int Hkv = prm.Hkv, Hq = Hkv * G;
-  const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int kn = lane & 15, kj = lane >> 4;  // score mapping: token, k-slot group
+  const int vt = lane / S::LPR, vd = lane % S::LPR;  // V mapping: row group, dims
+  const bool odd = (kj & 1) != 0;  // G == 8: this lane's score rows are heads 4..7
+
+  // The context length, this wave's block ids and q are loaded together, so
+  // a work-group waits one memory round trip, not two, before its first
+  // tile: the block ids of partition p need no length (the table row is
+  // max_blocks wide and padded; ids past the context are masked below).
+  // Wave w takes logical blocks jb + w, jb + w + 4, ...: its it-th id sits in
+  // lane it of a VGPR, and each tile reads it with readlane, so the id never
+  // waits on the vector memory queue.
+  const int32_t* trow = prm.tables + int64_t(b) * prm.max_blocks;
+  const int jb = p * prm.part_blocks;
+  const int first = jb + wave;
+  const int jl = first + WAVES * lane;
+  const int blk_raw = jl < prm.max_blocks ? trow[jl] : -1;
+  half8_t qa[S::NCH];  // q as the MFMA A operand: head kn % G, group kj's dims
+  {
+    const _Float16* qh = prm.q + (int64_t(b) * Hq + g * G + kn % G) * D;
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c) qa[c] = *reinterpret_cast<const half8_t*>(qh + S::dim_base(c, kj));
+  }
+  const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
 
   if (ctx <= 0) {  // rejected on the host when lengths are given; never NaN
     if (p == 0)
@@ -251,19 +273,9 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   const int nblk = (ctx + BT - 1) / BT;
   const int nparts = (nblk + prm.part_blocks - 1) / prm.part_blocks;
   if (p >= nparts) return;
-  const int jb = p * prm.part_blocks, je = min(nblk, jb + prm.part_blocks);
-
-  const int kn = lane & 15, kj = lane >> 4;  // score mapping: token, k-slot group
-  const int vt = lane / S::LPR, vd = lane % S::LPR;  // V mapping: row group, dims
-  const bool odd = (kj & 1) != 0;  // G == 8: this lane's score rows are heads 4..7
-
-  // q as the MFMA A operand: head (kn % G), the dims of group kj per chunk
-  half8_t qa[S::NCH];
-  {
-    const _Float16* qh = prm.q + (int64_t(b) * Hq + g * G + kn % G) * D;
-#pragma unroll
-    for (int c = 0; c < S::NCH; ++c) qa[c] = *reinterpret_cast<const half8_t*>(qh + S::dim_base(c, kj));
-  }
+  const int je = min(nblk, jb + prm.part_blocks);
+  const int n_my = first < je ? (je - first + WAVES - 1) / WAVES : 0;  // <= 64
+  const int blk_lane = lane < n_my ? blk_raw : -1;
 
   // mh: running max per head (wave-uniform); lrow: this lane's share of the
   // softmax denominator per score row; o: V accumulators, D/16 dims x G heads
@@ -281,7 +293,6 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   __shared__ float merge_o[WAVES][G][D];
   __shared__ float merge_ml[WAVES][G][2];
 
-  const int32_t* trow = prm.tables + int64_t(b) * prm.max_blocks;
   const char* Kc = static_cast<const char*>(prm.K);
   const char* Vc = static_cast<const char*>(prm.V);
   const int64_t head_off = int64_t(g) * S::TILE;
@@ -314,13 +325,6 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
     uint4 v[S::NI];
     int blk;
   };
-
-  // Block ids of this wave's tiles (it-th tile = logical block
-  // jb + wave + 4*it) sit one per lane in a VGPR, loaded once; each tile reads
-  // its id with readlane, so the id never waits on the vector memory queue.
-  const int first = jb + wave;
-  const int n_my = first < je ? (je - first + WAVES - 1) / WAVES : 0;  // <= 64
-  const int blk_lane = lane < n_my ? trow[first + WAVES * lane] : -1;
 
   // A bad id (outside the pool) still loads block 0, which exists; compute()
   // then masks every row of that tile.
@@ -557,22 +561,40 @@ __global__ __launch_bounds__(128) void lse_reduce_kernel(const float* __restrict
   constexpr int CH = 16;
   const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
   const int d = threadIdx.x;
+  if (d >= D) return;
+  const int64_t base = (int64_t(b) * Hq + h) * max_parts;
+  // The first group is loaded together with the context length (one memory
+  // round trip for up to 16 partitions); slots past the sequence's partition
+  // count hold stale data and are replaced by neutral values below.
+  float m0[CH], l0[CH], o0[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const int64_t pi = base + (u < max_parts ? u : 0);
+    m0[u] = part_m[pi];
+    l0[u] = part_l[pi];
+    o0[u] = part_o[pi * D + d];
+  }
   const int ctx = clamp_ctx(ctx_lens[b], max_blocks, max_context);
-  if (ctx <= 0 || d >= D) return;
+  if (ctx <= 0) return;
   const int nblk = (ctx + BT - 1) / BT;
   const int nparts = (nblk + part_blocks - 1) / part_blocks;
   if (nparts <= 1) return;
-  const int64_t base = (int64_t(b) * Hq + h) * max_parts;
   float M = -INFINITY, L = 0.0f, O = 0.0f;
   for (int p0 = 0; p0 < nparts; p0 += CH) {
     float mv[CH], lv[CH], ov[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const bool ok = p0 + u < nparts;
-      const int64_t pi = base + (ok ? p0 + u : 0);
-      mv[u] = ok ? part_m[pi] : -INFINITY;
-      lv[u] = ok ? part_l[pi] : 0.0f;
-      ov[u] = ok ? part_o[pi * D + d] : 0.0f;
+      if (p0 == 0) {
+        mv[u] = ok ? m0[u] : -INFINITY;
+        lv[u] = ok ? l0[u] : 0.0f;
+        ov[u] = ok ? o0[u] : 0.0f;
+      } else {
+        const int64_t pi = base + (ok ? p0 + u : 0);
+        mv[u] = ok ? part_m[pi] : -INFINITY;
+        lv[u] = ok ? part_l[pi] : 0.0f;
+        ov[u] = ok ? part_o[pi * D + d] : 0.0f;
+      }
     }
     float cm = M;
 #pragma unroll
