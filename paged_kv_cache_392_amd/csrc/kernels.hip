@@ -101,6 +101,16 @@ __device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t
   hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, b) - bias);
 }
 
+// The same codes biased by 1152: two halves holding 1152 + x, exact (no
+// subtraction). Sums over biased codes are corrected once per head.
+__device__ __forceinline__ void i8x4_to_f16x4_biased(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = w ^ 0x80808080u;
+  lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+}
+
+constexpr float I8_BIAS = 1152.0f;
+
 // ---------------------------------------------------------------------------
 // append / copy
 
@@ -324,13 +334,33 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
     uint4 k[S::KL];
     uint4 v[S::NI];
     int blk;
+    uint32_t sc;  // int8: the tile's (K, V) fp16 scales
   };
+
+  // int8: the scales of this wave's tiles, one (K, V) pair per lane like the
+  // block ids, loaded once; each tile takes its pair with readlane. The value
+  // probabilities enter v_dot2 in fp16, pre-scaled by the tile's V scale and
+  // 2^-vexp, with vexp chosen from the wave's largest V scale so that
+  // p * scale_V * 2^-vexp <= 2^8 * 2^7 (p <= 2^8 under the lazy max).
+  uint32_t sc_lane = 0;
+  float vexp_scale = 1.0f, vexp_unscale = 1.0f;
+  if constexpr (I8) {
+    const bool ok = unsigned(blk_lane) < unsigned(prm.num_blocks);
+    sc_lane = ok ? reinterpret_cast<const uint32_t*>(prm.scales)[int64_t(blk_lane) * Hkv + g] : 0u;
+    float vmax = fabsf(hi_half(sc_lane));
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) vmax = fmaxf(vmax, xor_shfl(vmax, m));
+    const int ve = vmax > 128.0f ? int(ceilf(__builtin_log2f(vmax))) - 7 : 0;
+    vexp_scale = __builtin_ldexpf(1.0f, -ve);
+    vexp_unscale = __builtin_ldexpf(1.0f, ve);
+  }
 
   // A bad id (outside the pool) still loads block 0, which exists; compute()
   // then masks every row of that tile.
   auto load = [&](int it, Tile& t) {
     const int blk = __builtin_amdgcn_readlane(blk_lane, it);
     t.blk = blk;
+    if constexpr (I8) t.sc = __builtin_amdgcn_readlane(sc_lane, it);
     const int safe = unsigned(blk) < unsigned(prm.num_blocks) ? blk : 0;
     const char* kb = Kc + safe * blk_stride + head_off;
     const char* vb = Vc + safe * blk_stride + head_off;
@@ -346,15 +376,37 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
     else return mh[e % G];
   };
 
+  // int8: the K codes enter the MFMA as 1152 + x, so every score of head h
+  // carries 1152 * sum_d q[h][d]; qb[h] holds that term (wave-uniform).
+  float qb[G];
+  if constexpr (I8) {
+    float part = 0.0f;  // this lane's dims of head kn % G
+#pragma unroll
+    for (int c = 0; c < S::NCH; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part += float(qa[c][e]);
+    part += xor_shfl(part, 16);
+    part += xor_shfl(part, 32);
+#pragma unroll
+    for (int h = 0; h < G; ++h) qb[h] = I8_BIAS * read_lane(part, h);
+  }
+  auto krow_bias = [&](int e) -> float {
+    if constexpr (G == 8) return odd ? qb[4 + e] : qb[e];
+    else return qb[e % G];
+  };
+  // int8 values: pairs of rows (i, i + 1) are contracted with v_dot2 on fp16
+  // probabilities and biased codes; vb[h] collects the bias part to remove.
+  constexpr bool PAIRS = I8 && S::NI >= 2;
+  float vb[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) vb[h] = 0.0f;
+
   auto compute = [&](int j, Tile& t) {
     const bool blk_ok = unsigned(t.blk) < unsigned(prm.num_blocks);
     float kscale = prm.scale_log2, vscale = 1.0f;
     if constexpr (I8) {
-      if (blk_ok) {
-        const _Float16* sc = prm.scales + (int64_t(t.blk) * Hkv + g) * 2;
-        kscale *= float(sc[0]);
-        vscale = float(sc[1]);
-      }
+      kscale *= lo_half(t.sc);
+      vscale = PAIRS ? hi_half(t.sc) * vexp_scale : hi_half(t.sc);
     }
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -363,8 +415,8 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
       if constexpr (I8) {
         const uint4& w = t.k[c >> 1];
         uint32_t a0, a1, a2, a3;
-        i8x4_to_f16x4((c & 1) ? w.z : w.x, a0, a1);
-        i8x4_to_f16x4((c & 1) ? w.w : w.y, a2, a3);
+        i8x4_to_f16x4_biased((c & 1) ? w.z : w.x, a0, a1);
+        i8x4_to_f16x4_biased((c & 1) ? w.w : w.y, a2, a3);
         kb = __builtin_bit_cast(half8_t, make_uint4(a0, a1, a2, a3));
       } else {
         kb = __builtin_bit_cast(half8_t, t.k[c]);
@@ -378,7 +430,9 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
     bool need = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      s[e] = tvalid ? acc[e] * kscale : -INFINITY;
+      float raw = acc[e];
+      if constexpr (I8) raw -= krow_bias(e);  // remove 1152 * sum(q) of the biased codes
+      s[e] = tvalid ? raw * kscale : -INFINITY;
       need |= s[e] > mrow(e) + LAZY_MAX;
     }
     if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first tile
@@ -397,6 +451,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
         mh[h] = mn;
 #pragma unroll
         for (int e = 0; e < S::CE; ++e) o[h][e] *= alpha[h];
+        vb[h] *= alpha[h];
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -437,6 +492,38 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
       for (int i = 0; i < S::NI; ++i)
         if (!blk_ok || j * BT + vt + S::RPI * i >= ctx) t.v[i] = make_uint4(0, 0, 0, 0);
     }
+    if constexpr (PAIRS) {
+#pragma unroll
+      for (int i = 0; i + 1 < S::NI; i += 2) {
+        uint32_t P[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const half2_t ph = {(_Float16)pv[i][h], (_Float16)pv[i + 1][h]};
+          P[h] = __builtin_bit_cast(uint32_t, ph);
+          vb[h] = dot2(P[h], 0x64806480u, vb[h]);  // (1152, 1152)
+        }
+        const uint32_t a4[4] = {t.v[i].x, t.v[i].y, t.v[i].z, t.v[i].w};
+        const uint32_t b4[4] = {t.v[i + 1].x, t.v[i + 1].y, t.v[i + 1].z, t.v[i + 1].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t alo, ahi, blo, bhi;
+          i8x4_to_f16x4_biased(a4[w], alo, ahi);
+          i8x4_to_f16x4_biased(b4[w], blo, bhi);
+          // (row i, row i + 1) pairs of one dim each
+          const uint32_t x0 = __builtin_amdgcn_perm(blo, alo, 0x05040100u);
+          const uint32_t x1 = __builtin_amdgcn_perm(blo, alo, 0x07060302u);
+          const uint32_t x2 = __builtin_amdgcn_perm(bhi, ahi, 0x05040100u);
+          const uint32_t x3 = __builtin_amdgcn_perm(bhi, ahi, 0x07060302u);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            o[h][4 * w + 0] = dot2(P[h], x0, o[h][4 * w + 0]);
+            o[h][4 * w + 1] = dot2(P[h], x1, o[h][4 * w + 1]);
+            o[h][4 * w + 2] = dot2(P[h], x2, o[h][4 * w + 2]);
+            o[h][4 * w + 3] = dot2(P[h], x3, o[h][4 * w + 3]);
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < S::NI; ++i) {
       const uint32_t w4[4] = {t.v[i].x, t.v[i].y, t.v[i].z, t.v[i].w};
@@ -460,6 +547,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
           }
         }
       }
+    }
     }
     // the next tile rewrites p_lds: its writes stay behind these reads
     __builtin_amdgcn_wave_barrier();
@@ -487,6 +575,12 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
     }
   }
 
+  if constexpr (PAIRS) {  // remove the bias part and the 2^-vexp pre-scale
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < S::CE; ++e) o[h][e] = (o[h][e] - vb[h]) * vexp_unscale;
+  }
   // wave totals: l over the 16 tokens of each score row, o over the V row groups
   float lh[G];
 #pragma unroll

@@ -142,6 +142,17 @@ def test_tiny_int8(seed, Hq, Hkv, D):
     lib.close()
 
 
+@pytest.mark.parametrize("v_scale", [300.0, 9000.0])
+def test_int8_large_value_scales(v_scale):
+    """V values of magnitude ~1e3..3e4 (fp16 V scales far above 1): the
+    value probabilities enter the fp16 dot products pre-scaled by a power of
+    two, so nothing overflows; error bound scaled with the values."""
+    w = workloads.tiny_random(811, B=4, Hq=32, Hkv=8, D=128, max_len=300, dtype="i8", v_scale=v_scale)
+    lib, o = run_pair(w)
+    assert max_err(lib, o) <= I8_TOL * v_scale
+    lib.close()
+
+
 @pytest.mark.parametrize("ptok", [16, 64, 128, 256, 512, 4096])
 def test_partition_size_within_tolerance(ptok):
     w = workloads.tiny_random(901, B=6, Hq=8, Hkv=2, D=128, max_len=1500)

@@ -93,19 +93,23 @@ def _normal(rng, shape):
     return rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
 
 
-def _decode_batch(name, rng, N, Hq, Hkv, D, lens, free_order, dtype="f16", append=True):
+def _scaled(x, factor):
+    return x if factor == 1.0 else (x.astype(np.float32) * np.float32(factor)).astype(np.float16)
+
+
+def _decode_batch(name, rng, N, Hq, Hkv, D, lens, free_order, dtype="f16", append=True, v_scale=1.0):
     """Shared shape of C1, C2, C5 and the headline: B sequences prefilled to
     ``lens``, one appended token each (unless ``append`` is False), then one
-    decode step."""
+    decode step. ``v_scale`` multiplies every V value (after the same draws)."""
     w = Workload(name, N, Hq, Hkv, D, dtype, free_order)
     names = [f"s{i}" for i in range(len(lens))]
     for s in names:
         w.steps.append(("create", s))
     for s, n in zip(names, lens):
-        w.steps.append(("prefill", s, _normal(rng, (n, Hkv, D)), _normal(rng, (n, Hkv, D))))
+        w.steps.append(("prefill", s, _normal(rng, (n, Hkv, D)), _scaled(_normal(rng, (n, Hkv, D)), v_scale)))
     if append:
         B = len(lens)
-        w.steps.append(("append", names, _normal(rng, (B, Hkv, D)), _normal(rng, (B, Hkv, D))))
+        w.steps.append(("append", names, _normal(rng, (B, Hkv, D)), _scaled(_normal(rng, (B, Hkv, D)), v_scale)))
     w.steps.append(("decode", names, _normal(rng, (len(lens), Hq, D))))
     return w
 
@@ -207,14 +211,15 @@ def headline(seed=6, batch=16, ctx=8192, spare_blocks=0):
     return w
 
 
-def tiny_random(seed, B=3, Hq=4, Hkv=2, D=64, max_len=40, N=None, dtype="f16"):
-    """Small random shapes for brute-force and edge-case checks."""
+def tiny_random(seed, B=3, Hq=4, Hkv=2, D=64, max_len=40, N=None, dtype="f16", v_scale=1.0):
+    """Small random shapes for brute-force and edge-case checks; ``v_scale``
+    stretches the V values (large int8 scales)."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(1, max_len + 1, B).tolist()
     if N is None:
         N = sum(-(-(n + 1) // 16) for n in lens) + 4
     order = rng.permutation(N).astype(np.int32)
-    w = _decode_batch(f"tiny_{seed}", rng, N, Hq, Hkv, D, lens, order, dtype=dtype)
+    w = _decode_batch(f"tiny_{seed}", rng, N, Hq, Hkv, D, lens, order, dtype=dtype, v_scale=v_scale)
     w.seed = seed
     return w
 
