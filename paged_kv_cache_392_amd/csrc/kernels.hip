@@ -753,8 +753,12 @@ int hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 // Tokens per split-K partition: explicit, from PKV_PARTITION_TOKENS, or
-// chosen so that about 2048 work-groups (8 per CU) are in flight, with at
-// least 4 blocks (one per wave) per partition.
+// chosen for a number of work-groups measured best on MI355X (256 CUs, two
+// decode work-groups resident per CU): about 2048 for fp16 (four rounds:
+// 528-token partitions at 8K context, 86 us against 91-97 us for 1024-2048)
+// and about 512 for int8 (one round: 2048-token partitions, 49 us against
+// 64 us at 528, where a work-group's first-tile latency weighs on half the
+// bytes per tile). At least 4 blocks (one per wave) per partition.
 int choose_part_blocks(const pkv_config& c, int B, int max_context, int partition_tokens) {
   if (partition_tokens == 0) {
     if (const char* env = std::getenv("PKV_PARTITION_TOKENS")) partition_tokens = std::atoi(env);
@@ -762,7 +766,8 @@ int choose_part_blocks(const pkv_config& c, int B, int max_context, int partitio
   if (partition_tokens > 0) return std::min(partition_tokens, MAX_PARTITION_TOKENS) / BT;
   const int nblk = (max_context + BT - 1) / BT;
   const int64_t groups = int64_t(B) * c.num_kv_heads;
-  int64_t want_parts = (2048 + groups - 1) / groups;
+  const int64_t want_wgs = c.dtype == PKV_I8 ? 512 : 2048;
+  int64_t want_parts = (want_wgs + groups - 1) / groups;
   if (want_parts < 1) want_parts = 1;
   int pb = int((nblk + want_parts - 1) / want_parts);
   if (pb < 4) pb = 4;
