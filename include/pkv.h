@@ -138,8 +138,18 @@ int pkv_copy_blocks(const pkv_config* cfg, void* pool_dev, const int32_t* pairs_
 /* Append ([p2] §2.2 pseudocode: the new token's k and v go to the cache
  * tail; cached K/V are never modified afterwards, [p1] §二): for token i,
  * write k_dev[i] and v_dev[i] (fp16, contiguous [n_tokens][Hkv][D], device)
- * into slot slots_dev[i] (int32, device) of `layer`. Bit-exact copy. Slots
- * outside [0, 16N) are skipped. fp16 pools only (UNSUPPORTED for int8). */
+ * into slot slots_dev[i] (int32, device) of `layer`. Slots outside [0, 16N)
+ * are skipped.
+ *   fp16 pools: bit-exact copy.
+ *   int8 pools ([p2] §4.1, 8-bit K/V with group scales): quantise on write,
+ *   one (block, KV head) scale each for K and V. A token at offset 0 sets
+ *   the block's scale from its own absmax (fp16(absmax / 127)); a token
+ *   whose absmax fits 127 * scale is coded with that scale; otherwise the
+ *   block takes the new token's scale and its earlier codes are re-rounded
+ *   into it (the scale never shrinks; earlier rows move by at most half a
+ *   step). Codes are rint(x / scale) clipped to [-127, 127]. Tokens that
+ *   write one block must be adjacent in the call and in increasing offset,
+ *   as pkv_seq_reserve returns them. */
 int pkv_append_kv(const pkv_config* cfg, void* pool_dev, int32_t layer, const void* k_dev,
                   const void* v_dev, const int32_t* slots_dev, int32_t n_tokens, void* stream);
 

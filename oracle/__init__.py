@@ -44,7 +44,7 @@ from .sizes import (
 from .allocator import RefAllocator, NoBlocks, UnknownSeq
 from .cache import RefCache
 from .attention import decode, decode_seq_head, brute_decode, gather
-from .quant import quantize_block_int8, quantize_pool_int8, dequantize_int8
+from .quant import quantize_block_int8, quantize_pool_int8, dequantize_int8, append_row_int8
 
 __all__ = [
     "BLOCK_TOKENS",
@@ -62,4 +62,5 @@ __all__ = [
     "quantize_block_int8",
     "quantize_pool_int8",
     "dequantize_int8",
+    "append_row_int8",
 ]

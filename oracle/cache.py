@@ -36,16 +36,29 @@ class RefCache:
             self.V[...] = fill
 
     def append(self, layer, k, v, slots):
-        """Write token i's K/V rows ``k[i], v[i]`` (shape ``[Hkv, D]``) at
-        ``slots[i] = block * 16 + offset`` of ``layer``: the decode-step
-        write of the new token's K and V at the cache tail ([p2] §2.2)."""
+        """Write token i's K/V rows ``k[i], v[i]`` (fp16, shape ``[Hkv, D]``)
+        at ``slots[i] = block * 16 + offset`` of ``layer``: the decode-step
+        write of the new token's K and V at the cache tail ([p2] §2.2).
+
+        An int8 store quantises on write, token by token in the given order
+        (``append_row_int8``; a block may be re-expressed in a larger scale
+        when a new row exceeds its range)."""
+        from .quant import append_row_int8
         k = np.asarray(k)
         v = np.asarray(v)
         assert k.shape == v.shape == (len(slots), self.kv_heads, self.head_dim)
         for i, slot in enumerate(slots):
             blk, off = divmod(int(slot), BLOCK_TOKENS)
-            self.K[layer, blk, :, off, :] = k[i]
-            self.V[layer, blk, :, off, :] = v[i]
+            if self.dtype == "f16":
+                self.K[layer, blk, :, off, :] = k[i]
+                self.V[layer, blk, :, off, :] = v[i]
+                continue
+            for g in range(self.kv_heads):
+                for which, store, rows in ((0, self.K, k), (1, self.V, v)):
+                    codes, sc = append_row_int8(store[layer, blk, g], self.scales[layer, blk, g, which], off,
+                                                rows[i, g])
+                    store[layer, blk, g] = codes
+                    self.scales[layer, blk, g, which] = sc
 
     def copy_blocks(self, pairs):
         """Copy-on-write: each ``(src, dst)`` copies the whole block (every

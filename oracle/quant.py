@@ -16,6 +16,9 @@ bits halves the cache. The pages do not give the formula. Reading taken:
 * slots past the tile's filled count are stored as 0.
 
 Dequantisation is ``code * scale`` (exact in fp64).
+
+``append_row_int8`` is the quantise-on-write rule for one new token in a
+partly filled block (the int8 append step).
 """
 
 import numpy as np
@@ -39,6 +42,48 @@ def quantize_block_int8(x, filled=BLOCK_TOKENS):
     q = np.rint(live / np.float32(scale))
     codes[:filled] = np.clip(q, -127, 127).astype(np.int8)
     return codes, scale
+
+
+def append_row_int8(codes, scale, off, x):
+    """Quantise-on-write of one new row ``x [D]`` (fp16) into slot ``off`` of
+    a ``[16, D]`` int8 tile whose rows ``< off`` are filled with ``scale``.
+
+    The pages say only that 8-bit K/V carry group scale factors ([p2] §4.1);
+    appending one token at a time to a block already holding codes needs a
+    rule, and the reading taken is the plainest that keeps every filled row
+    within half a step of its value:
+
+    * a token at offset 0 opens the block: its scale comes from its own
+      absmax, exactly as the block quantiser does for a one-row tile;
+    * a token whose absmax fits the block's range (``a <= 127 * scale``) is
+      quantised with the block's scale; earlier codes stay as they are;
+    * otherwise the block takes the new row's scale
+      ``fp16(fp32(a) / 127)`` and its earlier codes are re-expressed in it,
+      ``clip(rint(fp32(code) * fp32(scale) / fp32(new_scale)), -127, 127)``.
+
+    Divisions are IEEE fp32, ``rint`` rounds half to even, and a zero scale
+    means zero codes. Returns ``(codes', scale')``; rows past ``off`` are
+    left unchanged."""
+    codes = np.array(codes, np.int8, copy=True)
+    x32 = np.asarray(x, np.float16).astype(np.float32)
+    a = np.float32(np.max(np.abs(x32)))
+    s = np.float16(scale)
+    if off == 0:
+        new = np.float16(a / np.float32(127.0))
+    elif a <= np.float32(127.0) * np.float32(s):
+        new = s
+    else:
+        new = np.float16(a / np.float32(127.0))
+        if new == 0:
+            codes[:off] = 0
+        else:
+            old = codes[:off].astype(np.float32) * np.float32(s)
+            codes[:off] = np.clip(np.rint(old / np.float32(new)), -127, 127).astype(np.int8)
+    if new == 0:
+        codes[off] = 0
+    else:
+        codes[off] = np.clip(np.rint(x32 / np.float32(new)), -127, 127).astype(np.int8)
+    return codes, new
 
 
 def dequantize_int8(codes, scale):

@@ -138,6 +138,76 @@ __global__ __launch_bounds__(256) void append_kv_f16_kernel(uint4* __restrict__ 
   Vl[dst] = v[src];
 }
 
+// int8 quantise-on-write. One wave per (token i, KV head h, K or V); the
+// wave whose token opens a run of consecutive tokens writing the same block
+// appends the whole run in order (a block's scale depends on the order). Per
+// token, with a = max |x| of its row and s the block's scale:
+//   offset 0:        s' = fp16(a / 127)           (the block is opened)
+//   a <= 127 * s:    s' = s                       (the row fits the range)
+//   otherwise:       s' = fp16(a / 127), and the earlier rows' codes are
+//                    re-expressed: rint(code * s / s')
+// then the row's codes are rint(x / s'), clipped to [-127, 127]; a zero
+// scale gives zero codes. Divisions are IEEE fp32, rint rounds half to
+// even. Each lane owns the same D/64 dims of every row, so it only reads
+// back bytes it wrote itself.
+template <int D>
+__global__ __launch_bounds__(64) void append_kv_i8_kernel(int8_t* __restrict__ Kl, int8_t* __restrict__ Vl,
+                                                          _Float16* __restrict__ Sl,
+                                                          const _Float16* __restrict__ k,
+                                                          const _Float16* __restrict__ v,
+                                                          const int32_t* __restrict__ slots, int n, int Hkv,
+                                                          int num_blocks) {
+  constexpr int PER = D / 64;  // dims per lane
+  const int i = blockIdx.x, h = blockIdx.y, which = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int nslots = num_blocks * BT;
+  const int slot = slots[i];
+  if (slot < 0 || slot >= nslots) return;
+  const int blk = slot / BT;
+  if (i > 0) {
+    const int prev = slots[i - 1];
+    if (prev >= 0 && prev < nslots && prev / BT == blk) return;  // inside a run led by an earlier wave
+  }
+  int8_t* tile = (which ? Vl : Kl) + (int64_t(blk) * Hkv + h) * BT * D;
+  _Float16* sp = Sl + (int64_t(blk) * Hkv + h) * 2 + which;
+  const _Float16* src = which ? v : k;
+  float sc = float(*sp);
+  for (int t = i; t < n; ++t) {
+    const int sl = slots[t];
+    if (t > i && (sl < 0 || sl >= nslots || sl / BT != blk)) break;
+    const int off = sl % BT;
+    float x[PER];
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      x[e] = float(src[(int64_t(t) * Hkv + h) * D + lane + 64 * e]);
+      a = fmaxf(a, fabsf(x[e]));
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) a = fmaxf(a, xor_shfl(a, m));
+    float sn = sc;
+    bool requant = false;
+    if (off == 0 || !(a <= 127.0f * sc)) {
+      sn = float(_Float16(a / 127.0f));
+      requant = off > 0;
+    }
+    if (requant) {
+      for (int r = 0; r < off; ++r)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          int8_t& c = tile[r * D + lane + 64 * e];
+          c = sn == 0.0f ? int8_t(0) : int8_t(fminf(fmaxf(__builtin_rintf(float(c) * sc / sn), -127.0f), 127.0f));
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      tile[off * D + lane + 64 * e] =
+          sn == 0.0f ? int8_t(0) : int8_t(fminf(fmaxf(__builtin_rintf(x[e] / sn), -127.0f), 127.0f));
+    sc = sn;
+  }
+  if (lane == 0) *sp = _Float16(sc);
+}
+
 // Copy-on-write: blockIdx = (pair, layer, region); region 0 = K, 1 = V,
 // 2 = int8 scales. Copies the whole (layer, block) slab: Hkv tiles.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ pool, const int32_t* __restrict__ pairs,
@@ -838,13 +908,28 @@ int pkv_append_kv(const pkv_config* cfg, void* pool_dev, int32_t layer, const vo
                   const int32_t* slots_dev, int32_t n_tokens, void* stream) {
   int st = pkv::validate_config(cfg);
   if (st != PKV_OK) return st;
-  if (cfg->dtype != PKV_F16) return pkv::fail(PKV_ERR_UNSUPPORTED, "append_kv writes fp16 pools only");
   if (layer < 0 || layer >= cfg->num_layers) return pkv::fail(PKV_ERR_INVALID_ARG, "layer %d out of range", layer);
   if (n_tokens < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "n_tokens must be >= 0");
   if (n_tokens == 0) return PKV_OK;
   if (!pool_dev || !k_dev || !v_dev || !slots_dev) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
   if (!aligned16(pool_dev) || !aligned16(k_dev) || !aligned16(v_dev))
     return pkv::fail(PKV_ERR_INVALID_ARG, "pool, k and v must be 16-byte aligned");
+  if (cfg->dtype == PKV_I8) {
+    if (n_tokens > INT32_MAX / 2) return pkv::fail(PKV_ERR_INVALID_ARG, "too many tokens in one call");
+    if (cfg->num_kv_heads > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
+    const int64_t layer_bytes = pkv::layer_elems(*cfg);
+    char* base = static_cast<char*>(pool_dev);
+    int8_t* Kl = reinterpret_cast<int8_t*>(base + layer * layer_bytes);
+    int8_t* Vl = reinterpret_cast<int8_t*>(base + pkv::region_bytes(*cfg) + layer * layer_bytes);
+    _Float16* Sl = reinterpret_cast<_Float16*>(base + 2 * pkv::region_bytes(*cfg) +
+                                               int64_t(layer) * cfg->num_blocks * cfg->num_kv_heads * 2 * 2);
+    const dim3 grid(unsigned(n_tokens), unsigned(cfg->num_kv_heads), 2);
+    auto kern = cfg->head_dim == 128 ? append_kv_i8_kernel<128> : append_kv_i8_kernel<64>;
+    hipLaunchKernelGGL(kern, grid, dim3(64), 0, static_cast<hipStream_t>(stream), Kl, Vl, Sl,
+                       static_cast<const _Float16*>(k_dev), static_cast<const _Float16*>(v_dev), slots_dev,
+                       n_tokens, cfg->num_kv_heads, cfg->num_blocks);
+    return hip_status(hipGetLastError(), "append_kv launch");
+  }
   const int64_t layer_bytes = pkv::layer_elems(*cfg) * 2;
   char* base = static_cast<char*>(pool_dev);
   uint4* Kl = reinterpret_cast<uint4*>(base + layer * layer_bytes);

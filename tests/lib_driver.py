@@ -60,7 +60,7 @@ class LibRun:
         return slots, cow
 
     def _write(self, slots, cow, k, v):
-        if self.cache is None or self.w.dtype == "i8":
+        if self.cache is None or (self.w.dtype == "i8" and self.w.i8_write != "append"):
             return
         import torch
         from paged_kv_cache_392_amd.cache import _dev_i32
@@ -160,7 +160,7 @@ class LibRun:
                "fused": fused is not None}
         if compute and self.cache is not None:
             import torch
-            if self.w.dtype == "i8":
+            if self.w.dtype == "i8" and self.w.i8_write != "append":
                 self.upload_quantised()
             dev = self.cache.device
             qd = torch.from_numpy(np.ascontiguousarray(q)).to(dev)

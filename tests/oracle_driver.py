@@ -16,9 +16,12 @@ class OracleRun:
         self.w = w
         self.layer = layer
         self.alloc = oracle.RefAllocator(w.num_blocks, w.free_order)
-        # fp16 store; for an int8 workload this is the unquantised shadow
-        # that is quantised just before each decode.
-        self.cache = oracle.RefCache(1, w.num_blocks, w.num_kv_heads, w.head_dim, "f16", fill=fill)
+        # fp16 store; for a bulk-quantised int8 workload this is the
+        # unquantised shadow that is quantised just before each decode; an
+        # int8 workload written by append quantises every token on write.
+        self.i8_append = w.dtype == "i8" and w.i8_write == "append"
+        self.cache = oracle.RefCache(1, w.num_blocks, w.num_kv_heads, w.head_dim,
+                                     "i8" if self.i8_append else "f16", fill=None if self.i8_append else fill)
         self.q8 = None
         self.seq = {}
         self.reserves = []  # (step index, name, slots, cow pairs)
@@ -107,7 +110,7 @@ class OracleRun:
         rec = {"names": list(names), "tables": np.array(tables, np.int32),
                "lens": np.array(lens, np.int32), "q": q, "out": None}
         if self.w.dtype == "i8":
-            self.q8 = self.quantised_cache()
+            self.q8 = self.cache if self.i8_append else self.quantised_cache()
         if compute:
             cache = self.q8 if self.w.dtype == "i8" else self.cache
             rec["out"] = oracle.decode(cache, q, tables, lens, 0, self.w.scale)

@@ -47,6 +47,21 @@ def check_stored_bytes(lib, o):
         assert np.array_equal(V[blk, :, off].view(np.uint16), o.cache.V[0, blk, :, off].view(np.uint16)), (blk, off)
 
 
+def check_stored_int8(lib, o):
+    """Codes of every live slot and the scales of every block holding one,
+    bit for bit (int8 pools written by append)."""
+    K = lib.cache.region(0, 0).cpu().numpy()
+    V = lib.cache.region(1, 0).cpu().numpy()
+    S = lib.cache.scales()[0].cpu().numpy()
+    blocks = set()
+    for blk, off in sorted(live_slots(o)):
+        assert np.array_equal(K[blk, :, off], o.cache.K[0, blk, :, off]), (blk, off)
+        assert np.array_equal(V[blk, :, off], o.cache.V[0, blk, :, off]), (blk, off)
+        blocks.add(blk)
+    for blk in sorted(blocks):
+        assert np.array_equal(S[blk].view(np.uint16), o.cache.scales[0, blk].view(np.uint16)), blk
+
+
 def check_host_records(lib, o):
     assert len(lib.reserves) == len(o.reserves)
     for a, b in zip(lib.reserves, o.reserves):
@@ -138,6 +153,31 @@ def test_tiny_shapes(seed, Hq, Hkv, D):
 def test_tiny_int8(seed, Hq, Hkv, D):
     w = workloads.tiny_random(800 + seed, B=4, Hq=Hq, Hkv=Hkv, D=D, max_len=200, dtype="i8")
     lib, o = run_pair(w)
+    assert max_err(lib, o) <= I8_TOL
+    lib.close()
+
+
+@pytest.mark.parametrize("seed,Hq,Hkv,D", [(21, 4, 2, 64), (22, 32, 8, 128), (23, 8, 1, 128), (24, 16, 2, 64),
+                                          (25, 64, 8, 128)])
+def test_int8_append_quantises_on_write_like_the_oracle(seed, Hq, Hkv, D):
+    """int8 pools written token by token (bulk prefill runs and the decode
+    step's append): codes and scales bit-exact, decode within the int8 bar."""
+    w = workloads.tiny_random(seed, B=4, Hq=Hq, Hkv=Hkv, D=D, max_len=300, dtype="i8", i8_write="append")
+    lib, o = run_pair(w)
+    check_host_records(lib, o)
+    check_stored_int8(lib, o)
+    assert max_err(lib, o) <= I8_TOL
+    lib.close()
+
+
+def test_int8_append_copy_on_write_prefix():
+    """The copy-on-write prefix workload on an int8 pool: the fork appends
+    into a shared partial block, whose codes and scales are copied first."""
+    w = workloads.c4_prefix(dtype="i8", sharers=6, prefix=300)
+    lib, o = run_pair(w)
+    assert any(cow for (_, _, _, cow) in o.reserves)
+    check_host_records(lib, o)
+    check_stored_int8(lib, o)
     assert max_err(lib, o) <= I8_TOL
     lib.close()
 

@@ -283,7 +283,8 @@ def test_device_calls_validate_before_launch():
     assert status(lambda: pkv.pkv_append_kv(cfg, fake + 8, 0, fake, fake, fake, 1, None)) == C.PKV_ERR_INVALID_ARG
     assert status(lambda: pkv.pkv_append_kv(cfg, 0, 0, fake, fake, fake, 1, None)) == C.PKV_ERR_INVALID_ARG
     i8 = pkv.make_config(1, 16, 2, 64, "i8")
-    assert status(lambda: pkv.pkv_append_kv(i8, fake, 0, fake, fake, fake, 1, None)) == C.PKV_ERR_UNSUPPORTED
+    assert status(lambda: pkv.pkv_append_kv(i8, fake, 1, fake, fake, fake, 1, None)) == C.PKV_ERR_INVALID_ARG
+    assert status(lambda: pkv.pkv_append_kv(i8, fake, 0, fake + 4, fake, fake, 1, None)) == C.PKV_ERR_INVALID_ARG
     assert status(lambda: pkv.pkv_copy_blocks(cfg, fake, 0, 1, None)) == C.PKV_ERR_INVALID_ARG
 
     lens = np.array([5, 0], np.int32)

@@ -148,3 +148,20 @@ def test_size_formula_without_factor_two_is_caught(monkeypatch):
                         lambda L, H, D, E, n, B=1: L * H * D * E * n * B)
     with pytest.raises(AssertionError):
         check_printed_sizes(__import__("os").path.join(__import__("os").path.dirname(__file__), "golden"))
+
+
+def test_append_without_requantising_is_caught(monkeypatch):
+    """A quantise-on-write that raises the scale but keeps the old codes
+    breaks the bound on earlier rows."""
+    from test_oracle_quant import test_append_beyond_range_requantises_the_block
+
+    real = qnt.append_row_int8
+
+    def lazy(codes, scale, off, x):
+        new_codes, new_scale = real(codes, scale, off, x)
+        new_codes[:off] = np.asarray(codes)[:off]
+        return new_codes, new_scale
+
+    monkeypatch.setattr(oracle, "append_row_int8", lazy)
+    with pytest.raises(AssertionError):
+        test_append_beyond_range_requantises_the_block()

@@ -79,6 +79,9 @@ class Workload:
     steps: list = field(default_factory=list)
     seed: int = 0
     layers: int = 1  # layers whose contents come from this script
+    # int8 workloads: "bulk" = the fp16 K/V are quantised block by block on
+    # the host before decode; "append" = every token is quantised on write
+    i8_write: str = "bulk"
 
     @property
     def scale(self):
@@ -159,7 +162,7 @@ def c3_mixed(seed=3, batch=16, churn_requests=200):
     return w
 
 
-def c4_prefix(seed=4, sharers=32, prefix=2048):
+def c4_prefix(seed=4, sharers=32, prefix=2048, dtype="f16"):
     """Copy-on-write prefix sharing: one 2048-token prefix shared by 32
     sequences, private suffixes of U[64, 1024] tokens, one decode step; then
     the lowest-index sequence whose length is not a multiple of 16 forks, the
@@ -169,7 +172,8 @@ def c4_prefix(seed=4, sharers=32, prefix=2048):
     N = 2304
     order = rng.permutation(N).astype(np.int32)
     suffix = rng.integers(64, 1025, sharers).tolist()
-    w = Workload("c4_prefix", N, 32, 8, 128, "f16", order)
+    w = Workload("c4_prefix", N, 32, 8, 128, dtype, order)
+    w.i8_write = "append"  # int8: the shared prefix and every suffix token quantised on write
     names = [f"s{i}" for i in range(sharers)]
     w.steps.append(("create", names[0]))
     w.steps.append(("prefill", names[0], _normal(rng, (prefix, 8, 128)), _normal(rng, (prefix, 8, 128))))
@@ -211,7 +215,7 @@ def headline(seed=6, batch=16, ctx=8192, spare_blocks=0):
     return w
 
 
-def tiny_random(seed, B=3, Hq=4, Hkv=2, D=64, max_len=40, N=None, dtype="f16", v_scale=1.0):
+def tiny_random(seed, B=3, Hq=4, Hkv=2, D=64, max_len=40, N=None, dtype="f16", v_scale=1.0, i8_write="bulk"):
     """Small random shapes for brute-force and edge-case checks; ``v_scale``
     stretches the V values (large int8 scales)."""
     rng = np.random.default_rng(seed)
@@ -221,6 +225,7 @@ def tiny_random(seed, B=3, Hq=4, Hkv=2, D=64, max_len=40, N=None, dtype="f16", v
     order = rng.permutation(N).astype(np.int32)
     w = _decode_batch(f"tiny_{seed}", rng, N, Hq, Hkv, D, lens, order, dtype=dtype, v_scale=v_scale)
     w.seed = seed
+    w.i8_write = i8_write
     return w
 
 
