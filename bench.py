@@ -49,6 +49,10 @@ def parse():
                     help="launch every layer directly instead of replaying layers 1.. as one HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--workload", choices=["headline", "c5"], default="headline",
+                    help="headline: the fp16 batch-16 8K decode step (the bench line); c5: the int8 "
+                         "batch-16 8K decode-only step over 32 int8 layer pools (timing and profiling; "
+                         "int8 parity is covered by the GPU tests)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -110,6 +114,10 @@ def main():
     import paged_kv_cache_392_amd as pkv
     from paged_kv_cache_392_amd import _capi as C
     import workloads
+
+    if args.workload == "c5":
+        int8_decode_bench(args, torch, pkv, C, workloads)
+        return
 
     dev = torch.device("cuda:0")
     K, W, L = args.steps, args.warmup, args.layers
@@ -389,6 +397,127 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, first_out, first_tables, first_lens, args.cpu_seconds,
                                               decode_bytes)
     print(json.dumps(result), flush=True)
+
+
+def int8_decode_bench(args, torch, pkv, C, workloads):
+    """int8 decode-only step (the int8 long-context config): batch 16 at
+    context 8192, 32 q / 8 KV heads, d128, one fp16 scale per (block, KV
+    head) for K and V, over 32 layer pools (8 GiB of codes). Codes and scales
+    are seeded device noise (values do not change the timing); tables come
+    from the library's allocator in the config's seeded block order. Layer 0
+    is launched directly with timing events, layers 1..31 are replayed from
+    one HIP graph and checked against direct launches bit for bit."""
+    dev = torch.device("cuda:0")
+    K, W, L = args.steps, args.warmup, args.layers
+    w = workloads.c5_int8()
+    ctx = 8192
+    N = w.num_blocks
+    cache = pkv.PagedKVCache(L, N, HKV, D, "i8", w.free_order, dev)
+    lib = C.load()
+    sp = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    for layer in range(L):
+        for which in (0, 1):
+            r = cache.region(which, layer)
+            r.copy_(torch.randint(-127, 128, r.shape, dtype=torch.int8, device=dev, generator=gen))
+    cache.scales().uniform_(0.01, 0.03, generator=gen)
+    seqs = [cache.create_seq() for _ in range(B)]
+    for s in seqs:
+        cache.reserve([s], [ctx])
+    max_blocks = ctx // 16
+    tables_h, lens_h = cache.block_tables(seqs, max_blocks)
+    tables_d = torch.from_numpy(tables_h).to(dev)
+    lens_d = torch.from_numpy(lens_h).to(dev)
+    q = torch.empty((L, B, HQ, D), dtype=torch.float16, device=dev).normal_(generator=gen)
+    out = torch.empty_like(q)
+    ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, HQ, ctx, args.partition_tokens)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    argv = []
+    for layer in range(L):
+        a = C.pkv_decode_args()
+        a.cfg = ctypes.pointer(cache.cfg)
+        a.pool_dev = cache.pool.data_ptr()
+        a.layer = layer
+        a.q_dev = q[layer].data_ptr()
+        a.num_seqs = B
+        a.num_q_heads = HQ
+        a.block_tables_dev = tables_d.data_ptr()
+        a.max_blocks = max_blocks
+        a.ctx_lens_dev = lens_d.data_ptr()
+        a.ctx_lens_host = C._i32p(lens_h)
+        a.max_context = ctx
+        a.out_dev = out[layer].data_ptr()
+        a.scale = 1.0 / math.sqrt(D)
+        a.workspace_dev = ws.data_ptr()
+        a.workspace_bytes = ws.numel()
+        a.partition_tokens = args.partition_tokens
+        argv.append(a)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for group in ev:
+        for e in group:
+            e.record()
+    ev_ptrs = [ctypes.cast((ctypes.c_void_p * 4)(*[e.cuda_event for e in g]), ctypes.POINTER(ctypes.c_void_p))
+               for g in ev]
+    keep = list(ev_ptrs)
+
+    def launch(layer, events=None, stream_handle=None):
+        a = argv[layer]
+        a.timing_events = events
+        C._check(lib.pkv_paged_decode(ctypes.byref(a), sp if stream_handle is None else stream_handle))
+
+    for _ in range(W):
+        for layer in range(L):
+            launch(layer)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream().cuda_stream
+        for layer in range(1, L):
+            launch(layer, stream_handle=cs)
+    torch.cuda.synchronize()
+    launch(0)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(K):
+        launch(0, keep[i])
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / K
+    check = [1, L // 2, L - 1] if L > 2 else list(range(1, L))
+    got = {l: out[l].clone() for l in check}
+    for l in check:
+        launch(l)
+    torch.cuda.synchronize()
+    same = all(torch.equal(got[l].view(torch.int16), out[l].view(torch.int16)) for l in check)
+    split_ms = np.array([g[0].elapsed_time(g[1]) for g in ev])
+    merge_ms = np.array([g[2].elapsed_time(g[3]) for g in ev])
+    nblk = ctx // 16
+    kernel_bytes = B * ctx * 2 * HKV * D + B * nblk * HKV * 4 + B * HQ * D * 2 + B * nblk * 4 + B * 4
+    step_bytes = L * (kernel_bytes + B * HQ * D * 2)
+    achieved = kernel_bytes / (float(np.mean(split_ms)) * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "paged decode HBM GB/s (% of peak), int8 K/V, 32q/8kv d128",
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": "int8 decode-only step, batch 16, context 8192, 32 q heads / 8 KV heads, "
+                               "head_dim 128, int8 K/V with one fp16 scale per (block, KV head), "
+                               "32 layer pools", "layers": L, "partition_tokens": args.partition_tokens or "auto"},
+        "decode_tok_s": round(B / (ms_per_step * 1e-3), 1),
+        "split_kernel_us": round(float(np.mean(split_ms)) * 1e3, 2),
+        "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2),
+        "graph_matches_eager_bitwise": same,
+        "roofline": {"bound": "hbm", "kernel": "paged_decode_kernel<128,4,i8> (split-K decode)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(kernel_bytes)},
+        "cpu_baseline": None,
+    }), flush=True)
 
 
 def cpu_baseline(w, gpu_out, gpu_tables, gpu_lens, budget_s, decode_bytes):
