@@ -49,10 +49,11 @@ def parse():
                     help="launch every layer directly instead of replaying layers 1.. as one HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--workload", choices=["headline", "c5"], default="headline",
+    ap.add_argument("--workload", choices=["headline", "c5", "prefix"], default="headline",
                     help="headline: the fp16 batch-16 8K decode step (the bench line); c5: the int8 "
-                         "batch-16 8K decode-only step over 32 int8 layer pools (timing and profiling; "
-                         "int8 parity is covered by the GPU tests)")
+                         "batch-16 8K decode-only step over 32 int8 layer pools; prefix: the decode step "
+                         "of 32 sequences sharing a 2048-token prefix, with and without the shared-prefix "
+                         "plan (timing and profiling; parity is covered by the GPU tests)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -117,6 +118,9 @@ def main():
 
     if args.workload == "c5":
         int8_decode_bench(args, torch, pkv, C, workloads)
+        return
+    if args.workload == "prefix":
+        prefix_decode_bench(args, torch, pkv, C, workloads)
         return
 
     dev = torch.device("cuda:0")
@@ -516,6 +520,149 @@ def int8_decode_bench(args, torch, pkv, C, workloads):
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
                      "bytes_per_launch": int(kernel_bytes)},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
+def prefix_decode_bench(args, torch, pkv, C, workloads):
+    """Shared-prefix decode step (the copy-on-write config's shape): one
+    sequence prefilled to 2048 tokens and forked 31 times, private suffixes
+    of the config's seeded U[64, 1024] lengths, one appended token each
+    (fused into the decode launch), 32 q / 8 KV heads, d128, over 32 layer
+    pools of seeded fp16 noise. The block state comes from the library's
+    allocator (fork, copy-on-write reserve) in the config's block order. The
+    step is timed twice, without and with the shared-prefix plan (layer 0
+    launched directly with timing events, layers 1.. replayed from a HIP
+    graph); the two outputs are compared."""
+    dev = torch.device("cuda:0")
+    K, W, L = args.steps, args.warmup, args.layers
+    w = workloads.c4_prefix()
+    prefix = next(len(st[2]) for st in w.steps if st[0] == "prefill")
+    suffix = [len(st[2]) for st in w.steps if st[0] == "prefill"][1:]
+    nseq = len(suffix)
+    cache = pkv.PagedKVCache(L, w.num_blocks, HKV, D, "f16", w.free_order, dev)
+    lib = C.load()
+    sp = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    cache.pool.view(torch.float16).normal_(generator=gen)
+    root = cache.create_seq()
+    cache.reserve([root], [prefix])
+    seqs = [root] + [cache.fork(root) for _ in range(nseq - 1)]
+    cache.reserve(seqs, suffix)
+    _, cow = cache.reserve(seqs, [1] * nseq)  # the decode step's token: its slot now, written in the launch
+    cache.copy_blocks(cow)
+    tables_h, lens_h = cache.block_tables(seqs)
+    max_blocks = tables_h.shape[1]
+    ctx = int(lens_h.max())
+    plan = cache.plan_shared_prefix(seqs)
+    tables_d = torch.from_numpy(tables_h).to(dev)
+    lens_d = torch.from_numpy(lens_h).to(dev)
+    q = torch.empty((L, nseq, HQ, D), dtype=torch.float16, device=dev).normal_(generator=gen)
+    kv_new = torch.empty((2, L, nseq, HKV, D), dtype=torch.float16, device=dev).normal_(generator=gen)
+
+    def build(use_plan):
+        out = torch.empty_like(q)
+        if use_plan:
+            nb = C.pkv_prefix_decode_workspace_bytes(cache.cfg, nseq, HQ, ctx, max_blocks, args.partition_tokens,
+                                                     plan.n_groups)
+        else:
+            nb = C.pkv_decode_workspace_bytes(cache.cfg, nseq, HQ, ctx, args.partition_tokens)
+        ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        argv = []
+        for layer in range(L):
+            a = C.pkv_decode_args()
+            a.cfg = ctypes.pointer(cache.cfg)
+            a.pool_dev = cache.pool.data_ptr()
+            a.layer = layer
+            a.q_dev = q[layer].data_ptr()
+            a.num_seqs = nseq
+            a.num_q_heads = HQ
+            a.block_tables_dev = tables_d.data_ptr()
+            a.max_blocks = max_blocks
+            a.ctx_lens_dev = lens_d.data_ptr()
+            a.ctx_lens_host = C._i32p(lens_h)
+            a.max_context = ctx
+            a.out_dev = out[layer].data_ptr()
+            a.scale = 1.0 / math.sqrt(D)
+            a.workspace_dev = ws.data_ptr()
+            a.workspace_bytes = ws.numel()
+            a.partition_tokens = args.partition_tokens
+            a.k_new_dev = kv_new[0, layer].data_ptr()
+            a.v_new_dev = kv_new[1, layer].data_ptr()
+            if use_plan:
+                a.prefix_plan_dev = plan.dev.data_ptr()
+                a.prefix_plan_host = C._i32p(plan.host)
+                a.prefix_groups = plan.n_groups
+            argv.append(a)
+        return out, ws, argv
+
+    def run(use_plan):
+        out, ws, argv = build(use_plan)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        for group in ev:
+            for e in group:
+                e.record()
+        ptrs = [ctypes.cast((ctypes.c_void_p * 4)(*[e.cuda_event for e in g]), ctypes.POINTER(ctypes.c_void_p))
+                for g in ev]
+
+        def launch(layer, events=None, stream_handle=None):
+            a = argv[layer]
+            a.timing_events = events
+            C._check(lib.pkv_paged_decode(ctypes.byref(a), sp if stream_handle is None else stream_handle))
+
+        for _ in range(W):
+            for layer in range(L):
+                launch(layer)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cs = torch.cuda.current_stream().cuda_stream
+            for layer in range(1, L):
+                launch(layer, stream_handle=cs)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(K):
+            launch(0, ptrs[i])
+            graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / K
+        split = float(np.mean([g[0].elapsed_time(g[1]) for g in ev])) * 1e3
+        merge = float(np.mean([g[2].elapsed_time(g[3]) for g in ev])) * 1e3
+        return ms, split, merge, out
+
+    ms0, split0, merge0, out0 = run(False)
+    ms1, split1, merge1, out1 = run(True)
+    diff = float((out0.float() - out1.float()).abs().max())
+    kv_tok = 2 * HKV * D * 2
+    groups = plan.groups()
+    shared = sum(nb * 16 * (len(mem) - 1) for nb, mem in groups)  # tokens read once instead of per member
+    logical = int(lens_h.sum())
+    unique_bytes = (logical - shared) * kv_tok + nseq * HQ * D * 2 * 2 + tables_h.size * 4
+    achieved = unique_bytes / (split1 * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "shared-prefix decode step tokens/s (32 sequences over one 2048-token prefix)",
+        "value": round(nseq / (ms1 * 1e-3), 1), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms1, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"decode step with fused append, {nseq} sequences forked from one "
+                               f"{prefix}-token prefix, private suffixes U[64, 1024] + 1, 32 q / 8 KV heads, "
+                               f"head_dim 128, fp16, {L} layer pools", "layers": L,
+                   "partition_tokens": args.partition_tokens or "auto", "plan_groups": plan.n_groups,
+                   "shared_blocks": [nb for nb, _ in groups]},
+        "with_plan": {"ms_per_step": round(ms1, 4), "decode_kernel_us": round(split1, 2),
+                      "merge_kernel_us": round(merge1, 2)},
+        "without_plan": {"ms_per_step": round(ms0, 4), "decode_kernel_us": round(split0, 2),
+                         "merge_kernel_us": round(merge0, 2), "tok_s": round(nseq / (ms0 * 1e-3), 1)},
+        "speedup": round(ms0 / ms1, 3),
+        "max_abs_diff_plan_vs_no_plan": diff,
+        "logical_kv_bytes": logical * kv_tok, "unique_kv_bytes": (logical - shared) * kv_tok,
+        "roofline": {"bound": "hbm", "kernel": "paged_decode_kernel<128,4,f16> with shared-prefix work-groups",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(unique_bytes)},
         "cpu_baseline": None,
     }), flush=True)
 

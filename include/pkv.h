@@ -126,6 +126,36 @@ int pkv_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
 int pkv_build_block_tables(const pkv_pool* pool, const int64_t* seqs, int32_t B, int32_t max_blocks,
                            int32_t* tables_host, int32_t* ctx_lens_host);
 
+/* ---- shared-prefix plan (host) ([p1] §三: requests with a common prefix
+ * point at the same physical blocks) -------------------------------------- */
+
+#define PKV_MAX_SHARERS 32         /* sequences per shared-prefix group        */
+#define PKV_PREFIX_GROUP_INTS 34   /* ints per group: blocks, members, ids[32]  */
+
+/* Ints a plan for B sequences may need: 2 B + (B / 2) * PKV_PREFIX_GROUP_INTS. */
+int32_t pkv_plan_ints(int32_t B);
+
+/* Group the B sequences (batch order) whose block tables begin with the same
+ * physical blocks, so one decode reads those blocks once for all of them.
+ * Sequences are keyed by their first block; each key's sequences form groups
+ * of up to max_members (1..PKV_MAX_SHARERS) in batch order. A group's shared
+ * run is the longest run of leading blocks identical in all its members,
+ * ending before the block holding each member's last token (so every member
+ * keeps a private suffix, and an appended token is never in a shared block);
+ * groups of fewer than 2 members or fewer than min_blocks (>= 1) shared
+ * blocks are dropped.
+ * plan_host (int32, plan_cap >= pkv_plan_ints(B)) receives:
+ *   [0, 2B)      per sequence b: [2b] = its shared blocks (0 if ungrouped),
+ *                [2b + 1] = group * 64 + member, or -1
+ *   then per group g, PKV_PREFIX_GROUP_INTS ints at 2B + g * 34:
+ *                [shared blocks, member count, batch index of each member
+ *                 (-1 padded)]
+ * *n_groups receives the group count. The plan holds batch indices: it is
+ * valid for this `seqs` order and these tables. INVALID_ARG on bad sizes,
+ * UNKNOWN_SEQ for an unknown id. */
+int pkv_plan_shared_prefix(const pkv_pool* pool, const int64_t* seqs, int32_t B, int32_t min_blocks,
+                           int32_t max_members, int32_t* plan_host, int32_t plan_cap, int32_t* n_groups);
+
 /* ---- device operations (asynchronous on `stream`) ------------------------ */
 
 /* Copy-on-write block copy ([p1] §三): for each of the n (src, dst) pairs in
@@ -184,6 +214,14 @@ typedef struct pkv_decode_args {
                                      attended like every other token. Same bytes
                                      as pkv_append_kv. fp16 pools only.          */
   const void* v_new_dev;
+  const int32_t* prefix_plan_dev; /* optional shared-prefix plan (NULL = none):
+                                     pkv_plan_shared_prefix's output for these
+                                     sequences in this order, uploaded. Each
+                                     group's shared blocks are read once for all
+                                     its members (fp16 pools). Same result up to
+                                     rounding.                                   */
+  const int32_t* prefix_plan_host;/* optional host copy, validated if non-NULL    */
+  int32_t prefix_groups;          /* groups in the plan (0 = no plan)             */
   void* const* timing_events;     /* optional (NULL = none): 4 hipEvent_t recorded
                                      around the split kernel ([0] start, [1] stop)
                                      and the merge kernel ([2], [3]; untouched if
@@ -216,6 +254,20 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * contents after the call unspecified). Calls sharing one workspace must be
  * ordered on one stream.
  *
+ * With a shared-prefix plan (prefix_plan_dev, prefix_groups > 0; fp16
+ * pools), extra work-groups of the same launch attend every group's members
+ * to the group's shared blocks, reading each K/V tile once for up to 128
+ * query rows on the matrix cores; the split work-groups cover each grouped
+ * sequence from its first unshared block, and the merge combines prefix and
+ * suffix partials in logical order. The workspace must hold
+ * pkv_prefix_decode_workspace_bytes() bytes. Members x (Hq/Hkv) must not
+ * exceed 128; a plan with prefix_groups > 0 on an int8 pool is UNSUPPORTED;
+ * INVALID_ARG for an inconsistent plan when the host copy is given (without
+ * it the plan is trusted: a wrong plan gives wrong results, never an
+ * out-of-bounds access). With both host copies (lengths and plan) and
+ * automatic partitions, split-K partitions are sized for the longest
+ * unshared stretch instead of max_context.
+ *
  * With k_new_dev/v_new_dev set, the call also performs the append step of
  * [p2] §2.2 for every sequence (one token each) before attending: the
  * decode step of the pages in one launch. pool_dev is then written.
@@ -225,6 +277,17 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * partition_tokens not a multiple of 16, only one of k_new/v_new given.
  * UNSUPPORTED: head_dim/group size not built, fused append on int8. */
 int pkv_paged_decode(const pkv_decode_args* args, void* stream);
+
+/* Workspace bytes pkv_paged_decode needs with a shared-prefix plan of
+ * n_groups groups: the whole workspace, in place of
+ * pkv_decode_workspace_bytes() (equal to it when n_groups == 0). Layout:
+ * fp32 partial rows m [B][Hq][P], l [B][Hq][P], o [B][Hq][P][D] whose P
+ * slots hold a grouped sequence's prefix partials (one per prefix partition
+ * of at most 64 shared blocks) followed by its split-K partials. Returns < 0
+ * (a status) on bad arguments. */
+int64_t pkv_prefix_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t max_context, int32_t max_blocks, int32_t partition_tokens,
+                                          int32_t n_groups);
 
 /* Upload host metadata for the next step (block tables, lengths: the
  * per-step upload of [p2] §3.3's batch that changes every step) from pinned

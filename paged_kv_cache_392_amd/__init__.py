@@ -10,11 +10,11 @@ the library and fails loudly if it is not built.
 
 from . import _capi
 from ._capi import (  # noqa: F401  (re-exported C names)
-    BLOCK_TOKENS, PKV_F16, PKV_I8, PkvError, NoBlocksError, make_config,
+    BLOCK_TOKENS, PKV_F16, PKV_I8, PKV_MAX_SHARERS, PKV_PREFIX_GROUP_INTS, PkvError, NoBlocksError, make_config,
     pkv_pool_bytes, pkv_pool_create, pkv_pool_destroy, pkv_seq_create, pkv_seq_free,
     pkv_seq_fork, pkv_seq_reserve, pkv_seq_len, pkv_seq_block_table, pkv_block_refcount,
-    pkv_num_free, pkv_free_list, pkv_build_block_tables, pkv_copy_blocks, pkv_append_kv,
-    pkv_decode_workspace_bytes, pkv_paged_decode, pkv_upload, pkv_probe_stream_read, pkv_strerror,
+    pkv_num_free, pkv_free_list, pkv_build_block_tables, pkv_plan_ints, pkv_plan_shared_prefix,
+    pkv_copy_blocks, pkv_append_kv, pkv_decode_workspace_bytes, pkv_prefix_decode_workspace_bytes, pkv_paged_decode, pkv_upload, pkv_probe_stream_read, pkv_strerror,
     pkv_last_error,
 )
 from .cache import PagedKVCache, paged_decode  # noqa: F401

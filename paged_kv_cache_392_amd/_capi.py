@@ -31,6 +31,8 @@ PKV_ERR_HIP = -6
 PKV_F16 = 0
 PKV_I8 = 1
 BLOCK_TOKENS = 16
+PKV_MAX_SHARERS = 32
+PKV_PREFIX_GROUP_INTS = 34
 
 _c_i32 = ctypes.c_int32
 _c_i64 = ctypes.c_int64
@@ -51,6 +53,7 @@ class pkv_decode_args(ctypes.Structure):
                 ("ctx_lens_host", _p_i32), ("max_context", _c_i32), ("out_dev", _vp),
                 ("scale", ctypes.c_float), ("workspace_dev", _vp), ("workspace_bytes", _c_i64),
                 ("partition_tokens", _c_i32), ("k_new_dev", _vp), ("v_new_dev", _vp),
+                ("prefix_plan_dev", _vp), ("prefix_plan_host", _p_i32), ("prefix_groups", _c_i32),
                 ("timing_events", ctypes.POINTER(_vp))]
 
 
@@ -78,9 +81,13 @@ _SIGS = {
     "pkv_num_free": (ctypes.c_int, [_vp, _p_i32]),
     "pkv_free_list": (ctypes.c_int, [_vp, _p_i32, _c_i32, _p_i32]),
     "pkv_build_block_tables": (ctypes.c_int, [_vp, _p_i64, _c_i32, _c_i32, _p_i32, _p_i32]),
+    "pkv_plan_ints": (_c_i32, [_c_i32]),
+    "pkv_plan_shared_prefix": (ctypes.c_int, [_vp, _p_i64, _c_i32, _c_i32, _c_i32, _p_i32, _c_i32, _p_i32]),
     "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(pkv_config), _vp, _vp, _c_i32, _vp]),
     "pkv_append_kv": (ctypes.c_int, [ctypes.POINTER(pkv_config), _vp, _c_i32, _vp, _vp, _vp, _c_i32, _vp]),
     "pkv_decode_workspace_bytes": (_c_i64, [ctypes.POINTER(pkv_config), _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_prefix_decode_workspace_bytes": (_c_i64, [ctypes.POINTER(pkv_config), _c_i32, _c_i32, _c_i32, _c_i32,
+                                                   _c_i32, _c_i32]),
     "pkv_paged_decode": (ctypes.c_int, [ctypes.POINTER(pkv_decode_args), _vp]),
     "pkv_upload": (ctypes.c_int, [_vp, _vp, _c_i64, _vp]),
     "pkv_probe_stream_read": (ctypes.c_int, [_vp, _c_i64, _vp, _vp]),
@@ -238,6 +245,20 @@ def pkv_build_block_tables(pool, seqs, max_blocks):
     return tables[:, :max_blocks], lens[:len(s)]
 
 
+def pkv_plan_ints(B):
+    return int(load().pkv_plan_ints(B))
+
+
+def pkv_plan_shared_prefix(pool, seqs, min_blocks=1, max_members=PKV_MAX_SHARERS):
+    """Returns ``(plan int32[pkv_plan_ints(B)], n_groups)``."""
+    s = np.ascontiguousarray(seqs, np.int64)
+    plan = np.full(max(pkv_plan_ints(len(s)), 1), -1, np.int32)
+    ng = _c_i32(0)
+    _check(load().pkv_plan_shared_prefix(pool, s.ctypes.data_as(_p_i64), len(s), min_blocks, max_members,
+                                         _i32p(plan), len(plan), ctypes.byref(ng)))
+    return plan[:pkv_plan_ints(len(s))], ng.value
+
+
 # ---- device calls -------------------------------------------------------------
 
 def pkv_copy_blocks(cfg, pool_dev, pairs_dev, n, stream):
@@ -251,6 +272,15 @@ def pkv_append_kv(cfg, pool_dev, layer, k_dev, v_dev, slots_dev, n_tokens, strea
 def pkv_decode_workspace_bytes(cfg, num_seqs, num_q_heads, max_context, partition_tokens=0):
     n = load().pkv_decode_workspace_bytes(ctypes.byref(cfg), num_seqs, num_q_heads, max_context,
                                           partition_tokens)
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def pkv_prefix_decode_workspace_bytes(cfg, num_seqs, num_q_heads, max_context, max_blocks, partition_tokens=0,
+                                      n_groups=0):
+    n = load().pkv_prefix_decode_workspace_bytes(ctypes.byref(cfg), num_seqs, num_q_heads, max_context,
+                                                 max_blocks, partition_tokens, n_groups)
     if n < 0:
         _check(int(n))
     return int(n)

@@ -22,6 +22,31 @@ import torch
 from . import _capi as C
 
 
+class PrefixPlan:
+    """A shared-prefix plan for one batch of ``num_seqs`` sequences
+    (``pkv_plan_shared_prefix``): the host ints, the group count, and the
+    same ints on the device."""
+
+    def __init__(self, host, n_groups, num_seqs, device):
+        self.host = np.ascontiguousarray(host, np.int32)
+        self.n_groups = int(n_groups)
+        self.num_seqs = int(num_seqs)
+        self.dev = _dev_i32(self.host, device)
+
+    def shared_blocks(self):
+        """Shared blocks per sequence (0 for an ungrouped one)."""
+        return self.host[:2 * self.num_seqs:2]
+
+    def groups(self):
+        """``[(shared_blocks, [batch indices])]`` per group."""
+        base, w = 2 * self.num_seqs, C.PKV_PREFIX_GROUP_INTS
+        out = []
+        for g in range(self.n_groups):
+            gd = self.host[base + g * w:base + (g + 1) * w]
+            out.append((int(gd[0]), [int(x) for x in gd[2:2 + gd[1]]]))
+        return out
+
+
 def _stream():
     return torch.cuda.current_stream().cuda_stream
 
@@ -201,22 +226,32 @@ class PagedKVCache:
             max_blocks = max(len(self.block_table(s)) for s in seqs)
         return C.pkv_build_block_tables(self.handle, seqs, max_blocks)
 
+    def plan_shared_prefix(self, seqs, min_blocks=1, max_members=C.PKV_MAX_SHARERS):
+        """Group the batch's sequences that share leading blocks so one decode
+        reads those blocks once for all of them (the plan is tied to this
+        order of ``seqs`` and to the current block tables)."""
+        host, ng = C.pkv_plan_shared_prefix(self.handle, seqs, min_blocks, max_members)
+        return PrefixPlan(host, ng, len(seqs), self.device)
+
     def paged_decode(self, q, block_tables, context_lens, layer=0, out=None, scale=None,
                      context_lens_host=None, max_context=None, workspace=None, partition_tokens=0,
-                     k_new=None, v_new=None):
+                     k_new=None, v_new=None, prefix_plan=None):
         """``out[b, h] = softmax(q[b, h] K_b^T * scale) V_b`` over the
         ``context_lens[b]`` tokens of each sequence, read in place through
         ``block_tables`` (device int32 ``[B, max_blocks]``). With ``k_new,
         v_new`` (fp16 ``[B, Hkv, D]``) the kernel first stores them as the
         last token of each sequence (the slot already reserved), so append
-        and attention run in one launch."""
+        and attention run in one launch. With ``prefix_plan`` (from
+        :meth:`plan_shared_prefix` for these sequences in this order) each
+        group's shared blocks are read once for all its members."""
         return paged_decode(self, q, block_tables, context_lens, layer, out, scale,
-                            context_lens_host, max_context, workspace, partition_tokens, k_new, v_new)
+                            context_lens_host, max_context, workspace, partition_tokens, k_new, v_new,
+                            prefix_plan)
 
 
 def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=None,
                  context_lens_host=None, max_context=None, workspace=None, partition_tokens=0,
-                 k_new=None, v_new=None):
+                 k_new=None, v_new=None, prefix_plan=None):
     if q.dtype != torch.float16 or q.dim() != 3:
         raise TypeError("q must be float16 [B, Hq, D]")
     q = q.contiguous()
@@ -235,7 +270,12 @@ def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
-    ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, Hq, max_context, partition_tokens)
+    n_groups = prefix_plan.n_groups if prefix_plan is not None else 0
+    if n_groups:
+        ws_bytes = C.pkv_prefix_decode_workspace_bytes(cache.cfg, B, Hq, max_context, max_blocks,
+                                                       partition_tokens, n_groups)
+    else:
+        ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, Hq, max_context, partition_tokens)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = cache.decode_workspace(ws_bytes)
     args = C.pkv_decode_args()
@@ -265,5 +305,11 @@ def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=
             raise ValueError(f"k_new, v_new must be float16 {list(shape)}")
         args.k_new_dev = k_new.data_ptr()
         args.v_new_dev = v_new.data_ptr()
+    if n_groups:
+        if prefix_plan.num_seqs != B:
+            raise ValueError("the plan was made for another batch size")
+        args.prefix_plan_dev = prefix_plan.dev.data_ptr()
+        args.prefix_plan_host = prefix_plan.host.ctypes.data_as(C._p_i32)
+        args.prefix_groups = n_groups
     C.pkv_paged_decode(args, _stream())
     return out

@@ -247,6 +247,11 @@ struct DecodeParams {
   float* part_l;
   float* part_o;  // [B][Hq][max_parts][D]
   _Float16* out;  // [B][Hq][D]
+  const int32_t* plan;  // shared-prefix plan (null = none): per sequence (shared blocks, group*64+member),
+                        // then PKV_PREFIX_GROUP_INTS per group
+  int prefix_z;         // grid z-planes of shared-prefix work-groups (0 = none)
+  int prefix_pp;        // prefix partitions per group
+  int num_groups;
   int max_blocks;
   int num_blocks;
   int Hkv;
@@ -302,7 +307,249 @@ __device__ __forceinline__ float read_lane(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
-// One work-group (4 wave64s) per (partition p, KV head g, sequence b).
+// ---------------------------------------------------------------------------
+// shared-prefix attention
+
+// Query rows a shared-prefix work-group attends per KV head: group members x
+// (Hq / Hkv), at most 128 (eight 16-row MFMA blocks over four waves).
+constexpr int PREFIX_ROWS = 128;
+
+// A group's np shared blocks are cut into at most pp partitions of
+// ceil(np / pp) blocks; prefix_parts of them are non-empty.
+__device__ __forceinline__ int prefix_blocks_per_part(int np, int pp) { return (np + pp - 1) / pp; }
+__device__ __forceinline__ int prefix_parts(int np, int pp) {
+  if (np <= 0 || pp <= 0) return 0;
+  const int pbp = prefix_blocks_per_part(np, pp);
+  return (np + pbp - 1) / pbp;
+}
+
+// Shared blocks of sequence b and how many prefix partials lead its partial
+// row (0 and 0 when it is in no group). The split kernel and the merge use
+// this one rule.
+__device__ __forceinline__ void seq_prefix(const int32_t* plan, int b, int max_blocks, int num_groups, int pp,
+                                           int& sb, int& pre) {
+  sb = 0;
+  pre = 0;
+  if (!plan) return;
+  sb = min(max(plan[2 * b], 0), max_blocks);
+  const int gm = plan[2 * b + 1];
+  if (gm >= 0 && (gm >> 6) < num_groups && sb > 0) pre = prefix_parts(sb, pp);
+}
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+
+// The shared-prefix role of a decode work-group (4 waves): KV head g,
+// partition `part` of group grp's shared blocks. The group's members share
+// their leading blocks ([p1] §三): each K/V tile of the run is read once here
+// and attended by all R = members x G query rows, in 16-row blocks (wave w
+// takes blocks w and w + 4).
+//
+// Per tile and row block, on the matrix cores:
+//   S^T (16 tokens x 16 rows) = K (16 x D) . Q^T (D x 16),
+//       v_mfma_f32_16x16x32_f16 over D/32 chunks: lane (n, j) receives
+//       tokens 4j..4j+3 of query row n;
+//   O^T (D x 16 rows) += V^T (D x 16 tokens) . P^T (16 tokens x 16 rows),
+//       v_mfma_f32_16x16x16_f16 per 16 dims, whose B operand (tokens
+//       4j..4j+3 of row n in lane (n, j)) is exactly the layout the scores
+//       arrive in: the probabilities go from one MFMA to the next without
+//       moving between lanes.
+// K tiles are staged in LDS row-major (rows padded by 16 bytes), V tiles
+// transposed ([dim][token]) so each lane reads its 4 tokens of one dim as 8
+// contiguous bytes. Online softmax per row in base 2 with the lazy running
+// max of the split role. Shared blocks are full, so nothing is masked. Each
+// row ends as one (m, l, o[D]) partial, written into slot `part` of the
+// member's own partial row, ahead of its split-K partials.
+template <int D, int G>
+__device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int grp, int part) {
+  constexpr int NCH = D / 32;           // score MFMA chunks
+  constexpr int NDB = D / 16;           // value MFMA dim blocks
+  constexpr int KROW = D * 2 + 16;      // bytes per staged K row
+  constexpr int VTROW = BT * 2 + 8;     // bytes per staged V^T row (16 tokens)
+  constexpr int PIECES = D / 8;         // 16-byte pieces per K/V row
+  constexpr int LOADERS = BT * PIECES;  // pieces per K (or V) tile
+  constexpr int TILE = BT * D * 2;
+  constexpr int PF = 4;                 // tiles in flight per thread
+  static_assert(PF % 2 == 0, "LDS stages alternate with the ring slot");
+  __shared__ __align__(16) char kst[2][BT * KROW];
+  __shared__ __align__(16) char vst[2][D * VTROW];
+  __shared__ int blk_ids[64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lj = lane >> 4;
+  const int B = gridDim.y, Hq = prm.Hkv * G;
+  const int32_t* gd = prm.plan + 2 * int64_t(B) + int64_t(grp) * PKV_PREFIX_GROUP_INTS;
+  const int np = min(gd[0], prm.max_blocks);
+  const int members = min(gd[1], PKV_MAX_SHARERS);
+  const int R = min(members * G, PREFIX_ROWS);
+  const int b0 = gd[2];
+  if (np <= 0 || R <= 0 || unsigned(b0) >= unsigned(B)) return;
+  const int pbp = prefix_blocks_per_part(np, prm.prefix_pp);  // <= 64: the host sizes prefix_pp
+  const int jb = part * pbp, je = min(np, jb + pbp);
+  if (jb >= je) return;
+  const int nt = je - jb;
+  if (tid < nt) blk_ids[tid] = prm.tables[int64_t(b0) * prm.max_blocks + jb + tid];
+
+  // q^T as the B operand of the score MFMA, per row block of this wave
+  const int rb0 = wave, rb1 = wave + 4;
+  const bool has0 = rb0 * 16 < R, has1 = rb1 * 16 < R;
+  auto member_of = [&](int r) { return r < R ? gd[2 + r / G] : -1; };
+  auto load_q = [&](int rb, half8_t (&qb)[NCH]) {
+    const int r = rb * 16 + ln;
+    const int bb = member_of(r);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      if (unsigned(bb) < unsigned(B)) {
+        qb[c] = *reinterpret_cast<const half8_t*>(prm.q + (int64_t(bb) * Hq + g * G + r % G) * D + 32 * c + 8 * lj);
+      } else {
+        qb[c] = half8_t{};
+      }
+    }
+  };
+  half8_t q0[NCH], q1[NCH];
+  if (has0) load_q(rb0, q0);
+  if (has1) load_q(rb1, q1);
+
+  float4_t o0[NDB], o1[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    o0[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    o1[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.0f, l1 = 0.0f;
+
+  // Tile staging: a tile is 2 x LOADERS 16-byte pieces (K, then V); thread
+  // t moves pieces t + 256 j. Tiles are fetched PF ahead into a register
+  // ring; the loads are unconditional (indices past the last tile re-read
+  // it) so the compiler counts outstanding loads statically.
+  const char* Kc = static_cast<const char*>(prm.K);
+  const char* Vc = static_cast<const char*>(prm.V);
+  constexpr int NLD = 2 * LOADERS / 256;
+  uint4 ring[PF][NLD];
+  auto gload = [&](int it, uint4 (&r)[NLD]) {
+    const int blk = blk_ids[min(it, nt - 1)];
+    const int safe = unsigned(blk) < unsigned(prm.num_blocks) ? blk : 0;
+    const int64_t base = (int64_t(safe) * prm.Hkv + g) * TILE;
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int q = tid + 256 * j;
+      const int pc = q % LOADERS;
+      r[j] = load_nt((q < LOADERS ? Kc : Vc) + base + pc * 16);
+    }
+  };
+  auto lstore = [&](int st, const uint4 (&r)[NLD]) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int q = tid + 256 * j;
+      const int pc = q % LOADERS, lrow = pc / PIECES, lpc = pc % PIECES;
+      if (q < LOADERS) {
+        *reinterpret_cast<uint4*>(kst[st] + lrow * KROW + lpc * 16) = r[j];
+      } else {
+        const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = lpc * 8 + 2 * i;
+          *reinterpret_cast<uint16_t*>(vst[st] + d * VTROW + lrow * 2) = uint16_t(w[i] & 0xFFFFu);
+          *reinterpret_cast<uint16_t*>(vst[st] + (d + 1) * VTROW + lrow * 2) = uint16_t(w[i] >> 16);
+        }
+      }
+    }
+  };
+
+  auto row_block = [&](int st, const half8_t (&qb)[NCH], float4_t (&o)[NDB], float& m, float& l) {
+    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const half8_t ka = *reinterpret_cast<const half8_t*>(kst[st] + ln * KROW + (32 * c + 8 * lj) * 2);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[c], acc, 0, 0, 0);
+    }
+    float s[4];
+    bool need = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[e] = acc[e] * prm.scale_log2;
+      need |= s[e] > m + LAZY_MAX;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first tile
+      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      mx = fmaxf(mx, xor_shfl(mx, 16));
+      mx = fmaxf(mx, xor_shfl(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.0f : exp2_fast(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+    }
+    // probabilities enter the value MFMA in fp16; the row sum adds the same
+    // rounded values, so weights and normaliser agree
+    half4_t pt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pt[e] = (_Float16)exp2_fast(s[e] - m);
+      l += float(pt[e]);
+    }
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+      const half4_t va = *reinterpret_cast<const half4_t*>(vst[st] + (16 * i + ln) * VTROW + lj * 8);
+      o[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pt, o[i], 0, 0, 0);
+    }
+  };
+
+  __syncthreads();  // block ids
+#pragma unroll
+  for (int u = 0; u < PF; ++u) gload(u, ring[u]);
+  lstore(0, ring[0]);
+  gload(PF, ring[0]);
+  __syncthreads();
+  // Tile it sits in LDS stage it & 1 and its successor in ring slot
+  // (it + 1) % PF. The loop runs whole rounds of PF (unrolled, so every slot
+  // index is a constant); past the last tile only the math is skipped: loads
+  // and stores stay unconditional, and the compiler's count of loads in
+  // flight stays exact across the loop.
+  for (int it0 = 0; it0 < nt; it0 += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int it = it0 + u;
+      const int st = u & 1;  // == it & 1: PF is even
+      if (it < nt) {
+        if (has0) row_block(st, q0, o0, m0, l0);
+        if (has1) row_block(st, q1, o1, m1, l1);
+      }
+      lstore(st ^ 1, ring[(u + 1) % PF]);
+      gload(it + 1 + PF, ring[(u + 1) % PF]);
+      __syncthreads();
+    }
+  }
+
+  // the row sums over the four token groups; one partial per row, in slot
+  // `part` of the member's (sequence, query head) partial row
+  auto finish = [&](int rb, float4_t (&o)[NDB], float m, float l) {
+    l += xor_shfl(l, 16);
+    l += xor_shfl(l, 32);
+    const int r = rb * 16 + ln;
+    const int bb = member_of(r);
+    if (unsigned(bb) >= unsigned(B)) return;
+    const int64_t pi = (int64_t(bb) * Hq + g * G + r % G) * prm.max_parts + part;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) prm.part_o[pi * D + 16 * i + 4 * lj + e] = o[i][e];
+    if (lj == 0) {
+      prm.part_m[pi] = m;
+      prm.part_l[pi] = l;
+    }
+  };
+  if (has0) finish(rb0, o0, m0, l0);
+  if (has1) finish(rb1, o1, m1, l1);
+}
+
+// One work-group (4 wave64s) per (KV head g, sequence b, partition p), in
+// that grid order (x, y, z). Work-groups go to the eight XCDs round-robin by
+// linear id, so the partition index, the dimension along which work runs out
+// first (short sequences, or a shared prefix attended elsewhere), varies
+// slowest: the busy work-groups of any one partition index are spread over
+// all XCDs instead of piling onto those whose id matches a low index.
 //
 // Scores on the matrix cores: per tile, S[r][n] = sum_k Q[r][k] K[n][k] with
 // v_mfma_f32_16x16x32_f16 over D/32 chunks. A-row r holds query head r % G of
@@ -317,7 +564,18 @@ __device__ __forceinline__ float read_lane(float x, int l) {
 template <int D, int G, bool I8>
 __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   using S = Shape<D, G, I8>;
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, b = blockIdx.y;
+  // With a shared-prefix plan the first prefix_z planes of the grid are
+  // shared-prefix work-groups: dispatched first, they run beside the split
+  // work-groups of the same launch.
+  if constexpr (!I8) {
+    if (int(blockIdx.z) < prm.prefix_z) {
+      const int k = blockIdx.y + gridDim.y * blockIdx.z;
+      if (k < prm.prefix_pp * prm.num_groups) prefix_role<D, G>(prm, g, k / prm.prefix_pp, k % prm.prefix_pp);
+      return;
+    }
+  }
+  const int p = blockIdx.z - prm.prefix_z;
   const int Hkv = prm.Hkv, Hq = Hkv * G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -333,7 +591,12 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   // lane it of a VGPR, and each tile reads it with readlane, so the id never
   // waits on the vector memory queue.
   const int32_t* trow = prm.tables + int64_t(b) * prm.max_blocks;
-  const int jb = p * prm.part_blocks;
+  // With a shared-prefix plan, a grouped sequence's leading shared blocks are
+  // attended by the shared-prefix work-groups: partitions start after them,
+  // and their partials follow the `pre` prefix partials in the partial row.
+  int sb, pre;
+  seq_prefix(prm.plan, b, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
+  const int jb = sb + p * prm.part_blocks;
   const int first = jb + wave;
   const int jl = first + WAVES * lane;
   const int blk_raw = jl < prm.max_blocks ? trow[jl] : -1;
@@ -351,7 +614,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
     return;
   }
   const int nblk = (ctx + BT - 1) / BT;
-  const int nparts = (nblk + prm.part_blocks - 1) / prm.part_blocks;
+  const int nparts = nblk > sb ? (nblk - sb + prm.part_blocks - 1) / prm.part_blocks : 0;
   if (p >= nparts) return;
   const int je = min(nblk, jb + prm.part_blocks);
   const int n_my = first < je ? (je - first + WAVES - 1) / WAVES : 0;  // <= 64
@@ -695,10 +958,10 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
       O += merge_o[w][h][d] * wt;
     }
     const int64_t row = int64_t(b) * Hq + g * G + h;
-    if (nparts == 1) {
+    if (nparts == 1 && pre == 0) {
       prm.out[row * D + d] = (_Float16)(L > 0.0f ? O / L : 0.0f);
     } else {
-      const int64_t pi = row * prm.max_parts + p;
+      const int64_t pi = row * prm.max_parts + pre + p;
       prm.part_o[pi * D + d] = O;
       if (d == 0) {
         prm.part_m[pi] = M;
@@ -708,56 +971,66 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
   }
 }
 
-// Merge the partitions of one (sequence, query head) by log-sum-exp:
+struct MergeParams {
+  const float* part_m;  // partials [B][Hq][max_parts] (+ [D]): prefix, then split-K
+  const float* part_l;
+  const float* part_o;
+  const int32_t* ctx_lens;
+  const int32_t* plan;  // null = no shared-prefix plan
+  _Float16* out;
+  int D, max_blocks, max_context, part_blocks, max_parts;
+  int num_groups, prefix_pp;
+};
+
+// Merge the partials of one (sequence, query head) by log-sum-exp:
 // M = max_p m_p, out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), in
-// partition order. One thread per output dim. The partials are read 16
-// partitions at a time, all loads of a group in flight together; across
-// groups the running max is raised as in the split kernel (a sequence of up
-// to 16 partitions is one group, exactly the two-pass formula above).
-// Sequences with a single partition were finished by the split kernel.
-__global__ __launch_bounds__(128) void lse_reduce_kernel(const float* __restrict__ part_m,
-                                                         const float* __restrict__ part_l,
-                                                         const float* __restrict__ part_o,
-                                                         const int32_t* __restrict__ ctx_lens,
-                                                         _Float16* __restrict__ out, int max_blocks,
-                                                         int max_context, int part_blocks, int max_parts,
-                                                         int D) {
+// logical order: the shared-prefix partials of the sequence's group (if it
+// has one), then its own split-K partitions, which follow them in the
+// sequence's partial row. One thread per output dim. Partials are read 16
+// at a time, all loads of a group in flight together (the first 16 with the
+// context length and the plan); across groups the running max is raised as
+// in the split kernel (up to 16 partials in all, this is exactly the
+// two-pass formula above). Sequences with a single partial were finished by
+// the split kernel.
+__global__ __launch_bounds__(128) void lse_reduce_kernel(MergeParams prm) {
   constexpr int CH = 16;
   const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
   const int d = threadIdx.x;
+  const int D = prm.D;
   if (d >= D) return;
-  const int64_t base = (int64_t(b) * Hq + h) * max_parts;
-  // The first group is loaded together with the context length (one memory
-  // round trip for up to 16 partitions); slots past the sequence's partition
-  // count hold stale data and are replaced by neutral values below.
+  const int64_t base = (int64_t(b) * Hq + h) * prm.max_parts;
   float m0[CH], l0[CH], o0[CH];
 #pragma unroll
   for (int u = 0; u < CH; ++u) {
-    const int64_t pi = base + (u < max_parts ? u : 0);
-    m0[u] = part_m[pi];
-    l0[u] = part_l[pi];
-    o0[u] = part_o[pi * D + d];
+    const int64_t pi = base + (u < prm.max_parts ? u : 0);
+    m0[u] = prm.part_m[pi];
+    l0[u] = prm.part_l[pi];
+    o0[u] = prm.part_o[pi * D + d];
   }
-  const int ctx = clamp_ctx(ctx_lens[b], max_blocks, max_context);
+  int sb, pre;
+  seq_prefix(prm.plan, b, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
+  const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
   if (ctx <= 0) return;
   const int nblk = (ctx + BT - 1) / BT;
-  const int nparts = (nblk + part_blocks - 1) / part_blocks;
-  if (nparts <= 1) return;
+  const int nparts = nblk > sb ? (nblk - sb + prm.part_blocks - 1) / prm.part_blocks : 0;
+  if (pre == 0 && nparts <= 1) return;
+  const int count = min(pre + nparts, prm.max_parts);
+
   float M = -INFINITY, L = 0.0f, O = 0.0f;
-  for (int p0 = 0; p0 < nparts; p0 += CH) {
+  for (int p0 = 0; p0 < count; p0 += CH) {
     float mv[CH], lv[CH], ov[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const bool ok = p0 + u < nparts;
+      const bool ok = p0 + u < count;
       if (p0 == 0) {
         mv[u] = ok ? m0[u] : -INFINITY;
         lv[u] = ok ? l0[u] : 0.0f;
         ov[u] = ok ? o0[u] : 0.0f;
       } else {
         const int64_t pi = base + (ok ? p0 + u : 0);
-        mv[u] = ok ? part_m[pi] : -INFINITY;
-        lv[u] = ok ? part_l[pi] : 0.0f;
-        ov[u] = ok ? part_o[pi * D + d] : 0.0f;
+        mv[u] = ok ? prm.part_m[pi] : -INFINITY;
+        lv[u] = ok ? prm.part_l[pi] : 0.0f;
+        ov[u] = ok ? prm.part_o[pi * D + d] : 0.0f;
       }
     }
     float cm = M;
@@ -776,7 +1049,7 @@ __global__ __launch_bounds__(128) void lse_reduce_kernel(const float* __restrict
       O += ov[u] * wt;
     }
   }
-  out[(int64_t(b) * Hq + h) * D + d] = (_Float16)(L > 0.0f ? O / L : 0.0f);
+  prm.out[(int64_t(b) * Hq + h) * D + d] = (_Float16)(L > 0.0f ? O / L : 0.0f);
 }
 
 // Host -> device staging of small host metadata (block tables, lengths): one
@@ -873,6 +1146,46 @@ decode_fn pick_kernel(int D, int G, bool i8) {
 int64_t workspace_bytes_for(const pkv_config& c, int B, int Hq, int max_parts) {
   if (max_parts <= 1) return 0;
   return int64_t(B) * Hq * max_parts * (c.head_dim + 2) * int64_t(sizeof(float));
+}
+
+// Prefix partitions per group. A partition adds 128 partial rows of D + 2
+// floats (66.5 KB at D = 128) against 8 KB of K/V per shared block, and its
+// work-group walks its blocks one tile after another, so partitions are
+// neither short (partial traffic) nor long (the chain outlasts the split
+// work-groups beside it): about 128 shared-prefix work-groups over groups
+// and KV heads, 16 to 64 blocks each (measured on MI355X: 32 sequences over
+// a 2048-token prefix run best at 96 work-groups of 11 blocks, 64 over two
+// 4096-token prefixes at 160 of 26).
+constexpr int PREFIX_TARGET_WGS = 128;
+int prefix_partitions(int Hkv, int n_groups, int max_blocks) {
+  const int64_t lo = (int64_t(max_blocks) + 63) / 64;  // <= 64 blocks: the block ids staged in LDS
+  const int64_t hi = std::max<int64_t>(lo, (max_blocks + 15) / 16);
+  const int64_t want = (PREFIX_TARGET_WGS + int64_t(Hkv) * n_groups - 1) / (int64_t(Hkv) * n_groups);
+  return int(std::min(hi, std::max(lo, want)));
+}
+
+// Workspace of one decode: partial rows m [B][Hq][P], l [B][Hq][P],
+// o [B][Hq][P][D] (fp32). Without a plan P is the split-K partition count
+// (no workspace when it is 1). With a shared-prefix plan every row also
+// holds up to prefix_pp prefix partials ahead of the split-K ones, and the
+// grid gains prefix_z planes of shared-prefix work-groups (one per group,
+// prefix partition and KV head).
+struct WsLayout {
+  int part_blocks, grid_parts, max_parts, prefix_pp, prefix_z;
+  int64_t bytes;
+};
+
+WsLayout ws_layout(const pkv_config& c, int B, int Hq, int max_context, int max_blocks, int partition_tokens,
+                   int n_groups) {
+  WsLayout w;
+  w.part_blocks = choose_part_blocks(c, B, max_context, partition_tokens);
+  w.grid_parts = max_parts_for(max_context, w.part_blocks);
+  w.prefix_pp = n_groups > 0 ? prefix_partitions(c.num_kv_heads, n_groups, max_blocks) : 0;
+  w.prefix_z = n_groups > 0 ? int((int64_t(w.prefix_pp) * n_groups + B - 1) / B) : 0;
+  w.max_parts = w.grid_parts + w.prefix_pp;
+  w.bytes = n_groups > 0 ? int64_t(B) * Hq * w.max_parts * (c.head_dim + 2) * int64_t(sizeof(float))
+                         : workspace_bytes_for(c, B, Hq, w.max_parts);
+  return w;
 }
 
 int check_partition_tokens(int partition_tokens) {
@@ -992,13 +1305,54 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
         return pkv::fail(PKV_ERR_INVALID_ARG, "context_len[%d] = %d outside [1, %lld]", b, n, (long long)cap);
     }
   }
-  const int pb = choose_part_blocks(c, a->num_seqs, a->max_context, a->partition_tokens);
-  const int mp = max_parts_for(a->max_context, pb);
-  const int64_t need = workspace_bytes_for(c, a->num_seqs, a->num_q_heads, mp);
+  // shared-prefix plan
+  const bool plan = a->prefix_groups > 0;
+  if (a->prefix_groups < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "prefix_groups must be >= 0");
+  if (plan && !a->prefix_plan_dev) return pkv::fail(PKV_ERR_INVALID_ARG, "prefix_groups > 0 needs prefix_plan_dev");
+  if (plan && c.dtype != PKV_F16) return pkv::fail(PKV_ERR_UNSUPPORTED, "shared-prefix plans need fp16 pools");
+  if (plan && a->prefix_groups > a->num_seqs / 2)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "more groups (%d) than pairs of sequences", a->prefix_groups);
+  if (plan && a->prefix_plan_host) {
+    const int32_t* ph = a->prefix_plan_host;
+    const int B = a->num_seqs;
+    for (int gi = 0; gi < a->prefix_groups; ++gi) {
+      const int32_t* gd = ph + 2 * int64_t(B) + int64_t(gi) * PKV_PREFIX_GROUP_INTS;
+      if (gd[0] < 1 || gd[0] > a->max_blocks || gd[1] < 2 || gd[1] > PKV_MAX_SHARERS || gd[1] * G > PREFIX_ROWS)
+        return pkv::fail(PKV_ERR_INVALID_ARG, "plan group %d: %d blocks, %d members (members x %d heads <= %d)", gi,
+                         gd[0], gd[1], G, PREFIX_ROWS);
+      for (int m = 0; m < gd[1]; ++m) {
+        const int bb = gd[2 + m];
+        if (bb < 0 || bb >= B || ph[2 * bb + 1] != gi * 64 + m || ph[2 * bb] != gd[0])
+          return pkv::fail(PKV_ERR_INVALID_ARG, "plan group %d member %d is inconsistent", gi, m);
+        if (a->ctx_lens_host && (a->ctx_lens_host[bb] - 1) / BT < gd[0])
+          return pkv::fail(PKV_ERR_INVALID_ARG, "plan group %d shares the block of a member's last token", gi);
+      }
+    }
+  }
+
+  const WsLayout wl =
+      ws_layout(c, a->num_seqs, a->num_q_heads, a->max_context, a->max_blocks, a->partition_tokens, a->prefix_groups);
+  const int mp0 = wl.grid_parts, mp = wl.max_parts;
+  const int64_t need = wl.bytes;
   if (need > 0 && (!a->workspace_dev || a->workspace_bytes < need))
     return pkv::fail(PKV_ERR_INVALID_ARG, "workspace too small: need %lld bytes", (long long)need);
   if (need > 0 && !aligned16(a->workspace_dev))
     return pkv::fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (int64_t(wl.prefix_z) + mp0 > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many partitions for one launch");
+
+  // With a plan and both host copies, partitions are sized for the longest
+  // stretch the split role covers (a grouped sequence's unshared tail, an
+  // ungrouped sequence's whole context) instead of max_context; never more
+  // partitions than the grid and the workspace hold.
+  int pb = wl.part_blocks;
+  if (plan && a->ctx_lens_host && a->prefix_plan_host && a->partition_tokens == 0) {
+    int span = 1;
+    for (int b = 0; b < a->num_seqs; ++b) {
+      const int nb = (a->ctx_lens_host[b] + BT - 1) / BT;
+      span = std::max(span, nb - std::max(0, std::min(a->prefix_plan_host[2 * b], a->max_blocks)));
+    }
+    pb = std::max(choose_part_blocks(c, a->num_seqs, span * BT, 0), (span + mp0 - 1) / mp0);
+  }
 
   const int64_t E = pkv::elem_bytes(c.dtype);
   const int64_t layer_bytes = pkv::layer_elems(c) * E;
@@ -1017,10 +1371,15 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   prm.ctx_lens = a->ctx_lens_dev;
   const int64_t rows = int64_t(a->num_seqs) * a->num_q_heads * mp;
   float* ws = static_cast<float*>(a->workspace_dev);
-  prm.part_m = need ? ws : nullptr;
-  prm.part_l = need ? ws + rows : nullptr;
-  prm.part_o = need ? ws + 2 * rows : nullptr;
+  const bool parts = need > 0;
+  prm.part_m = parts ? ws : nullptr;
+  prm.part_l = parts ? ws + rows : nullptr;
+  prm.part_o = parts ? ws + 2 * rows : nullptr;
   prm.out = static_cast<_Float16*>(a->out_dev);
+  prm.plan = plan ? a->prefix_plan_dev : nullptr;
+  prm.prefix_z = wl.prefix_z;
+  prm.prefix_pp = wl.prefix_pp;
+  prm.num_groups = plan ? a->prefix_groups : 0;
   prm.max_blocks = a->max_blocks;
   prm.num_blocks = c.num_blocks;
   prm.Hkv = c.num_kv_heads;
@@ -1033,22 +1392,48 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
   if (a->timing_events)
     for (int i = 0; i < 4; ++i) ev[i] = static_cast<hipEvent_t>(a->timing_events[i]);
-  const dim3 grid(mp, c.num_kv_heads, a->num_seqs);
+
+  // The fused append (if any) writes into private tail blocks only, which no
+  // shared-prefix work-group reads.
+  const dim3 grid(c.num_kv_heads, a->num_seqs, wl.prefix_z + mp0);
   if (ev[0] && ev[1])
     hipExtLaunchKernelGGL(fn, grid, dim3(256), 0, s, ev[0], ev[1], 0, prm);
   else
     hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, prm);
   st = hip_status(hipGetLastError(), "paged_decode launch");
-  if (st != PKV_OK || mp <= 1) return st;
+  if (st != PKV_OK || (mp0 <= 1 && !plan)) return st;
+  MergeParams mg;
+  mg.part_m = prm.part_m;
+  mg.part_l = prm.part_l;
+  mg.part_o = prm.part_o;
+  mg.ctx_lens = a->ctx_lens_dev;
+  mg.plan = prm.plan;
+  mg.out = prm.out;
+  mg.D = c.head_dim;
+  mg.max_blocks = a->max_blocks;
+  mg.max_context = a->max_context;
+  mg.part_blocks = pb;
+  mg.max_parts = mp;
+  mg.num_groups = prm.num_groups;
+  mg.prefix_pp = prm.prefix_pp;
   const dim3 rgrid(a->num_q_heads, a->num_seqs);
   if (ev[2] && ev[3])
-    hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, ev[2], ev[3], 0, prm.part_m,
-                          prm.part_l, prm.part_o, a->ctx_lens_dev, prm.out, a->max_blocks, a->max_context, pb,
-                          mp, c.head_dim);
+    hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, ev[2], ev[3], 0, mg);
   else
-    hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, prm.part_m, prm.part_l, prm.part_o,
-                       a->ctx_lens_dev, prm.out, a->max_blocks, a->max_context, pb, mp, c.head_dim);
+    hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, mg);
   return hip_status(hipGetLastError(), "lse_reduce launch");
+}
+
+int64_t pkv_prefix_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int32_t num_q_heads,
+                                          int32_t max_context, int32_t max_blocks, int32_t partition_tokens,
+                                          int32_t n_groups) {
+  int st = pkv::validate_config(cfg);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 1 || num_q_heads < 1 || max_context < 1 || max_blocks < 1 || n_groups < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_seqs, num_q_heads, max_context, max_blocks >= 1, n_groups >= 0");
+  st = check_partition_tokens(partition_tokens);
+  if (st != PKV_OK) return st;
+  return ws_layout(*cfg, num_seqs, num_q_heads, max_context, max_blocks, partition_tokens, n_groups).bytes;
 }
 
 int pkv_upload(void* dst_dev, const void* src_host, int64_t bytes, void* stream) {
@@ -1077,6 +1462,7 @@ int pkv_upload(void* dst_dev, const void* src_host, int64_t bytes, void* stream)
                      static_cast<char*>(dst_dev), static_cast<const char*>(attr.devicePointer), bytes);
   return hip_status(hipGetLastError(), "upload launch");
 }
+
 
 int pkv_probe_stream_read(const void* buf_dev, int64_t bytes, void* sink_dev, void* stream) {
   if (!buf_dev || !sink_dev || bytes < 16 || !aligned16(buf_dev))

@@ -15,6 +15,7 @@
 //   - a write at a non-zero offset of a block with refcount > 1 moves the
 //     writer to a fresh block and reports the (old, new) pair to copy;
 //   - a reservation either succeeds whole or changes nothing.
+#include <algorithm>
 #include <cstring>
 #include <unordered_map>
 #include <vector>
@@ -237,6 +238,72 @@ int pkv_build_block_tables(const pkv_pool* pool, const int64_t* seqs, int32_t B,
     for (int32_t j = int32_t(nb); j < max_blocks; ++j) row[j] = -1;
     ctx_lens_host[b] = s->len;
   }
+  return PKV_OK;
+}
+
+int32_t pkv_plan_ints(int32_t B) { return B < 0 ? 0 : 2 * B + (B / 2) * PKV_PREFIX_GROUP_INTS; }
+
+int pkv_plan_shared_prefix(const pkv_pool* pool, const int64_t* seqs, int32_t B, int32_t min_blocks,
+                           int32_t max_members, int32_t* plan_host, int32_t plan_cap, int32_t* n_groups) {
+  if (!pool || !seqs || !plan_host || !n_groups) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  if (B < 0 || min_blocks < 1 || max_members < 1 || max_members > PKV_MAX_SHARERS)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "need B >= 0, min_blocks >= 1, max_members in [1, %d]", PKV_MAX_SHARERS);
+  if (plan_cap < pkv_plan_ints(B))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "plan_cap %d < %d", plan_cap, pkv_plan_ints(B));
+  std::vector<const Seq*> sq(B);
+  for (int32_t b = 0; b < B; ++b) {
+    sq[b] = find(pool, seqs[b]);
+    if (!sq[b]) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seqs[b]);
+  }
+  // blocks that may be shared: full, and before the block of the last token
+  auto shareable = [&](int32_t b) { return sq[b]->len >= 1 ? (sq[b]->len - 1) / PKV_BLOCK_TOKENS : 0; };
+  // sequences keyed by their first block, keys in order of first appearance
+  std::vector<int32_t> keys;
+  std::unordered_map<int32_t, std::vector<int32_t>> by_first;
+  for (int32_t b = 0; b < B; ++b) {
+    if (shareable(b) < min_blocks) continue;
+    const int32_t first = sq[b]->table[0];
+    auto it = by_first.find(first);
+    if (it == by_first.end()) {
+      keys.push_back(first);
+      by_first[first] = {b};
+    } else {
+      it->second.push_back(b);
+    }
+  }
+  for (int32_t b = 0; b < B; ++b) {
+    plan_host[2 * b] = 0;
+    plan_host[2 * b + 1] = -1;
+  }
+  int32_t ng = 0;
+  for (int32_t key : keys) {
+    const std::vector<int32_t>& all = by_first[key];
+    for (size_t c0 = 0; c0 < all.size(); c0 += size_t(max_members)) {
+      const size_t c1 = std::min(all.size(), c0 + size_t(max_members));
+      if (c1 - c0 < 2) continue;
+      int32_t np = shareable(all[c0]);
+      for (size_t i = c0 + 1; i < c1; ++i) np = std::min(np, shareable(all[i]));
+      const std::vector<int32_t>& t0 = sq[all[c0]]->table;
+      int32_t lcp = 0;
+      while (lcp < np) {
+        bool same = true;
+        for (size_t i = c0 + 1; i < c1 && same; ++i) same = sq[all[i]]->table[lcp] == t0[lcp];
+        if (!same) break;
+        ++lcp;
+      }
+      if (lcp < min_blocks) continue;
+      int32_t* gd = plan_host + 2 * int64_t(B) + int64_t(ng) * PKV_PREFIX_GROUP_INTS;
+      gd[0] = lcp;
+      gd[1] = int32_t(c1 - c0);
+      for (int32_t m = 0; m < PKV_MAX_SHARERS; ++m) gd[2 + m] = m < int32_t(c1 - c0) ? all[c0 + m] : -1;
+      for (size_t i = c0; i < c1; ++i) {
+        plan_host[2 * all[i]] = lcp;
+        plan_host[2 * all[i] + 1] = ng * 64 + int32_t(i - c0);
+      }
+      ++ng;
+    }
+  }
+  *n_groups = ng;
   return PKV_OK;
 }
 

@@ -486,3 +486,95 @@ def test_upload_kernel_copies_pinned_host_bytes():
     with pytest.raises(pkv.PkvError):
         pkv.pkv_upload(src.data_ptr(), src.data_ptr(), 4096, stream)  # host target
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix plan: shared blocks read once per group
+
+@pytest.mark.parametrize("seed,groups,singles,Hq,Hkv,D,max_members", [
+    (41, ((700, 6), (333, 3)), 2, 32, 8, 128, 32),  # 4 q heads per KV head
+    (42, ((1000, 16),), 1, 16, 2, 128, 16),  # 8 per KV head: 128 query rows
+    (43, ((517, 5), (64, 2)), 2, 4, 2, 64, 32),  # 2 per KV head, d64
+    (44, ((800, 32),), 0, 8, 8, 128, 32),  # 1 per KV head, 32 members
+    (45, ((2100, 12), (48, 3)), 1, 8, 1, 64, 16),  # a single KV head, runs of 2 blocks
+    (46, ((512, 40),), 2, 32, 8, 128, 32),  # 40 sharers: groups of 32 and 8
+])
+def test_shared_prefix_plan_matches_oracle(seed, groups, singles, Hq, Hkv, D, max_members):
+    w = workloads.prefix_forest(seed, groups=groups, singles=singles, Hq=Hq, Hkv=Hkv, D=D, suffix=(0, 600))
+    lib, o = run_pair(w, prefix_plan={"max_members": max_members})
+    plan_host, ng = lib.decodes[0]["plan"]
+    assert ng >= len(groups)
+    check_host_records(lib, o)
+    check_stored_bytes(lib, o)
+    err = max_err(lib, o)
+    announce(f"plan groups={ng} max abs err {err:.3g}")
+    assert err <= F16_TOL
+    lib.close()
+
+
+@pytest.mark.parametrize("ptok", [16, 64, 512])
+def test_shared_prefix_plan_partition_sizes(ptok):
+    w = workloads.prefix_forest(47, groups=((1200, 8),), singles=2, suffix=(0, 900))
+    lib, o = run_pair(w, prefix_plan={}, partition_tokens=ptok)
+    assert lib.decodes[0]["plan"][1] == 1
+    assert max_err(lib, o) <= F16_TOL
+    lib.close()
+
+
+def test_c4_prefix_plan_and_fused_append():
+    """The copy-on-write workload with a plan (32 members x 4 query heads
+    per KV head = 128 rows over 128 shared blocks): oracle parity with and
+    without the fused append, and the two plan paths bit for bit."""
+    w = workloads.c4_prefix()
+    announce("c4 with shared-prefix plan")
+    o = OracleRun(w).run()
+    plain = LibRun(w, device=DEV, poison=True).run(prefix_plan={})
+    assert plain.decodes[0]["plan"][1] == 1
+    check_host_records(plain, o)
+    check_stored_bytes(plain, o)
+    assert max_err(plain, o) <= F16_TOL
+    announce("c4 with shared-prefix plan and fused append")
+    fused = LibRun(w, device=DEV, poison=True, fused_append=True).run(prefix_plan={})
+    assert fused.decodes[0]["fused"]  # the 32-sequence step (the second appends for the child only)
+    check_stored_bytes(fused, o)
+    for a, b in zip(fused.decodes, plain.decodes):
+        assert np.array_equal(a["out"].view(np.uint16), b["out"].view(np.uint16))
+    plain.close()
+    fused.close()
+
+
+def test_shared_prefix_plan_graph_replay_and_determinism():
+    """A plan decode captured into a HIP graph: every replay (with eager
+    decodes of another batch between them) gives the eager result bit for
+    bit, and repeated eager calls agree bit for bit."""
+    w = workloads.prefix_forest(48, groups=((900, 10), (400, 4)), singles=3, suffix=(0, 700))
+    announce("plan graph replay")
+    lib = LibRun(w, device=DEV).run(prefix_plan={})
+    rec = lib.decodes[0]
+    from paged_kv_cache_392_amd.cache import PrefixPlan
+    B = len(rec["lens"])
+    plan = PrefixPlan(rec["plan"][0], rec["plan"][1], B, DEV)
+    td = torch.from_numpy(rec["tables"]).to(DEV)
+    ld = torch.from_numpy(rec["lens"]).to(DEV)
+    qd = torch.from_numpy(rec["q"]).to(DEV)
+    cache = lib.cache
+    ws_bytes = pkv.pkv_prefix_decode_workspace_bytes(cache.cfg, B, 32, int(rec["lens"].max()),
+                                                     rec["tables"].shape[1], 0, plan.n_groups)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    for _ in range(3):
+        again = cache.paged_decode(qd, td, ld, context_lens_host=rec["lens"], workspace=ws, prefix_plan=plan)
+        torch.cuda.synchronize()
+        assert np.array_equal(again.cpu().numpy().view(np.uint16), rec["out"].view(np.uint16))
+    out = torch.empty_like(again)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cache.paged_decode(qd, td, ld, context_lens_host=rec["lens"], out=out, workspace=ws, prefix_plan=plan)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.zero_()
+        cache.paged_decode(qd[:3], td[:3], ld[:3], context_lens_host=rec["lens"][:3], workspace=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint16), rec["out"].view(np.uint16)), r
+    lib.close()

@@ -335,3 +335,181 @@ def test_device_calls_validate_before_launch():
                                                None)) == C.PKV_ERR_UNSUPPORTED
     assert status(lambda: pkv.pkv_paged_decode(args(max_blocks=300, max_context=4800, workspace_bytes=10,
                                                     partition_tokens=64), None)) == C.PKV_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix plan (host)
+
+def expected_groups(tables, lens, min_blocks, max_members):
+    """The planner's rule restated: sequences with at least min_blocks
+    shareable blocks (full, before the block of the last token) keyed by
+    their first block, keys in order of first appearance, members in batch
+    order, chunks of max_members; a chunk's shared run is its members'
+    longest common run of leading blocks within every member's shareable
+    count; chunks of one member or with a run below min_blocks are dropped."""
+    share = [(int(n) - 1) // 16 for n in lens]
+    keys, by = [], {}
+    for b, t in enumerate(tables):
+        if share[b] < min_blocks:
+            continue
+        k = int(t[0])
+        if k not in by:
+            keys.append(k)
+            by[k] = []
+        by[k].append(b)
+    out = []
+    for k in keys:
+        mem = by[k]
+        for c in range(0, len(mem), max_members):
+            ch = mem[c:c + max_members]
+            if len(ch) < 2:
+                continue
+            lim = min(share[b] for b in ch)
+            run = 0
+            while run < lim and len({int(tables[b][run]) for b in ch}) == 1:
+                run += 1
+            if run >= min_blocks:
+                out.append((run, ch))
+    return out
+
+
+def check_plan(tables, lens, host, ng, min_blocks, max_members):
+    B = len(lens)
+    assert len(host) == pkv.pkv_plan_ints(B) == 2 * B + (B // 2) * 34
+    groups = expected_groups(tables, lens, min_blocks, max_members)
+    assert ng == len(groups)
+    per = {b: (0, -1) for b in range(B)}
+    for g, (run, ch) in enumerate(groups):
+        gd = host[2 * B + 34 * g:2 * B + 34 * (g + 1)]
+        assert gd[0] == run and gd[1] == len(ch)
+        assert list(gd[2:2 + len(ch)]) == ch and all(x == -1 for x in gd[2 + len(ch):])
+        for i, b in enumerate(ch):
+            per[b] = (run, g * 64 + i)
+            # every member shares the run, and keeps the block of its last token private
+            assert np.array_equal(tables[b][:run], tables[ch[0]][:run])
+            assert run <= (int(lens[b]) - 1) // 16
+    for b in range(B):
+        assert (host[2 * b], host[2 * b + 1]) == per[b], b
+
+
+@pytest.mark.parametrize("groups,singles,min_blocks,max_members", [
+    (((700, 6), (333, 3)), 2, 1, 32),
+    (((700, 6), (333, 3)), 2, 30, 32),  # the short prefix is dropped
+    (((512, 40),), 3, 1, 32),  # 40 sharers: chunks of 32 and 8
+    (((512, 9),), 0, 1, 4),  # chunks of 4, 4 and a dropped single
+    (((16, 3), (31, 2), (32, 2)), 1, 1, 32),  # runs of 0-2 blocks
+])
+def test_plan_matches_rule_and_invariants(groups, singles, min_blocks, max_members):
+    w = workloads.prefix_forest(31, groups=groups, singles=singles, Hq=8, Hkv=2, D=64, suffix=(0, 40))
+    lib = LibRun(w).run(prefix_plan={"min_blocks": min_blocks, "max_members": max_members})
+    rec = lib.decodes[0]
+    host, ng = rec["plan"]
+    check_plan(rec["tables"], rec["lens"], host, ng, min_blocks, max_members)
+    if groups == ((700, 6), (333, 3)) and min_blocks == 1:
+        assert ng == 2
+    lib.close()
+
+
+def test_plan_on_the_copy_on_write_workload():
+    """32 forks of a 2048-token prefix: one group of 32 sharing 128 blocks;
+    then a parent and its child forked after the parent's last token."""
+    lib = LibRun(workloads.c4_prefix()).run(prefix_plan={})
+    first, second = lib.decodes
+    host, ng = first["plan"]
+    assert ng == 1 and host[2 * 32] == 128 and host[2 * 32 + 1] == 32
+    check_plan(first["tables"], first["lens"], host, ng, 1, 32)
+    host, ng = second["plan"]
+    check_plan(second["tables"], second["lens"], host, ng, 1, 32)
+    assert ng == 1 and host[4] >= 128
+    lib.close()
+
+
+def test_plan_argument_errors():
+    cfg = pkv.make_config(1, 8, 1, 64)
+    pool = pkv.pkv_pool_create(cfg)
+    s = pkv.pkv_seq_create(pool)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_plan_shared_prefix(pool, [s], min_blocks=0)
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_plan_shared_prefix(pool, [s], max_members=33)
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.pkv_plan_shared_prefix(pool, [s, 12345])
+    assert e.value.status == pkv._capi.PKV_ERR_UNKNOWN_SEQ
+    host, ng = pkv.pkv_plan_shared_prefix(pool, [s, s])  # empty sequences: nothing shared
+    assert ng == 0 and list(host[:4]) == [0, -1, 0, -1]
+    assert pkv.pkv_plan_ints(0) == 0 and pkv.pkv_plan_ints(5) == 10 + 2 * 34
+    pkv.pkv_pool_destroy(pool)
+
+
+def test_prefix_workspace_bytes():
+    cfg = pkv.make_config(1, 16, 8, 128)
+    # no groups: the plain decode's workspace
+    for B, ctx, pt in [(16, 100, 128), (16, 8193, 512), (3, 3000, 0)]:
+        assert pkv.pkv_prefix_decode_workspace_bytes(cfg, B, 32, ctx, 600, pt, 0) == \
+            pkv.pkv_decode_workspace_bytes(cfg, B, 32, ctx, pt)
+    # each partial row holds the split-K partitions (1 here) and one slot per
+    # prefix partition of at most 32 shared blocks (1 here)
+    assert pkv.pkv_prefix_decode_workspace_bytes(cfg, 16, 32, 100, 7, 128, 2) == 16 * 32 * 2 * 130 * 4
+    # 9000 tokens in 512-token partitions: 18; one group over 8 KV heads and
+    # 600 table blocks: 16 prefix partitions (about 128 prefix work-groups)
+    assert pkv.pkv_prefix_decode_workspace_bytes(cfg, 4, 32, 9000, 600, 512, 1) == 4 * 32 * 34 * 130 * 4
+    # one KV head: 38 partitions of at most 16 blocks
+    one = pkv.make_config(1, 16, 1, 128)
+    assert pkv.pkv_prefix_decode_workspace_bytes(one, 4, 8, 9000, 600, 512, 1) == 4 * 8 * (18 + 38) * 130 * 4
+    with pytest.raises(pkv.PkvError):
+        pkv.pkv_prefix_decode_workspace_bytes(cfg, 16, 32, 100, 7, 128, -1)
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="argument checks with placeholder pointers: CPU only")
+def test_decode_plan_validated_before_launch():
+    cfg = pkv.make_config(1, 64, 2, 64)
+    fake = 1 << 20
+    C = pkv._capi
+    B, mb = 34, 4
+    lens = np.full(B, 40, np.int32)
+
+    def plan(run=2, members=(0, 1)):
+        p = np.full(pkv.pkv_plan_ints(B), -1, np.int32)
+        p[0:2 * B:2] = 0
+        gd = p[2 * B:2 * B + 34]
+        gd[0], gd[1] = run, len(members)
+        for i, b in enumerate(members):
+            gd[2 + i] = b
+            p[2 * b], p[2 * b + 1] = run, i
+        return p
+
+    def call(p, groups=1, c=cfg, dev=fake, Hq=4):
+        a = C.pkv_decode_args()
+        a.cfg = C.ctypes.pointer(c)
+        a.pool_dev, a.q_dev, a.block_tables_dev, a.ctx_lens_dev, a.out_dev = fake, fake, fake, fake, fake
+        a.num_seqs, a.num_q_heads, a.max_blocks, a.max_context = B, Hq, mb, 64
+        a.ctx_lens_host = lens.ctypes.data_as(C._p_i32)
+        a.scale = 0.125
+        a.workspace_dev, a.workspace_bytes = fake, 1 << 30
+        a.prefix_plan_dev = dev
+        a.prefix_plan_host = p.ctypes.data_as(C._p_i32) if p is not None else None
+        a.prefix_groups = groups
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_paged_decode(a, None)
+        return e.value.status
+
+    assert call(plan(), dev=None) == C.PKV_ERR_INVALID_ARG
+    assert call(plan(), groups=-1) == C.PKV_ERR_INVALID_ARG
+    assert call(plan(), groups=18) == C.PKV_ERR_INVALID_ARG  # more groups than pairs
+    assert call(plan(run=0)) == C.PKV_ERR_INVALID_ARG
+    assert call(plan(run=3)) == C.PKV_ERR_INVALID_ARG  # the block of the last token (40 -> block 2)
+    assert call(plan(members=(0,))) == C.PKV_ERR_INVALID_ARG
+    assert call(plan(members=(0, 40))) == C.PKV_ERR_INVALID_ARG
+    bad = plan()
+    bad[3] = 5  # member 1's back-reference
+    assert call(bad) == C.PKV_ERR_INVALID_ARG
+    bad = plan()
+    bad[2] = 1  # member 1's run differs from the group's
+    assert call(bad) == C.PKV_ERR_INVALID_ARG
+    i8 = pkv.make_config(1, 64, 2, 64, "i8")
+    assert call(plan(), c=i8) == C.PKV_ERR_UNSUPPORTED
+    # 8 query heads per KV head: 17 members are 136 query rows, over 128
+    assert call(plan(members=tuple(range(17))), Hq=16) == C.PKV_ERR_INVALID_ARG
+    bad = plan(members=tuple(range(32)))
+    bad[2 * B + 1] = 33  # over 32 members
+    assert call(bad) == C.PKV_ERR_INVALID_ARG

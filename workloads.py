@@ -192,6 +192,50 @@ def c4_prefix(seed=4, sharers=32, prefix=2048, dtype="f16"):
     return w
 
 
+def prefix_forest(seed, groups=((700, 6),), singles=2, Hq=32, Hkv=8, D=128, suffix=(1, 300), N=None,
+                  shuffle=True):
+    """Several shared prefixes in one batch: for each ``(prefix, sharers)`` a
+    root prefilled to ``prefix`` tokens and forked ``sharers - 1`` times; every
+    member (root included) then prefills a private suffix of U[suffix]
+    tokens (0 allowed); ``singles`` unrelated sequences of U[1, max prefix]
+    tokens; one appended token each; one decode over all of them in a
+    shuffled batch order (members of a group not adjacent)."""
+    rng = np.random.default_rng(seed)
+    sizes = [(int(p), int(n)) for p, n in groups]
+    top = max([p for p, _ in sizes] + [1])
+    suf = [rng.integers(suffix[0], suffix[1] + 1, n).tolist() for _, n in sizes]
+    single_lens = rng.integers(1, top + 1, singles).tolist()
+    if N is None:
+        need = sum(-(-(p + 1) // 16) + sum(-(-(x + 1) // 16) + 1 for x in sf) for (p, _), sf in zip(sizes, suf))
+        need += sum(-(-(n + 1) // 16) for n in single_lens)
+        N = need + 8
+    order = rng.permutation(N).astype(np.int32)
+    w = Workload("prefix_forest", N, Hq, Hkv, D, "f16", order)
+    names = []
+    for gi, ((p, n), sf) in enumerate(zip(sizes, suf)):
+        root = f"g{gi}m0"
+        w.steps.append(("create", root))
+        w.steps.append(("prefill", root, _normal(rng, (p, Hkv, D)), _normal(rng, (p, Hkv, D))))
+        members = [root] + [f"g{gi}m{i}" for i in range(1, n)]
+        for m in members[1:]:
+            w.steps.append(("fork", root, m))
+        for m, x in zip(members, sf):
+            if x:
+                w.steps.append(("prefill", m, _normal(rng, (x, Hkv, D)), _normal(rng, (x, Hkv, D))))
+        names += members
+    for i, n in enumerate(single_lens):
+        w.steps.append(("create", f"u{i}"))
+        w.steps.append(("prefill", f"u{i}", _normal(rng, (n, Hkv, D)), _normal(rng, (n, Hkv, D))))
+        names.append(f"u{i}")
+    if shuffle:
+        names = [names[i] for i in rng.permutation(len(names))]
+    B = len(names)
+    w.steps.append(("append", names, _normal(rng, (B, Hkv, D)), _normal(rng, (B, Hkv, D))))
+    w.steps.append(("decode", names, _normal(rng, (B, Hq, D))))
+    w.seed = seed
+    return w
+
+
 def c5_int8(seed=5, batch=16, ctx=8192):
     """Long-context int8 KV: 16 sequences at 8192 tokens of N(0,1) fp16 data
     stored as int8 with one fp16 scale per (block, KV head); decode only."""
