@@ -25,7 +25,7 @@ Modules
 sizes      KV-cache byte counts (the size formula and its table).
 allocator  block pool: free list, refcounts, block tables, fork, COW.
 cache      the paged K/V store: append, block copy, gather.
-attention  decode attention by definition (NumPy fp64) and by brute force.
+attention  decode and causal prefill attention by definition (NumPy fp64), decode by brute force.
 quant      int8 absmax quantiser with one scale per (block, KV head).
 
 Pinning status: every function here is pinned by a ``-m "not gpu"`` test
@@ -43,7 +43,7 @@ from .sizes import (
 )
 from .allocator import RefAllocator, NoBlocks, UnknownSeq
 from .cache import RefCache
-from .attention import decode, decode_seq_head, brute_decode, gather
+from .attention import decode, decode_seq_head, brute_decode, gather, prefill
 from .quant import quantize_block_int8, quantize_pool_int8, dequantize_int8, append_row_int8
 
 __all__ = [
@@ -58,6 +58,7 @@ __all__ = [
     "decode",
     "decode_seq_head",
     "brute_decode",
+    "prefill",
     "gather",
     "quantize_block_int8",
     "quantize_pool_int8",

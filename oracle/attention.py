@@ -126,3 +126,53 @@ def brute_decode(cache, q, block_tables, context_lens, layer=0, scale=None):
                     acc += weights[t] * rows[t][d]
                 out[b][h][d] = acc / total
     return out
+
+
+def prefill(cache, q, q_lens, block_tables, context_lens, layer=0, scale=None):
+    """Attention of each sequence's newest ``q_lens[b]`` tokens over its cache.
+
+    The prefill phase feeds a prompt's tokens in together ([p1] §二; [p2]
+    §1.3) and writes their K/V into the cache ([p2] §2.2); Flash Attention
+    tiles this attention without changing its result ([p1] §四). Reading
+    taken: the attention is causal. Token ``i`` of the chunk sits at logical
+    position ``p = context_lens[b] - q_lens[b] + i`` and attends to tokens
+    ``0..p``, itself included, which is what decoding the chunk one token at
+    a time would give ([p2] §2.2 pseudocode: attend over ``[:cache_len+1]``
+    after appending) and what makes cached K/V reusable ([p1] §二). A chunk
+    may follow cached tokens (``p`` starts above 0).
+
+    ``q`` is ``[T, Hq, D]`` with sequence ``b``'s tokens at rows
+    ``sum(q_lens[:b]) ..``; the cache must already hold each sequence's
+    ``context_lens[b]`` tokens, the chunk's own included. Returns fp64
+    ``[T, Hq, D]``. Per (sequence, KV head) the scores are one matrix product
+    of the gathered rows, positions after ``p`` are excluded before the
+    softmax, and the weights multiply V.
+    """
+    q = np.asarray(q)
+    T, Hq, D = q.shape
+    Hkv = cache.kv_heads
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if int(np.sum(q_lens)) != T:
+        raise ValueError("q_lens must add up to the rows of q")
+    out = np.empty((T, Hq, D), np.float64)
+    row0 = 0
+    for b, ql in enumerate(q_lens):
+        ql, n = int(ql), int(context_lens[b])
+        if ql < 1 or ql > n:
+            raise ValueError("need 1 <= q_lens[b] <= context_lens[b]")
+        pos = np.arange(n - ql, n)  # logical positions of the chunk's tokens
+        visible = np.arange(n)[None, :] <= pos[:, None]  # [ql, n]
+        for g in range(Hkv):
+            Kc = gather(cache.K, layer, block_tables[b], n, g, cache.scales, 0)
+            Vc = gather(cache.V, layer, block_tables[b], n, g, cache.scales, 1)
+            for h in range(g * G, (g + 1) * G):
+                s = (q[row0:row0 + ql, h].astype(np.float64) @ Kc.T) * np.float64(scale)  # [ql, n]
+                s = np.where(visible, s, -np.inf)
+                e = np.exp(s - s.max(axis=1, keepdims=True))
+                out[row0:row0 + ql, h] = (e / e.sum(axis=1, keepdims=True)) @ Vc
+        row0 += ql
+    return out

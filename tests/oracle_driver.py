@@ -26,6 +26,7 @@ class OracleRun:
         self.seq = {}
         self.reserves = []  # (step index, name, slots, cow pairs)
         self.decodes = []  # dicts: names, tables, lens, q, out
+        self.prefills = []  # dicts: names, q_lens, tables, lens, q, out
         self.churn_log = []
 
     # -- steps -----------------------------------------------------------
@@ -61,6 +62,8 @@ class OracleRun:
                 self._churn(step[1])
             elif kind == "decode":
                 self._decode(step[1], step[2], decode)
+            elif kind == "prefill_attn":
+                self._prefill_attn(step[1], step[2], step[3], decode)
             else:
                 raise ValueError(kind)
         return self
@@ -115,3 +118,13 @@ class OracleRun:
             cache = self.q8 if self.w.dtype == "i8" else self.cache
             rec["out"] = oracle.decode(cache, q, tables, lens, 0, self.w.scale)
         self.decodes.append(rec)
+
+    def _prefill_attn(self, names, q_lens, q, compute):
+        sids = [self.seq[n] for n in names]
+        max_blocks = max(len(self.alloc.tables[s]) for s in sids)
+        tables, lens = self.alloc.block_tables(sids, max_blocks)
+        rec = {"names": list(names), "q_lens": list(q_lens), "tables": np.array(tables, np.int32),
+               "lens": np.array(lens, np.int32), "q": q, "out": None}
+        if compute:
+            rec["out"] = oracle.prefill(self.cache, q, q_lens, tables, lens, 0, self.w.scale)
+        self.prefills.append(rec)

@@ -165,3 +165,52 @@ def test_append_without_requantising_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "append_row_int8", lazy)
     with pytest.raises(AssertionError):
         test_append_beyond_range_requantises_the_block()
+
+
+def test_causal_off_by_one_is_caught(monkeypatch):
+    """A prefill whose token does not see itself (positions < p instead of
+    <= p) fails the SDPA pin."""
+    from test_oracle_prefill import check_prefill_against_sdpa
+
+    def prefill(cache, q, q_lens, block_tables, context_lens, layer=0, scale=None):
+        q = np.asarray(q)
+        T, Hq, D = q.shape
+        G = Hq // cache.kv_heads
+        sc = 1.0 / math.sqrt(D) if scale is None else scale
+        out = np.zeros((T, Hq, D))
+        row0 = 0
+        for b, ql in enumerate(q_lens):
+            n = int(context_lens[b])
+            for g in range(cache.kv_heads):
+                Kc = att.gather(cache.K, layer, block_tables[b], n, g)
+                Vc = att.gather(cache.V, layer, block_tables[b], n, g)
+                for i in range(ql):
+                    p = n - ql + i
+                    for h in range(g * G, (g + 1) * G):
+                        s = (Kc[:max(p, 1)] @ q[row0 + i, h].astype(np.float64)) * sc
+                        e = np.exp(s - s.max())
+                        out[row0 + i, h] = (e / e.sum()) @ Vc[:max(p, 1)]
+            row0 += ql
+        return out
+
+    monkeypatch.setattr(oracle, "prefill", prefill)
+    with pytest.raises(AssertionError):
+        check_prefill_against_sdpa(workloads.prefill_chunks(11, [5, 0], [12, 30], 8, 2, 64))
+
+
+def test_prefill_grouping_mixup_is_caught(monkeypatch):
+    """Interleaved head grouping in the prefill fails the SDPA pin."""
+    from test_oracle_prefill import check_prefill_against_sdpa
+    real = att.prefill
+
+    def prefill(cache, q, q_lens, block_tables, context_lens, layer=0, scale=None):
+        q = np.asarray(q)
+        G = q.shape[1] // cache.kv_heads
+        perm = [(h % cache.kv_heads) * G + h // cache.kv_heads for h in range(q.shape[1])]
+        out = real(cache, q[:, perm], q_lens, block_tables, context_lens, layer, scale)
+        inv = np.argsort(perm)
+        return out[:, inv]
+
+    monkeypatch.setattr(oracle, "prefill", prefill)
+    with pytest.raises(AssertionError):
+        check_prefill_against_sdpa(workloads.prefill_chunks(11, [5, 0], [12, 30], 8, 2, 64))

@@ -16,6 +16,9 @@ Step kinds::
     ("free", name)                   release a sequence
     ("churn", Churn)                 alloc/free traffic of earlier requests
     ("decode", names, q)             one decode step over the named sequences
+    ("prefill_attn", names, q_lens, q)  causal attention of each named
+                                     sequence's newest q_lens[i] tokens (already
+                                     written) over its cache; q is [sum q_lens, Hq, D]
 
 ``k``/``v`` are ``[n, Hkv, D]`` fp16 and ``q`` is ``[B, Hq, D]`` fp16, drawn as
 ``standard_normal(float32).astype(float16)``. Draws follow one fixed order:
@@ -232,6 +235,33 @@ def prefix_forest(seed, groups=((700, 6),), singles=2, Hq=32, Hkv=8, D=128, suff
     B = len(names)
     w.steps.append(("append", names, _normal(rng, (B, Hkv, D)), _normal(rng, (B, Hkv, D))))
     w.steps.append(("decode", names, _normal(rng, (B, Hq, D))))
+    w.seed = seed
+    return w
+
+
+def prefill_chunks(seed, cached, chunk, Hq=32, Hkv=8, D=128, N=None, shuffle=True):
+    """Paged prefill: sequence i holds ``cached[i]`` earlier tokens (0 = a
+    fresh prompt), then a chunk of ``chunk[i]`` new tokens is written and
+    attended causally over the whole cache. Pool blocks in random order
+    (``shuffle``); the earlier tokens and the chunk are written in separate
+    steps, so a chunk may start inside a partly filled block."""
+    rng = np.random.default_rng(seed)
+    B = len(chunk)
+    if N is None:
+        N = sum(-(-(c + k) // 16) for c, k in zip(cached, chunk)) + 4
+    order = rng.permutation(N).astype(np.int32)  # drawn either way: the values that follow stay the same
+    if not shuffle:
+        order = np.arange(N, dtype=np.int32)
+    w = Workload("prefill_chunks", N, Hq, Hkv, D, "f16", order)
+    names = [f"s{i}" for i in range(B)]
+    for s_ in names:
+        w.steps.append(("create", s_))
+    for s_, c in zip(names, cached):
+        if c:
+            w.steps.append(("prefill", s_, _normal(rng, (c, Hkv, D)), _normal(rng, (c, Hkv, D))))
+    for s_, k in zip(names, chunk):
+        w.steps.append(("prefill", s_, _normal(rng, (k, Hkv, D)), _normal(rng, (k, Hkv, D))))
+    w.steps.append(("prefill_attn", names, [int(k) for k in chunk], _normal(rng, (int(sum(chunk)), Hq, D))))
     w.seed = seed
     return w
 
