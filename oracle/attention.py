@@ -139,7 +139,8 @@ def prefill(cache, q, q_lens, block_tables, context_lens, layer=0, scale=None):
     ``0..p``, itself included, which is what decoding the chunk one token at
     a time would give ([p2] §2.2 pseudocode: attend over ``[:cache_len+1]``
     after appending) and what makes cached K/V reusable ([p1] §二). A chunk
-    may follow cached tokens (``p`` starts above 0).
+    may follow cached tokens (``p`` starts above 0); a sequence with an empty
+    chunk contributes no rows.
 
     ``q`` is ``[T, Hq, D]`` with sequence ``b``'s tokens at rows
     ``sum(q_lens[:b]) ..``; the cache must already hold each sequence's
@@ -162,8 +163,10 @@ def prefill(cache, q, q_lens, block_tables, context_lens, layer=0, scale=None):
     row0 = 0
     for b, ql in enumerate(q_lens):
         ql, n = int(ql), int(context_lens[b])
-        if ql < 1 or ql > n:
-            raise ValueError("need 1 <= q_lens[b] <= context_lens[b]")
+        if ql < 0 or ql > n or n < 1:
+            raise ValueError("need 0 <= q_lens[b] <= context_lens[b] and context_lens[b] >= 1")
+        if ql == 0:  # no new tokens in this sequence: no rows
+            continue
         pos = np.arange(n - ql, n)  # logical positions of the chunk's tokens
         visible = np.arange(n)[None, :] <= pos[:, None]  # [ql, n]
         for g in range(Hkv):

@@ -135,3 +135,14 @@ def test_bad_lengths_are_rejected():
         oracle.prefill(run.cache, rec["q"], [6], rec["tables"], rec["lens"])
     with pytest.raises(ValueError):
         oracle.prefill(run.cache, rec["q"], [5], rec["tables"], np.array([4]))
+
+
+def test_empty_chunk_contributes_no_rows():
+    """A sequence without new tokens adds no rows; the others are as if it
+    were absent."""
+    w = workloads.prefill_chunks(18, [3, 9, 0], [7, 0, 5], 4, 2, 8)
+    run = OracleRun(w).run()
+    rec = run.prefills[0]
+    assert rec["out"].shape[0] == 12
+    alone = oracle.prefill(run.cache, rec["q"], [7, 5], rec["tables"][[0, 2]], rec["lens"][[0, 2]], 0, w.scale)
+    np.testing.assert_array_equal(rec["out"], alone)
