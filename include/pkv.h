@@ -289,6 +289,45 @@ int64_t pkv_prefix_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seq
                                           int32_t max_context, int32_t max_blocks, int32_t partition_tokens,
                                           int32_t n_groups);
 
+/* ---- paged prefill ([p1] §二, [p2] §1.3: a prompt's tokens are processed
+ * together; [p1] §四: tiled attention with an online softmax) ------------- */
+
+typedef struct pkv_prefill_args {
+  const pkv_config* cfg;
+  const void* pool_dev;
+  int32_t layer;
+  const void* q_dev;              /* fp16 [T][Hq][D]: the chunks' queries,
+                                     sequence after sequence                     */
+  int32_t num_seqs;               /* B, in [1, 65535]                             */
+  int32_t num_q_heads;            /* Hq, a multiple of Hkv; Hq/Hkv in {1,2,4,8}   */
+  const int32_t* q_start_dev;     /* int32 [B + 1]: sequence b's rows of q and out
+                                     are q_start[b] .. q_start[b + 1] - 1         */
+  const int32_t* q_start_host;    /* the same, on the host: required              */
+  const int32_t* block_tables_dev;/* int32 [B][max_blocks]                        */
+  int32_t max_blocks;
+  const int32_t* ctx_lens_dev;    /* int32 [B]: tokens cached, the chunk's own
+                                     included (append the chunk's K/V first)      */
+  const int32_t* ctx_lens_host;   /* optional host copy, validated if non-NULL    */
+  int32_t max_context;            /* >= every ctx_len; at most 16384              */
+  void* out_dev;                  /* fp16 [T][Hq][D]                              */
+  float scale;                    /* softmax scale, normally 1/sqrt(D)            */
+} pkv_prefill_args;
+
+/* Causal attention of a chunk of new tokens per sequence over its paged
+ * cache: token i of sequence b's chunk (qlen_b = q_start[b+1] - q_start[b]
+ * tokens) sits at logical position ctx_lens[b] - qlen_b + i and attends to
+ * tokens 0..that position, itself included; with ctx_lens[b] > qlen_b the
+ * chunk follows cached tokens (chunked prefill). Query head h uses KV head
+ * h / (Hq/Hkv). The K/V rows are read in place through the block table.
+ * fp32 accumulation, fp16 probabilities in the value product, fp16 output
+ * (nearest even). The chunk's K/V must already be in the cache
+ * (pkv_append_kv). fp16 pools; head_dim 64 or 128. No workspace.
+ * INVALID_ARG: null pointers, q_start not starting at 0 or decreasing,
+ * misalignment, a chunk longer than its context or a context out of range
+ * (host copies). UNSUPPORTED: int8 pools, group size or head_dim not built,
+ * a context above 16384 tokens. Sequences with qlen_b = 0 are skipped. */
+int pkv_paged_prefill(const pkv_prefill_args* args, void* stream);
+
 /* Upload host metadata for the next step (block tables, lengths: the
  * per-step upload of [p2] §3.3's batch that changes every step) from pinned
  * host memory to device memory, with a kernel on `stream` that reads the

@@ -2,7 +2,7 @@
 
 The work runs in libpkv (``include/pkv.h``): a C++ block allocator and HIP
 kernels for append, copy-on-write block copies, split-K paged decode and the
-log-sum-exp merge. This package is its thin Python binding: ``_capi`` keeps
+log-sum-exp merge, and causal paged prefill. This package is its thin Python binding: ``_capi`` keeps
 the C names (argument marshalling only) and ``PagedKVCache`` wraps them with
 torch tensors for device memory and streams. Importing the package opens
 the library and fails loudly if it is not built.
@@ -14,7 +14,8 @@ from ._capi import (  # noqa: F401  (re-exported C names)
     pkv_pool_bytes, pkv_pool_create, pkv_pool_destroy, pkv_seq_create, pkv_seq_free,
     pkv_seq_fork, pkv_seq_reserve, pkv_seq_len, pkv_seq_block_table, pkv_block_refcount,
     pkv_num_free, pkv_free_list, pkv_build_block_tables, pkv_plan_ints, pkv_plan_shared_prefix,
-    pkv_copy_blocks, pkv_append_kv, pkv_decode_workspace_bytes, pkv_prefix_decode_workspace_bytes, pkv_paged_decode, pkv_upload, pkv_probe_stream_read, pkv_strerror,
+    pkv_copy_blocks, pkv_append_kv, pkv_decode_workspace_bytes, pkv_prefix_decode_workspace_bytes, pkv_paged_decode,
+    pkv_paged_prefill, pkv_upload, pkv_probe_stream_read, pkv_strerror,
     pkv_last_error,
 )
 from .cache import PagedKVCache, paged_decode  # noqa: F401

@@ -57,6 +57,14 @@ class pkv_decode_args(ctypes.Structure):
                 ("timing_events", ctypes.POINTER(_vp))]
 
 
+class pkv_prefill_args(ctypes.Structure):
+    _fields_ = [("cfg", ctypes.POINTER(pkv_config)), ("pool_dev", _vp), ("layer", _c_i32),
+                ("q_dev", _vp), ("num_seqs", _c_i32), ("num_q_heads", _c_i32),
+                ("q_start_dev", _vp), ("q_start_host", _p_i32), ("block_tables_dev", _vp),
+                ("max_blocks", _c_i32), ("ctx_lens_dev", _vp), ("ctx_lens_host", _p_i32),
+                ("max_context", _c_i32), ("out_dev", _vp), ("scale", ctypes.c_float)]
+
+
 class PkvError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"pkv error {status}: {message}")
@@ -89,6 +97,7 @@ _SIGS = {
     "pkv_prefix_decode_workspace_bytes": (_c_i64, [ctypes.POINTER(pkv_config), _c_i32, _c_i32, _c_i32, _c_i32,
                                                    _c_i32, _c_i32]),
     "pkv_paged_decode": (ctypes.c_int, [ctypes.POINTER(pkv_decode_args), _vp]),
+    "pkv_paged_prefill": (ctypes.c_int, [ctypes.POINTER(pkv_prefill_args), _vp]),
     "pkv_upload": (ctypes.c_int, [_vp, _vp, _c_i64, _vp]),
     "pkv_probe_stream_read": (ctypes.c_int, [_vp, _c_i64, _vp, _vp]),
     "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -288,6 +297,10 @@ def pkv_prefix_decode_workspace_bytes(cfg, num_seqs, num_q_heads, max_context, m
 
 def pkv_paged_decode(args, stream):
     _check(load().pkv_paged_decode(ctypes.byref(args), stream))
+
+
+def pkv_paged_prefill(args, stream):
+    _check(load().pkv_paged_prefill(ctypes.byref(args), stream))
 
 
 def pkv_upload(dst_dev, src_host, nbytes, stream):

@@ -226,6 +226,55 @@ class PagedKVCache:
             max_blocks = max(len(self.block_table(s)) for s in seqs)
         return C.pkv_build_block_tables(self.handle, seqs, max_blocks)
 
+    def paged_prefill(self, q, q_lens, block_tables, context_lens, layer=0, out=None, scale=None,
+                      context_lens_host=None, max_context=None):
+        """Causal attention of each sequence's newest ``q_lens[b]`` tokens
+        (their K/V already appended) over its cache: ``q`` is fp16
+        ``[T, Hq, D]``, sequence after sequence; token i of sequence b's
+        chunk sits at position ``context_lens[b] - q_lens[b] + i`` and sees
+        tokens up to itself. Returns ``out [T, Hq, D]`` fp16."""
+        if q.dtype != torch.float16 or q.dim() != 3:
+            raise TypeError("q must be float16 [T, Hq, D]")
+        q = q.contiguous()
+        T, Hq, D = q.shape
+        ql = np.ascontiguousarray(q_lens, np.int64)
+        if ql.sum() != T:
+            raise ValueError("q_lens must add up to the rows of q")
+        B = len(ql)
+        starts = np.zeros(B + 1, np.int32)
+        starts[1:] = np.cumsum(ql)
+        starts_dev = _dev_i32(starts, self.device)
+        if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+            raise TypeError("block_tables and context_lens must be int32")
+        block_tables = block_tables.contiguous()
+        context_lens = context_lens.contiguous()
+        max_blocks = block_tables.shape[1]
+        host = None if context_lens_host is None else np.ascontiguousarray(context_lens_host, np.int32)
+        if max_context is None:
+            max_context = int(host.max()) if host is not None else max_blocks * 16
+        if scale is None:
+            scale = 1.0 / math.sqrt(D)
+        if out is None:
+            out = torch.empty((T, Hq, D), dtype=torch.float16, device=q.device)
+        a = C.pkv_prefill_args()
+        a.cfg = C.ctypes.pointer(self.cfg)
+        a.pool_dev = self.pool.data_ptr()
+        a.layer = layer
+        a.q_dev = q.data_ptr()
+        a.num_seqs = B
+        a.num_q_heads = Hq
+        a.q_start_dev = starts_dev.data_ptr()
+        a.q_start_host = starts.ctypes.data_as(C._p_i32)
+        a.block_tables_dev = block_tables.data_ptr()
+        a.max_blocks = max_blocks
+        a.ctx_lens_dev = context_lens.data_ptr()
+        a.ctx_lens_host = host.ctypes.data_as(C._p_i32) if host is not None else None
+        a.max_context = max_context
+        a.out_dev = out.data_ptr()
+        a.scale = scale
+        C.pkv_paged_prefill(a, _stream())
+        return out
+
     def plan_shared_prefix(self, seqs, min_blocks=1, max_members=C.PKV_MAX_SHARERS):
         """Group the batch's sequences that share leading blocks so one decode
         reads those blocks once for all of them (the plan is tied to this

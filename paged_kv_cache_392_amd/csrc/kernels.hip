@@ -338,13 +338,20 @@ __device__ __forceinline__ void seq_prefix(const int32_t* plan, int b, int max_b
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
-// The shared-prefix role of a decode work-group (4 waves): KV head g,
-// partition `part` of group grp's shared blocks. The group's members share
-// their leading blocks ([p1] §三): each K/V tile of the run is read once here
-// and attended by all R = members x G query rows, in 16-row blocks (wave w
-// takes blocks w and w + 4).
+// Attention of up to 128 query rows over consecutive tiles of one block
+// table, by a work-group of 4 waves on the matrix cores: the shared-prefix
+// work-groups of the decode and the paged prefill both run it. Rows come in
+// 16-row blocks (wave w takes blocks w and w + 4); row r's q is at qrow(r)
+// (null: a padding row, never emitted). With MASK, row r sees logical
+// tokens below limit(r) only (padding rows must not be masked entirely),
+// and V rows of tokens at or past nvalid (slots never written) are staged
+// as zeros, so a masked weight of 0 never meets a stale NaN.
+// Tiles jb .. jb + nt - 1 of `trow` (nt <= MAXT, their block ids staged in
+// LDS). emit(r, o, m, l) receives row r's unnormalised output, lane
+// (n, j) holding dims 16 i + 4 j + e of row 16 rb + n, with the row's
+// base-2 running max m and its sum l.
 //
-// Per tile and row block, on the matrix cores:
+// Per tile and row block:
 //   S^T (16 tokens x 16 rows) = K (16 x D) . Q^T (D x 16),
 //       v_mfma_f32_16x16x32_f16 over D/32 chunks: lane (n, j) receives
 //       tokens 4j..4j+3 of query row n;
@@ -356,11 +363,11 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 // K tiles are staged in LDS row-major (rows padded by 16 bytes), V tiles
 // transposed ([dim][token]) so each lane reads its 4 tokens of one dim as 8
 // contiguous bytes. Online softmax per row in base 2 with the lazy running
-// max of the split role. Shared blocks are full, so nothing is masked. Each
-// row ends as one (m, l, o[D]) partial, written into slot `part` of the
-// member's own partial row, ahead of its split-K partials.
-template <int D, int G>
-__device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int grp, int part) {
+// max of the split kernel.
+template <int D, int MAXT, bool MASK, typename QRow, typename Limit, typename Emit>
+__device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int Hkv, int g, int num_blocks,
+                                            const int32_t* trow, int jb, int nt, int R, int nvalid,
+                                            float scale_log2, QRow qrow, Limit limit, Emit emit) {
   constexpr int NCH = D / 32;           // score MFMA chunks
   constexpr int NDB = D / 16;           // value MFMA dim blocks
   constexpr int KROW = D * 2 + 16;      // bytes per staged K row
@@ -372,43 +379,25 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
   static_assert(PF % 2 == 0, "LDS stages alternate with the ring slot");
   __shared__ __align__(16) char kst[2][BT * KROW];
   __shared__ __align__(16) char vst[2][D * VTROW];
-  __shared__ int blk_ids[64];
+  __shared__ int blk_ids[MAXT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lj = lane >> 4;
-  const int B = gridDim.y, Hq = prm.Hkv * G;
-  const int32_t* gd = prm.plan + 2 * int64_t(B) + int64_t(grp) * PKV_PREFIX_GROUP_INTS;
-  const int np = min(gd[0], prm.max_blocks);
-  const int members = min(gd[1], PKV_MAX_SHARERS);
-  const int R = min(members * G, PREFIX_ROWS);
-  const int b0 = gd[2];
-  if (np <= 0 || R <= 0 || unsigned(b0) >= unsigned(B)) return;
-  const int pbp = prefix_blocks_per_part(np, prm.prefix_pp);  // <= 64: the host sizes prefix_pp
-  const int jb = part * pbp, je = min(np, jb + pbp);
-  if (jb >= je) return;
-  const int nt = je - jb;
-  if (tid < nt) blk_ids[tid] = prm.tables[int64_t(b0) * prm.max_blocks + jb + tid];
+  for (int i = tid; i < nt; i += 256) blk_ids[i] = trow[jb + i];
 
   // q^T as the B operand of the score MFMA, per row block of this wave
   const int rb0 = wave, rb1 = wave + 4;
   const bool has0 = rb0 * 16 < R, has1 = rb1 * 16 < R;
-  auto member_of = [&](int r) { return r < R ? gd[2 + r / G] : -1; };
   auto load_q = [&](int rb, half8_t (&qb)[NCH]) {
-    const int r = rb * 16 + ln;
-    const int bb = member_of(r);
+    const _Float16* qp = qrow(rb * 16 + ln);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      if (unsigned(bb) < unsigned(B)) {
-        qb[c] = *reinterpret_cast<const half8_t*>(prm.q + (int64_t(bb) * Hq + g * G + r % G) * D + 32 * c + 8 * lj);
-      } else {
-        qb[c] = half8_t{};
-      }
-    }
+    for (int c = 0; c < NCH; ++c) qb[c] = qp ? *reinterpret_cast<const half8_t*>(qp + 32 * c + 8 * lj) : half8_t{};
   };
   half8_t q0[NCH], q1[NCH];
   if (has0) load_q(rb0, q0);
   if (has1) load_q(rb1, q1);
+  const int lim0 = MASK ? limit(rb0 * 16 + ln) : 0, lim1 = MASK ? limit(rb1 * 16 + ln) : 0;
 
   float4_t o0[NDB], o1[NDB];
 #pragma unroll
@@ -422,14 +411,12 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
   // t moves pieces t + 256 j. Tiles are fetched PF ahead into a register
   // ring; the loads are unconditional (indices past the last tile re-read
   // it) so the compiler counts outstanding loads statically.
-  const char* Kc = static_cast<const char*>(prm.K);
-  const char* Vc = static_cast<const char*>(prm.V);
   constexpr int NLD = 2 * LOADERS / 256;
   uint4 ring[PF][NLD];
   auto gload = [&](int it, uint4 (&r)[NLD]) {
     const int blk = blk_ids[min(it, nt - 1)];
-    const int safe = unsigned(blk) < unsigned(prm.num_blocks) ? blk : 0;
-    const int64_t base = (int64_t(safe) * prm.Hkv + g) * TILE;
+    const int safe = unsigned(blk) < unsigned(num_blocks) ? blk : 0;
+    const int64_t base = (int64_t(safe) * Hkv + g) * TILE;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int q = tid + 256 * j;
@@ -437,7 +424,7 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
       r[j] = load_nt((q < LOADERS ? Kc : Vc) + base + pc * 16);
     }
   };
-  auto lstore = [&](int st, const uint4 (&r)[NLD]) {
+  auto lstore = [&](int st, const uint4 (&r)[NLD], int it) {
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int q = tid + 256 * j;
@@ -445,7 +432,8 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
       if (q < LOADERS) {
         *reinterpret_cast<uint4*>(kst[st] + lrow * KROW + lpc * 16) = r[j];
       } else {
-        const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+        const bool live = !MASK || (jb + it) * BT + lrow < nvalid;
+        const uint32_t w[4] = {live ? r[j].x : 0u, live ? r[j].y : 0u, live ? r[j].z : 0u, live ? r[j].w : 0u};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d = lpc * 8 + 2 * i;
@@ -456,7 +444,8 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
     }
   };
 
-  auto row_block = [&](int st, const half8_t (&qb)[NCH], float4_t (&o)[NDB], float& m, float& l) {
+  auto row_block = [&](int st, int tok0, int lim, const half8_t (&qb)[NCH], float4_t (&o)[NDB], float& m,
+                       float& l) {
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -467,7 +456,8 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
     bool need = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      s[e] = acc[e] * prm.scale_log2;
+      s[e] = acc[e] * scale_log2;
+      if (MASK && tok0 + 4 * lj + e >= lim) s[e] = -INFINITY;
       need |= s[e] > m + LAZY_MAX;
     }
     if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first tile
@@ -499,7 +489,7 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
   __syncthreads();  // block ids
 #pragma unroll
   for (int u = 0; u < PF; ++u) gload(u, ring[u]);
-  lstore(0, ring[0]);
+  lstore(0, ring[0], 0);
   gload(PF, ring[0]);
   __syncthreads();
   // Tile it sits in LDS stage it & 1 and its successor in ring slot
@@ -513,21 +503,52 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
       const int it = it0 + u;
       const int st = u & 1;  // == it & 1: PF is even
       if (it < nt) {
-        if (has0) row_block(st, q0, o0, m0, l0);
-        if (has1) row_block(st, q1, o1, m1, l1);
+        const int tok0 = (jb + it) * BT;
+        if (has0) row_block(st, tok0, lim0, q0, o0, m0, l0);
+        if (has1) row_block(st, tok0, lim1, q1, o1, m1, l1);
       }
-      lstore(st ^ 1, ring[(u + 1) % PF]);
+      lstore(st ^ 1, ring[(u + 1) % PF], it + 1);
       gload(it + 1 + PF, ring[(u + 1) % PF]);
       __syncthreads();
     }
   }
 
-  // the row sums over the four token groups; one partial per row, in slot
-  // `part` of the member's (sequence, query head) partial row
-  auto finish = [&](int rb, float4_t (&o)[NDB], float m, float l) {
-    l += xor_shfl(l, 16);
-    l += xor_shfl(l, 32);
-    const int r = rb * 16 + ln;
+  // the row sums over the four token groups
+  l0 += xor_shfl(l0, 16);
+  l0 += xor_shfl(l0, 32);
+  l1 += xor_shfl(l1, 16);
+  l1 += xor_shfl(l1, 32);
+  if (has0 && rb0 * 16 + ln < R) emit(rb0 * 16 + ln, o0, m0, l0);
+  if (has1 && rb1 * 16 + ln < R) emit(rb1 * 16 + ln, o1, m1, l1);
+}
+
+// The shared-prefix role of a decode work-group: KV head g, partition `part`
+// of group grp's shared blocks. The group's members share their leading
+// blocks ([p1] §三): each K/V tile of the run is read once here and attended
+// by all R = members x G query rows. Shared blocks are full, so nothing is
+// masked. Each row ends as one (m, l, o[D]) partial, written into slot
+// `part` of the member's own partial row, ahead of its split-K partials.
+template <int D, int G>
+__device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int grp, int part) {
+  constexpr int NDB = D / 16;
+  const int lj = (threadIdx.x & 63) >> 4;
+  const int B = gridDim.y, Hq = prm.Hkv * G;
+  const int32_t* gd = prm.plan + 2 * int64_t(B) + int64_t(grp) * PKV_PREFIX_GROUP_INTS;
+  const int np = min(gd[0], prm.max_blocks);
+  const int members = min(gd[1], PKV_MAX_SHARERS);
+  const int R = min(members * G, PREFIX_ROWS);
+  const int b0 = gd[2];
+  if (np <= 0 || R <= 0 || unsigned(b0) >= unsigned(B)) return;
+  const int pbp = prefix_blocks_per_part(np, prm.prefix_pp);  // <= 64: the host sizes prefix_pp
+  const int jb = part * pbp, je = min(np, jb + pbp);
+  if (jb >= je) return;
+  auto member_of = [&](int r) { return r < R ? gd[2 + r / G] : -1; };
+  auto qrow = [&](int r) -> const _Float16* {
+    const int bb = member_of(r);
+    return unsigned(bb) < unsigned(B) ? prm.q + (int64_t(bb) * Hq + g * G + r % G) * D : nullptr;
+  };
+  auto no_limit = [](int) { return 0; };
+  auto emit = [&](int r, const float4_t (&o)[NDB], float m, float l) {
     const int bb = member_of(r);
     if (unsigned(bb) >= unsigned(B)) return;
     const int64_t pi = (int64_t(bb) * Hq + g * G + r % G) * prm.max_parts + part;
@@ -540,8 +561,71 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
       prm.part_l[pi] = l;
     }
   };
-  if (has0) finish(rb0, o0, m0, l0);
-  if (has1) finish(rb1, o1, m1, l1);
+  attend_rows<D, 64, false>(static_cast<const char*>(prm.K), static_cast<const char*>(prm.V), prm.Hkv, g,
+                            prm.num_blocks, prm.tables + int64_t(b0) * prm.max_blocks, jb, je - jb, R, 0,
+                            prm.scale_log2, qrow, no_limit, emit);
+}
+
+// ---------------------------------------------------------------------------
+// paged prefill
+
+// Context a prefill work-group walks: at most 1024 tiles (16384 tokens), its
+// block ids staged in LDS.
+constexpr int PREFILL_MAX_TILES = 1024;
+
+struct PrefillParams {
+  const char* K;  // this layer's K region: [N][Hkv][16][D] fp16
+  const char* V;
+  const _Float16* q;        // [T][Hq][D], sequence-major
+  const int32_t* q_start;   // [B + 1]: sequence b's rows q_start[b] .. q_start[b + 1] - 1
+  const int32_t* tables;    // [B][max_blocks]
+  const int32_t* ctx_lens;  // [B]: cached tokens, the chunk's own included
+  _Float16* out;            // [T][Hq][D]
+  int Hkv, max_blocks, num_blocks, max_context, qtiles;
+  float scale_log2;
+};
+
+// Causal attention of a chunk of new tokens over the paged cache ([p1] §二
+// and [p2] §1.3: the prompt's tokens are processed together; [p1] §四: tiled
+// with an online softmax, same result). One work-group per (KV head g, query
+// tile, sequence b): a query tile is 128 / G consecutive tokens of the chunk,
+// and its rows are (token, query head of the group), so every K/V tile read
+// is attended by 128 query rows on the matrix cores. Token i of sequence b's
+// chunk sits at logical position ctx - qlen + i and sees tokens 0..itself;
+// the work-group walks tiles 0 .. that of its last token, masking per row.
+// Query tiles are dispatched latest first (they walk the most tiles).
+template <int D, int G>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
+  constexpr int NDB = D / 16;
+  constexpr int QT = PREFIX_ROWS / G;  // query tokens per work-group
+  const int g = blockIdx.x, b = blockIdx.z;
+  const int qt = prm.qtiles - 1 - int(blockIdx.y);
+  const int Hq = prm.Hkv * G;
+  const int t0 = prm.q_start[b], ql = prm.q_start[b + 1] - t0;
+  const int n = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
+  const int i0 = qt * QT;
+  if (ql <= 0 || i0 >= ql || ql > n) return;
+  const int cnt = min(QT, ql - i0), R = cnt * G;
+  const int pos0 = n - ql + i0;  // logical position of the tile's first token
+  const int nt = min((pos0 + cnt - 1) / BT + 1, PREFILL_MAX_TILES);
+  const int lj = (threadIdx.x & 63) >> 4;
+  auto qrow = [&](int r) -> const _Float16* {
+    return r < R ? prm.q + (int64_t(t0 + i0 + r / G) * Hq + g * G + r % G) * D : nullptr;
+  };
+  auto limit = [&](int r) { return r < R ? pos0 + r / G + 1 : INT_MAX; };
+  auto emit = [&](int r, const float4_t (&o)[NDB], float, float l) {
+    _Float16* dst = prm.out + (int64_t(t0 + i0 + r / G) * Hq + g * G + r % G) * D + 4 * lj;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+      half4_t h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = (_Float16)(l > 0.0f ? o[i][e] / l : 0.0f);
+      *reinterpret_cast<half4_t*>(dst + 16 * i) = h;
+    }
+  };
+  attend_rows<D, PREFILL_MAX_TILES, true>(prm.K, prm.V, prm.Hkv, g, prm.num_blocks,
+                                          prm.tables + int64_t(b) * prm.max_blocks, 0, nt, R, n, prm.scale_log2,
+                                          qrow, limit, emit);
 }
 
 // One work-group (4 wave64s) per (KV head g, sequence b, partition p), in
@@ -1422,6 +1506,82 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   else
     hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, mg);
   return hip_status(hipGetLastError(), "lse_reduce launch");
+}
+
+int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  int st = pkv::validate_config(a->cfg);
+  if (st != PKV_OK) return st;
+  const pkv_config& c = *a->cfg;
+  if (a->num_seqs < 1 || a->num_seqs > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "num_seqs must be in [1, 65535]");
+  if (!a->q_start_host) return pkv::fail(PKV_ERR_INVALID_ARG, "q_start_host is required");
+  const int32_t* qs = a->q_start_host;
+  if (qs[0] != 0) return pkv::fail(PKV_ERR_INVALID_ARG, "q_start[0] must be 0");
+  int max_ql = 0;
+  for (int b = 0; b < a->num_seqs; ++b) {
+    const int ql = qs[b + 1] - qs[b];
+    if (ql < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "q_start must not decrease (sequence %d)", b);
+    max_ql = std::max(max_ql, ql);
+  }
+  if (max_ql == 0) return PKV_OK;  // no query rows
+  if (!a->pool_dev || !a->q_dev || !a->q_start_dev || !a->block_tables_dev || !a->ctx_lens_dev || !a->out_dev)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+  if (!aligned16(a->pool_dev) || !aligned16(a->q_dev) || !aligned16(a->out_dev))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "pool, q and out must be 16-byte aligned");
+  if (a->layer < 0 || a->layer >= c.num_layers) return pkv::fail(PKV_ERR_INVALID_ARG, "layer %d out of range", a->layer);
+  if (a->num_q_heads < 1 || a->num_q_heads % c.num_kv_heads)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", a->num_q_heads,
+                     c.num_kv_heads);
+  if (c.dtype != PKV_F16) return pkv::fail(PKV_ERR_UNSUPPORTED, "paged prefill reads fp16 pools");
+  if (a->max_blocks < 1 || a->max_context < 1)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks and max_context must be >= 1");
+  if (std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context) > int64_t(PREFILL_MAX_TILES) * BT)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "prefill context above %d tokens", PREFILL_MAX_TILES * BT);
+  const int G = a->num_q_heads / c.num_kv_heads;
+  if (c.num_kv_heads > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
+  if (a->ctx_lens_host) {
+    const int64_t cap = std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context);
+    for (int b = 0; b < a->num_seqs; ++b) {
+      const int32_t n = a->ctx_lens_host[b];
+      if (n < 1 || n > cap)
+        return pkv::fail(PKV_ERR_INVALID_ARG, "context_len[%d] = %d outside [1, %lld]", b, n, (long long)cap);
+      if (qs[b + 1] - qs[b] > n)
+        return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %d: %d query tokens but %d cached", b, qs[b + 1] - qs[b], n);
+    }
+  }
+  typedef void (*fn_t)(PrefillParams);
+  fn_t fn = nullptr;
+  if (c.head_dim == 128) {
+    fn = G == 1 ? prefill_kernel<128, 1> : G == 2 ? prefill_kernel<128, 2> : G == 4 ? prefill_kernel<128, 4>
+       : G == 8 ? prefill_kernel<128, 8> : nullptr;
+  } else if (c.head_dim == 64) {
+    fn = G == 1 ? prefill_kernel<64, 1> : G == 2 ? prefill_kernel<64, 2> : G == 4 ? prefill_kernel<64, 4>
+       : G == 8 ? prefill_kernel<64, 8> : nullptr;
+  }
+  if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", G);
+  const int QT = PREFIX_ROWS / G;
+  const int qtiles = (max_ql + QT - 1) / QT;
+  if (qtiles > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "chunk too long");
+
+  const int64_t layer_bytes = pkv::layer_elems(c) * pkv::elem_bytes(c.dtype);
+  const char* base = static_cast<const char*>(a->pool_dev);
+  PrefillParams prm;
+  prm.K = base + a->layer * layer_bytes;
+  prm.V = base + pkv::region_bytes(c) + a->layer * layer_bytes;
+  prm.q = static_cast<const _Float16*>(a->q_dev);
+  prm.q_start = a->q_start_dev;
+  prm.tables = a->block_tables_dev;
+  prm.ctx_lens = a->ctx_lens_dev;
+  prm.out = static_cast<_Float16*>(a->out_dev);
+  prm.Hkv = c.num_kv_heads;
+  prm.max_blocks = a->max_blocks;
+  prm.num_blocks = c.num_blocks;
+  prm.max_context = a->max_context;
+  prm.qtiles = qtiles;
+  prm.scale_log2 = a->scale * LOG2E;
+  hipLaunchKernelGGL(fn, dim3(c.num_kv_heads, qtiles, a->num_seqs), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     prm);
+  return hip_status(hipGetLastError(), "paged_prefill launch");
 }
 
 int64_t pkv_prefix_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int32_t num_q_heads,

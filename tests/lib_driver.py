@@ -45,6 +45,7 @@ class LibRun:
         self.seq = {}
         self.reserves = []
         self.decodes = []
+        self.prefills = []
         self.churn_log = []
 
     def close(self):
@@ -105,6 +106,8 @@ class LibRun:
                 self._churn(step[1])
             elif kind == "decode":
                 self._decode(step[1], step[2], decode, decode_kw)
+            elif kind == "prefill_attn":
+                self._prefill_attn(step[1], step[2], step[3], decode)
             else:
                 raise ValueError(kind)
         if self.pending is not None:
@@ -183,3 +186,19 @@ class LibRun:
             torch.cuda.synchronize()
             rec["out"] = out.cpu().numpy()
         self.decodes.append(rec)
+
+    def _prefill_attn(self, names, q_lens, q, compute):
+        sids = [self.seq[n] for n in names]
+        max_blocks = max(len(pkv.pkv_seq_block_table(self.handle, s)) for s in sids)
+        tables, lens = pkv.pkv_build_block_tables(self.handle, sids, max_blocks)
+        rec = {"names": list(names), "q_lens": list(q_lens), "tables": tables.copy(), "lens": lens.copy(),
+               "q": q, "out": None}
+        if compute and self.cache is not None:
+            import torch
+            dev = self.cache.device
+            out = self.cache.paged_prefill(torch.from_numpy(np.ascontiguousarray(q)).to(dev), q_lens,
+                                           torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev),
+                                           context_lens_host=lens, scale=self.w.scale)
+            torch.cuda.synchronize()
+            rec["out"] = out.cpu().numpy()
+        self.prefills.append(rec)

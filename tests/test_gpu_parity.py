@@ -578,3 +578,67 @@ def test_shared_prefix_plan_graph_replay_and_determinism():
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().view(np.uint16), rec["out"].view(np.uint16)), r
     lib.close()
+
+
+# ---------------------------------------------------------------------------
+# paged prefill: causal attention of new chunks over the paged cache
+
+def prefill_err(lib, o):
+    errs = []
+    for a, b in zip(lib.prefills, o.prefills):
+        assert a["out"].dtype == np.float16 and np.isfinite(a["out"]).all()
+        errs.append(float(np.abs(a["out"].astype(np.float64) - b["out"]).max()))
+    return max(errs)
+
+
+@pytest.mark.parametrize("seed,cached,chunk,Hq,Hkv,D", [
+    (61, [0, 0, 0], [1, 17, 300], 32, 8, 128),  # fresh prompts; 32 tokens per work-group
+    (62, [5, 100, 1000], [40, 33, 129], 32, 8, 128),  # chunks after cached tokens
+    (63, [0, 31], [200, 64], 16, 2, 128),  # 8 q heads per KV head: 16 tokens per work-group
+    (64, [7, 0], [300, 129], 8, 8, 64),  # MHA, d64: 128 tokens per work-group
+    (65, [0, 16, 3], [77, 64, 0], 4, 2, 64),  # a sequence with an empty chunk
+    (66, [2000], [600], 8, 1, 128),  # MQA after a long cached run
+])
+def test_prefill_matches_oracle(seed, cached, chunk, Hq, Hkv, D):
+    w = workloads.prefill_chunks(seed, cached, chunk, Hq, Hkv, D)
+    lib, o = run_pair(w)
+    check_host_records(lib, o)
+    check_stored_bytes(lib, o)
+    err = prefill_err(lib, o)
+    announce(f"prefill max abs err {err:.3g}")
+    assert err <= F16_TOL
+    lib.close()
+
+
+def test_prefill_long_prompts_and_physical_order():
+    """Two 2048-token prompts (32 q / 8 KV heads, d128) against the oracle,
+    and the same result bit for bit under another physical block order."""
+    outs = []
+    for shuffle in (True, False):
+        w = workloads.prefill_chunks(67, [0, 512], [2048, 1536], 32, 8, 128, shuffle=shuffle)
+        announce(f"prefill 2 x 2048 shuffle={shuffle}")
+        o = OracleRun(w).run(decode=shuffle)
+        lib = LibRun(w, device=DEV, poison=True).run()
+        if shuffle:
+            assert prefill_err(lib, o) <= F16_TOL
+        outs.append((lib.prefills[0]["tables"], lib.prefills[0]["out"]))
+        lib.close()
+    assert not np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1].view(np.uint16), outs[1][1].view(np.uint16))
+
+
+def test_prefill_last_row_equals_decode():
+    """The chunk's last token attends exactly what a decode of it over the
+    same cache attends: the two kernels agree within the fp16 bar."""
+    w = workloads.prefill_chunks(68, [300, 0, 45], [50, 97, 3], 32, 8, 128)
+    announce("prefill last row vs decode")
+    lib = LibRun(w, device=DEV).run()
+    rec = lib.prefills[0]
+    ends = np.cumsum(rec["q_lens"]) - 1
+    qd = torch.from_numpy(np.ascontiguousarray(rec["q"][ends])).to(DEV)
+    out = lib.cache.paged_decode(qd, torch.from_numpy(rec["tables"]).to(DEV), torch.from_numpy(rec["lens"]).to(DEV),
+                                 context_lens_host=rec["lens"], scale=w.scale)
+    torch.cuda.synchronize()
+    diff = float(np.abs(out.cpu().numpy().astype(np.float64) - rec["out"][ends].astype(np.float64)).max())
+    assert diff <= F16_TOL, diff
+    lib.close()

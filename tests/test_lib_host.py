@@ -513,3 +513,49 @@ def test_decode_plan_validated_before_launch():
     bad = plan(members=tuple(range(32)))
     bad[2 * B + 1] = 33  # over 32 members
     assert call(bad) == C.PKV_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="argument checks with placeholder pointers: CPU only")
+def test_prefill_validated_before_launch():
+    C = pkv._capi
+    fake = 1 << 20
+    cfg = pkv.make_config(1, 64, 2, 64)
+    lens = np.array([40, 10], np.int32)
+
+    def call(starts, c=cfg, Hq=4, max_context=64, max_blocks=4, host_lens=True, **kw):
+        st = np.ascontiguousarray(starts, np.int32)
+        a = C.pkv_prefill_args()
+        a.cfg = C.ctypes.pointer(c)
+        a.pool_dev, a.q_dev, a.q_start_dev, a.block_tables_dev, a.ctx_lens_dev, a.out_dev = (fake,) * 6
+        a.layer, a.num_seqs, a.num_q_heads = 0, 2, Hq
+        a.q_start_host = st.ctypes.data_as(C._p_i32)
+        a.max_blocks, a.max_context = max_blocks, max_context
+        a.ctx_lens_host = lens.ctypes.data_as(C._p_i32) if host_lens else None
+        a.scale = 0.125
+        for k, v in kw.items():
+            setattr(a, k, v)
+        with pytest.raises(pkv.PkvError) as e:
+            pkv.pkv_paged_prefill(a, None)
+        return e.value.status
+
+    assert call([1, 2, 3]) == C.PKV_ERR_INVALID_ARG  # must start at 0
+    assert call([0, 5, 3]) == C.PKV_ERR_INVALID_ARG  # decreasing
+    assert call([0, 5, 16]) == C.PKV_ERR_INVALID_ARG  # 11 query tokens, 10 cached
+    assert call([0, 5, 8], q_start_host=None) == C.PKV_ERR_INVALID_ARG
+    assert call([0, 5, 8], q_dev=None) == C.PKV_ERR_INVALID_ARG
+    assert call([0, 5, 8], out_dev=fake + 2) == C.PKV_ERR_INVALID_ARG
+    assert call([0, 5, 8], layer=1) == C.PKV_ERR_INVALID_ARG
+    assert call([0, 5, 8], Hq=6) == C.PKV_ERR_UNSUPPORTED  # 3 q heads per KV head
+    assert call([0, 5, 8], Hq=5) == C.PKV_ERR_INVALID_ARG
+    assert call([0, 5, 8], c=pkv.make_config(1, 64, 2, 64, "i8")) == C.PKV_ERR_UNSUPPORTED
+    assert call([0, 5, 8], max_context=20000, max_blocks=2000, host_lens=False) == C.PKV_ERR_UNSUPPORTED
+    lens[0] = 0
+    assert call([0, 0, 8]) == C.PKV_ERR_INVALID_ARG  # a context of 0 tokens
+    lens[0] = 40
+    # no query rows at all: nothing to do, nothing launched
+    st = np.zeros(3, np.int32)
+    a = C.pkv_prefill_args()
+    a.cfg = C.ctypes.pointer(cfg)
+    a.num_seqs, a.num_q_heads = 2, 4
+    a.q_start_host = st.ctypes.data_as(C._p_i32)
+    pkv.pkv_paged_prefill(a, None)
