@@ -347,23 +347,24 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 // and V rows of tokens at or past nvalid (slots never written) are staged
 // as zeros, so a masked weight of 0 never meets a stale NaN.
 // Tiles jb .. jb + nt - 1 of `trow` (nt <= MAXT, their block ids staged in
-// LDS). emit(r, o, m, l) receives row r's unnormalised output, lane
-// (n, j) holding dims 16 i + 4 j + e of row 16 rb + n, with the row's
-// base-2 running max m and its sum l.
+// LDS), taken two at a time (a step of 32 tokens). emit(r, o, m, l)
+// receives row r's unnormalised output, lane (n, j) holding dims
+// 16 i + 4 j + e of row 16 rb + n, with the row's base-2 running max m and
+// its sum l.
 //
-// Per tile and row block:
-//   S^T (16 tokens x 16 rows) = K (16 x D) . Q^T (D x 16),
-//       v_mfma_f32_16x16x32_f16 over D/32 chunks: lane (n, j) receives
-//       tokens 4j..4j+3 of query row n;
-//   O^T (D x 16 rows) += V^T (D x 16 tokens) . P^T (16 tokens x 16 rows),
-//       v_mfma_f32_16x16x16_f16 per 16 dims, whose B operand (tokens
-//       4j..4j+3 of row n in lane (n, j)) is exactly the layout the scores
-//       arrive in: the probabilities go from one MFMA to the next without
-//       moving between lanes.
-// K tiles are staged in LDS row-major (rows padded by 16 bytes), V tiles
-// transposed ([dim][token]) so each lane reads its 4 tokens of one dim as 8
-// contiguous bytes. Online softmax per row in base 2 with the lazy running
-// max of the split kernel.
+// Per step and row block:
+//   S^T (16 tokens x 16 rows) = K (16 x D) . Q^T (D x 16) for each of the
+//       two tiles, v_mfma_f32_16x16x32_f16 over D/32 chunks: lane (n, j)
+//       receives tokens 4j..4j+3 of query row n from each tile;
+//   O^T (D x 16 rows) += V^T (D x 32 tokens) . P^T (32 tokens x 16 rows),
+//       one v_mfma_f32_16x16x32_f16 per 16 dims. The contraction's k slots
+//       8j..8j+7 of lane (n, j) are tokens 4j..4j+3 of the first tile and
+//       then of the second: exactly the scores the lane holds, so P goes from
+//       one MFMA to the next without moving between lanes, and V^T is
+//       staged in LDS with its 32 token columns in that same order.
+// K tiles are staged in LDS row-major (rows padded by 16 bytes); each V
+// row is scattered into its column of V^T. Online softmax per row in base 2
+// with the lazy running max of the split kernel.
 template <int D, int MAXT, bool MASK, typename QRow, typename Limit, typename Emit>
 __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int Hkv, int g, int num_blocks,
                                             const int32_t* trow, int jb, int nt, int R, int nvalid,
@@ -371,13 +372,13 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   constexpr int NCH = D / 32;           // score MFMA chunks
   constexpr int NDB = D / 16;           // value MFMA dim blocks
   constexpr int KROW = D * 2 + 16;      // bytes per staged K row
-  constexpr int VTROW = BT * 2 + 8;     // bytes per staged V^T row (16 tokens)
+  constexpr int VTROW = 2 * BT * 2 + 16;  // bytes per staged V^T row (32 tokens)
   constexpr int PIECES = D / 8;         // 16-byte pieces per K/V row
   constexpr int LOADERS = BT * PIECES;  // pieces per K (or V) tile
   constexpr int TILE = BT * D * 2;
-  constexpr int PF = 4;                 // tiles in flight per thread
-  static_assert(PF % 2 == 0, "LDS stages alternate with the ring slot");
-  __shared__ __align__(16) char kst[2][BT * KROW];
+  constexpr int PFS = 2;                // steps (tile pairs) in flight per thread
+  static_assert(PFS % 2 == 0, "LDS stages alternate with the ring slot");
+  __shared__ __align__(16) char kst[2][2][BT * KROW];
   __shared__ __align__(16) char vst[2][D * VTROW];
   __shared__ int blk_ids[MAXT];
 
@@ -385,6 +386,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lj = lane >> 4;
   for (int i = tid; i < nt; i += 256) blk_ids[i] = trow[jb + i];
+  const int nsteps = (nt + 1) / 2;
 
   // q^T as the B operand of the score MFMA, per row block of this wave
   const int rb0 = wave, rb1 = wave + 4;
@@ -408,60 +410,94 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.0f, l1 = 0.0f;
 
   // Tile staging: a tile is 2 x LOADERS 16-byte pieces (K, then V); thread
-  // t moves pieces t + 256 j. Tiles are fetched PF ahead into a register
-  // ring; the loads are unconditional (indices past the last tile re-read
+  // t moves pieces t + 256 j. K pieces run along a row (16-byte LDS stores
+  // without conflicts), V pieces down the 16 tokens (their 2-byte scatter
+  // into V^T then spreads over the banks). Steps are fetched PFS ahead into
+  // a register ring; the loads are unconditional (tiles past the last re-read
   // it) so the compiler counts outstanding loads statically.
   constexpr int NLD = 2 * LOADERS / 256;
-  uint4 ring[PF][NLD];
-  auto gload = [&](int it, uint4 (&r)[NLD]) {
-    const int blk = blk_ids[min(it, nt - 1)];
-    const int safe = unsigned(blk) < unsigned(num_blocks) ? blk : 0;
-    const int64_t base = (int64_t(safe) * Hkv + g) * TILE;
-#pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int q = tid + 256 * j;
-      const int pc = q % LOADERS;
-      r[j] = load_nt((q < LOADERS ? Kc : Vc) + base + pc * 16);
+  uint4 ring[PFS][2][NLD];
+  auto piece = [&](int q, int& lrow, int& lpc) {
+    const int pc = q % LOADERS;
+    if (q < LOADERS) {
+      lrow = pc / PIECES;
+      lpc = pc % PIECES;
+    } else {
+      lrow = pc % BT;
+      lpc = pc / BT;
     }
   };
-  auto lstore = [&](int st, const uint4 (&r)[NLD], int it) {
+  auto gload = [&](int step, uint4 (&r)[2][NLD]) {
 #pragma unroll
-    for (int j = 0; j < NLD; ++j) {
-      const int q = tid + 256 * j;
-      const int pc = q % LOADERS, lrow = pc / PIECES, lpc = pc % PIECES;
-      if (q < LOADERS) {
-        *reinterpret_cast<uint4*>(kst[st] + lrow * KROW + lpc * 16) = r[j];
-      } else {
-        const bool live = !MASK || (jb + it) * BT + lrow < nvalid;
-        const uint32_t w[4] = {live ? r[j].x : 0u, live ? r[j].y : 0u, live ? r[j].z : 0u, live ? r[j].w : 0u};
+    for (int sub = 0; sub < 2; ++sub) {
+      const int blk = blk_ids[min(2 * step + sub, nt - 1)];
+      const int safe = unsigned(blk) < unsigned(num_blocks) ? blk : 0;
+      const int64_t base = (int64_t(safe) * Hkv + g) * TILE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = lpc * 8 + 2 * i;
-          *reinterpret_cast<uint16_t*>(vst[st] + d * VTROW + lrow * 2) = uint16_t(w[i] & 0xFFFFu);
-          *reinterpret_cast<uint16_t*>(vst[st] + (d + 1) * VTROW + lrow * 2) = uint16_t(w[i] >> 16);
+      for (int j = 0; j < NLD; ++j) {
+        const int q = tid + 256 * j;
+        int lrow, lpc;
+        piece(q, lrow, lpc);
+        r[sub][j] = load_nt((q < LOADERS ? Kc : Vc) + base + lrow * (D * 2) + lpc * 16);
+      }
+    }
+  };
+  auto lstore = [&](int st, const uint4 (&r)[2][NLD], int step) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int q = tid + 256 * j;
+        int lrow, lpc;
+        piece(q, lrow, lpc);
+        if (q < LOADERS) {
+          *reinterpret_cast<uint4*>(kst[st][sub] + lrow * KROW + lpc * 16) = r[sub][j];
+        } else {
+          const bool live = !MASK || (jb + 2 * step + sub) * BT + lrow < nvalid;
+          const uint32_t w[4] = {live ? r[sub][j].x : 0u, live ? r[sub][j].y : 0u, live ? r[sub][j].z : 0u,
+                                 live ? r[sub][j].w : 0u};
+          const int col = (lrow >> 2) * 8 + sub * 4 + (lrow & 3);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = lpc * 8 + 2 * i;
+            *reinterpret_cast<uint16_t*>(vst[st] + d * VTROW + col * 2) = uint16_t(w[i] & 0xFFFFu);
+            *reinterpret_cast<uint16_t*>(vst[st] + (d + 1) * VTROW + col * 2) = uint16_t(w[i] >> 16);
+          }
         }
       }
     }
   };
 
-  auto row_block = [&](int st, int tok0, int lim, const half8_t (&qb)[NCH], float4_t (&o)[NDB], float& m,
+  auto row_block = [&](int st, int step, int lim, const half8_t (&qb)[NCH], float4_t (&o)[NDB], float& m,
                        float& l) {
-    float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float4_t acc[2];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const half8_t ka = *reinterpret_cast<const half8_t*>(kst[st] + ln * KROW + (32 * c + 8 * lj) * 2);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[c], acc, 0, 0, 0);
+    for (int sub = 0; sub < 2; ++sub) {
+      acc[sub] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const half8_t ka = *reinterpret_cast<const half8_t*>(kst[st][sub] + ln * KROW + (32 * c + 8 * lj) * 2);
+        acc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[c], acc[sub], 0, 0, 0);
+      }
     }
-    float s[4];
+    float s[8];
     bool need = false;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s[e] = acc[e] * scale_log2;
-      if (MASK && tok0 + 4 * lj + e >= lim) s[e] = -INFINITY;
-      need |= s[e] > m + LAZY_MAX;
+    for (int sub = 0; sub < 2; ++sub) {
+      const int tile = 2 * step + sub;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = acc[sub][e] * scale_log2;
+        if (tile >= nt) x = -INFINITY;  // the odd tail's stand-in tile
+        if (MASK && (jb + tile) * BT + 4 * lj + e >= lim) x = -INFINITY;
+        s[sub * 4 + e] = x;
+        need |= x > m + LAZY_MAX;
+      }
     }
-    if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first tile
-      float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first step
+      float mx = s[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, s[k]);
       mx = fmaxf(mx, xor_shfl(mx, 16));
       mx = fmaxf(mx, xor_shfl(mx, 32));
       const float mn = fmaxf(m, mx);
@@ -473,42 +509,41 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
     }
     // probabilities enter the value MFMA in fp16; the row sum adds the same
     // rounded values, so weights and normaliser agree
-    half4_t pt;
+    half8_t pt;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pt[e] = (_Float16)exp2_fast(s[e] - m);
-      l += float(pt[e]);
+    for (int k = 0; k < 8; ++k) {
+      pt[k] = (_Float16)exp2_fast(s[k] - m);
+      l += float(pt[k]);
     }
 #pragma unroll
     for (int i = 0; i < NDB; ++i) {
-      const half4_t va = *reinterpret_cast<const half4_t*>(vst[st] + (16 * i + ln) * VTROW + lj * 8);
-      o[i] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pt, o[i], 0, 0, 0);
+      const half8_t va = *reinterpret_cast<const half8_t*>(vst[st] + (16 * i + ln) * VTROW + lj * 16);
+      o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt, o[i], 0, 0, 0);
     }
   };
 
   __syncthreads();  // block ids
 #pragma unroll
-  for (int u = 0; u < PF; ++u) gload(u, ring[u]);
+  for (int u = 0; u < PFS; ++u) gload(u, ring[u]);
   lstore(0, ring[0], 0);
-  gload(PF, ring[0]);
+  gload(PFS, ring[0]);
   __syncthreads();
-  // Tile it sits in LDS stage it & 1 and its successor in ring slot
-  // (it + 1) % PF. The loop runs whole rounds of PF (unrolled, so every slot
-  // index is a constant); past the last tile only the math is skipped: loads
-  // and stores stay unconditional, and the compiler's count of loads in
-  // flight stays exact across the loop.
-  for (int it0 = 0; it0 < nt; it0 += PF) {
+  // Step it sits in LDS stage it & 1 and its successor in ring slot
+  // (it + 1) % PFS. The loop runs whole rounds of PFS (unrolled, so every
+  // slot index is a constant); past the last step only the math is skipped:
+  // loads and stores stay unconditional, and the compiler's count of loads
+  // in flight stays exact across the loop.
+  for (int it0 = 0; it0 < nsteps; it0 += PFS) {
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int u = 0; u < PFS; ++u) {
       const int it = it0 + u;
-      const int st = u & 1;  // == it & 1: PF is even
-      if (it < nt) {
-        const int tok0 = (jb + it) * BT;
-        if (has0) row_block(st, tok0, lim0, q0, o0, m0, l0);
-        if (has1) row_block(st, tok0, lim1, q1, o1, m1, l1);
+      const int st = u & 1;  // == it & 1: PFS is even
+      if (it < nsteps) {
+        if (has0) row_block(st, it, lim0, q0, o0, m0, l0);
+        if (has1) row_block(st, it, lim1, q1, o1, m1, l1);
       }
-      lstore(st ^ 1, ring[(u + 1) % PF], it + 1);
-      gload(it + 1 + PF, ring[(u + 1) % PF]);
+      lstore(st ^ 1, ring[(u + 1) % PFS], it + 1);
+      gload(it + 1 + PFS, ring[(u + 1) % PFS]);
       __syncthreads();
     }
   }
