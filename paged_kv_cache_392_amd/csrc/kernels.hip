@@ -81,6 +81,14 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Non-temporal for data read once (decode), cached for data re-read (prefill).
+template <bool STREAM>
+__device__ __forceinline__ uint4 load_tile(const void* p) {
+  if constexpr (STREAM) return load_nt(p);
+  const u32x4 v = *static_cast<const u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float lo_half(uint32_t w) {
   return float(__builtin_bit_cast(half2_t, w).x);
 }
@@ -337,17 +345,21 @@ __device__ __forceinline__ void seq_prefix(const int32_t* plan, int b, int max_b
 }
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
 
 // Attention of up to 128 query rows over consecutive tiles of one block
 // table, by a work-group of 4 waves on the matrix cores: the shared-prefix
 // work-groups of the decode and the paged prefill both run it. Rows come in
 // 16-row blocks (wave w takes blocks w and w + 4); row r's q is at qrow(r)
 // (null: a padding row, never emitted). With MASK, row r sees logical
-// tokens below limit(r) only (padding rows must not be masked entirely),
+// tokens below limit(r) only (padding rows must not be masked entirely;
+// every limit must be at least full_tokens, below which no row is masked),
 // and V rows of tokens at or past nvalid (slots never written) are staged
 // as zeros, so a masked weight of 0 never meets a stale NaN.
 // Tiles jb .. jb + nt - 1 of `trow` (nt <= MAXT, their block ids staged in
-// LDS), taken two at a time (a step of 32 tokens). emit(r, o, m, l)
+// LDS), taken two at a time (a step of 32 tokens). STREAM: tiles are read
+// once (non-temporal loads); otherwise other work-groups re-read them, and
+// ordinary loads keep them in L2. emit(r, o, m, l)
 // receives row r's unnormalised output, lane (n, j) holding dims
 // 16 i + 4 j + e of row 16 rb + n, with the row's base-2 running max m and
 // its sum l.
@@ -360,26 +372,30 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 //       one v_mfma_f32_16x16x32_f16 per 16 dims. The contraction's k slots
 //       8j..8j+7 of lane (n, j) are tokens 4j..4j+3 of the first tile and
 //       then of the second: exactly the scores the lane holds, so P goes from
-//       one MFMA to the next without moving between lanes, and V^T is
-//       staged in LDS with its 32 token columns in that same order.
-// K tiles are staged in LDS row-major (rows padded by 16 bytes); each V
-// row is scattered into its column of V^T. Online softmax per row in base 2
-// with the lazy running max of the split kernel.
-template <int D, int MAXT, bool MASK, typename QRow, typename Limit, typename Emit>
+//       one MFMA to the next without moving between lanes.
+// K and V tiles are both staged in LDS row-major (rows padded by 16 bytes,
+// 16-byte stores). The V^T operand comes from the LDS transpose read
+// ds_read_b64_tr_b16: within each 16-lane group, lane s addresses 4
+// halves and lane i receives element i % 4 of lanes i/4, 4 + i/4, 8 + i/4
+// and 12 + i/4 (checked on gfx950 with a one-wave probe). With lane s of
+// group j pointing at V[4j + s/4][16 i + 4 (s % 4)], lane (n, j) receives
+// V[4j..4j+3][16 i + n]: the A operand, 4 tokens of one dim. Online
+// softmax per row in base 2 with the lazy running max of the split kernel.
+template <int D, int MAXT, bool MASK, bool STREAM, typename QRow, typename Limit, typename Emit>
 __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int Hkv, int g, int num_blocks,
                                             const int32_t* trow, int jb, int nt, int R, int nvalid,
-                                            float scale_log2, QRow qrow, Limit limit, Emit emit) {
+                                            int full_tokens, float scale_log2, QRow qrow, Limit limit,
+                                            Emit emit) {
   constexpr int NCH = D / 32;           // score MFMA chunks
   constexpr int NDB = D / 16;           // value MFMA dim blocks
   constexpr int KROW = D * 2 + 16;      // bytes per staged K row
-  constexpr int VTROW = 2 * BT * 2 + 16;  // bytes per staged V^T row (32 tokens)
   constexpr int PIECES = D / 8;         // 16-byte pieces per K/V row
   constexpr int LOADERS = BT * PIECES;  // pieces per K (or V) tile
   constexpr int TILE = BT * D * 2;
   constexpr int PFS = 2;                // steps (tile pairs) in flight per thread
   static_assert(PFS % 2 == 0, "LDS stages alternate with the ring slot");
   __shared__ __align__(16) char kst[2][2][BT * KROW];
-  __shared__ __align__(16) char vst[2][D * VTROW];
+  __shared__ __align__(16) char vst[2][2][BT * KROW];
   __shared__ int blk_ids[MAXT];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -397,8 +413,8 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
     for (int c = 0; c < NCH; ++c) qb[c] = qp ? *reinterpret_cast<const half8_t*>(qp + 32 * c + 8 * lj) : half8_t{};
   };
   half8_t q0[NCH], q1[NCH];
-  if (has0) load_q(rb0, q0);
-  if (has1) load_q(rb1, q1);
+  load_q(rb0, q0);
+  load_q(rb1, q1);
   const int lim0 = MASK ? limit(rb0 * 16 + ln) : 0, lim1 = MASK ? limit(rb1 * 16 + ln) : 0;
 
   float4_t o0[NDB], o1[NDB];
@@ -409,23 +425,16 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   }
   float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.0f, l1 = 0.0f;
 
-  // Tile staging: a tile is 2 x LOADERS 16-byte pieces (K, then V); thread
-  // t moves pieces t + 256 j. K pieces run along a row (16-byte LDS stores
-  // without conflicts), V pieces down the 16 tokens (their 2-byte scatter
-  // into V^T then spreads over the banks). Steps are fetched PFS ahead into
-  // a register ring; the loads are unconditional (tiles past the last re-read
-  // it) so the compiler counts outstanding loads statically.
+  // Tile staging: a tile is 2 x LOADERS 16-byte pieces (K, then V), each
+  // piece along a row; thread t moves pieces t + 256 j. Steps are fetched
+  // PFS ahead into a register ring; the loads are unconditional (tiles past
+  // the last re-read it) so the compiler counts outstanding loads statically.
   constexpr int NLD = 2 * LOADERS / 256;
   uint4 ring[PFS][2][NLD];
   auto piece = [&](int q, int& lrow, int& lpc) {
     const int pc = q % LOADERS;
-    if (q < LOADERS) {
-      lrow = pc / PIECES;
-      lpc = pc % PIECES;
-    } else {
-      lrow = pc % BT;
-      lpc = pc / BT;
-    }
+    lrow = pc / PIECES;
+    lpc = pc % PIECES;
   };
   auto gload = [&](int step, uint4 (&r)[2][NLD]) {
 #pragma unroll
@@ -438,7 +447,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
         const int q = tid + 256 * j;
         int lrow, lpc;
         piece(q, lrow, lpc);
-        r[sub][j] = load_nt((q < LOADERS ? Kc : Vc) + base + lrow * (D * 2) + lpc * 16);
+        r[sub][j] = load_tile<STREAM>((q < LOADERS ? Kc : Vc) + base + lrow * (D * 2) + lpc * 16);
       }
     }
   };
@@ -454,50 +463,40 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
           *reinterpret_cast<uint4*>(kst[st][sub] + lrow * KROW + lpc * 16) = r[sub][j];
         } else {
           const bool live = !MASK || (jb + 2 * step + sub) * BT + lrow < nvalid;
-          const uint32_t w[4] = {live ? r[sub][j].x : 0u, live ? r[sub][j].y : 0u, live ? r[sub][j].z : 0u,
-                                 live ? r[sub][j].w : 0u};
-          const int col = (lrow >> 2) * 8 + sub * 4 + (lrow & 3);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int d = lpc * 8 + 2 * i;
-            *reinterpret_cast<uint16_t*>(vst[st] + d * VTROW + col * 2) = uint16_t(w[i] & 0xFFFFu);
-            *reinterpret_cast<uint16_t*>(vst[st] + (d + 1) * VTROW + col * 2) = uint16_t(w[i] >> 16);
-          }
+          *reinterpret_cast<uint4*>(vst[st][sub] + lrow * KROW + lpc * 16) =
+              live ? r[sub][j] : make_uint4(0u, 0u, 0u, 0u);
         }
       }
     }
   };
 
-  auto row_block = [&](int st, int step, int lim, const half8_t (&qb)[NCH], float4_t (&o)[NDB], float& m,
-                       float& l) {
-    float4_t acc[2];
+  // Online softmax of one row block's scores of a step (two tiles), kept
+  // short because the VALU, not the matrix cores, sets this loop's pace:
+  // masking only on `masked` steps (the diagonal and the odd tail, a
+  // wave-uniform choice); the lazy-max test on the raw scores' maximum;
+  // one FMA into each exponential; row sums of the fp16 probabilities by
+  // v_dot2 against ones. Returns P in the value MFMA's k-slot order.
+  auto softmax = [&](const float4_t (&acc)[2], int step, int lim, bool masked, float4_t (&o)[NDB], float& m,
+                     float& l) {
+    float a[8];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      acc[sub] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const half8_t ka = *reinterpret_cast<const half8_t*>(kst[st][sub] + ln * KROW + (32 * c + 8 * lj) * 2);
-        acc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[c], acc[sub], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) a[sub * 4 + e] = acc[sub][e];
+    if (masked) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int tile = 2 * step + sub;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool out = tile >= nt || (MASK && (jb + tile) * BT + 4 * lj + e >= lim);
+          a[sub * 4 + e] = out ? -INFINITY : a[sub * 4 + e];
+        }
       }
     }
-    float s[8];
-    bool need = false;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int tile = 2 * step + sub;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = acc[sub][e] * scale_log2;
-        if (tile >= nt) x = -INFINITY;  // the odd tail's stand-in tile
-        if (MASK && (jb + tile) * BT + 4 * lj + e >= lim) x = -INFINITY;
-        s[sub * 4 + e] = x;
-        need |= x > m + LAZY_MAX;
-      }
-    }
-    if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first step
-      float mx = s[0];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) mx = fmaxf(mx, s[k]);
+    const float amax = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+    if (__builtin_amdgcn_ballot_w64(amax * scale_log2 > m + LAZY_MAX)) {  // wave-uniform, rare after the first step
+      float mx = amax * scale_log2;
       mx = fmaxf(mx, xor_shfl(mx, 16));
       mx = fmaxf(mx, xor_shfl(mx, 32));
       const float mn = fmaxf(m, mx);
@@ -509,16 +508,52 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
     }
     // probabilities enter the value MFMA in fp16; the row sum adds the same
     // rounded values, so weights and normaliser agree
+    const float nm = -m;
     half8_t pt;
+    const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pt[k] = (_Float16)exp2_fast(s[k] - m);
-      l += float(pt[k]);
+    for (int k = 0; k < 8; k += 2) {
+      const half2_t pp = {(_Float16)exp2_fast(__builtin_fmaf(a[k], scale_log2, nm)),
+                          (_Float16)exp2_fast(__builtin_fmaf(a[k + 1], scale_log2, nm))};
+      pt[k] = pp.x;
+      pt[k + 1] = pp.y;
+      l = __builtin_amdgcn_fdot2(pp, ones, l, false);
     }
+    return pt;
+  };
+
+  // One step for both row blocks of the wave: every K and V fragment is
+  // read from LDS once and used by both. Both blocks are always computed
+  // (rows past R have zero q and are never emitted): guards around single
+  // MFMAs would become branches that split the scheduling regions.
+  auto step_rows = [&](int st, int step) {
+    float4_t acc0[2], acc1[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      acc0[sub] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      acc1[sub] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const half8_t ka = *reinterpret_cast<const half8_t*>(kst[st][sub] + ln * KROW + (32 * c + 8 * lj) * 2);
+        acc0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q0[c], acc0[sub], 0, 0, 0);
+        acc1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q1[c], acc1[sub], 0, 0, 0);
+      }
+    }
+    // tokens below full_tokens are visible to every row: no mask before them
+    const bool masked = 2 * step + 1 >= nt || (MASK && (jb + 2 * step + 2) * BT > full_tokens);
+    const half8_t pt0 = softmax(acc0, step, lim0, masked, o0, m0, l0);
+    const half8_t pt1 = softmax(acc1, step, lim1, masked, o1, m1, l1);
+    // lane (n, j) addresses V[4j + n/4][16 i + 4 (n % 4)] of each tile
+    const int vofs = (4 * lj + (ln >> 2)) * KROW + (ln & 3) * 8;
 #pragma unroll
     for (int i = 0; i < NDB; ++i) {
-      const half8_t va = *reinterpret_cast<const half8_t*>(vst[st] + (16 * i + ln) * VTROW + lj * 16);
-      o[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt, o[i], 0, 0, 0);
+      const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4_t*)(vst[st][0] + vofs + 32 * i));
+      const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) short4_t*)(vst[st][1] + vofs + 32 * i));
+      const half8_t va = __builtin_bit_cast(half8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      o0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt0, o0[i], 0, 0, 0);
+      o1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt1, o1[i], 0, 0, 0);
     }
   };
 
@@ -538,10 +573,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
     for (int u = 0; u < PFS; ++u) {
       const int it = it0 + u;
       const int st = u & 1;  // == it & 1: PFS is even
-      if (it < nsteps) {
-        if (has0) row_block(st, it, lim0, q0, o0, m0, l0);
-        if (has1) row_block(st, it, lim1, q1, o1, m1, l1);
-      }
+      if (it < nsteps) step_rows(st, it);
       lstore(st ^ 1, ring[(u + 1) % PFS], it + 1);
       gload(it + 1 + PFS, ring[(u + 1) % PFS]);
       __syncthreads();
@@ -596,8 +628,8 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
       prm.part_l[pi] = l;
     }
   };
-  attend_rows<D, 64, false>(static_cast<const char*>(prm.K), static_cast<const char*>(prm.V), prm.Hkv, g,
-                            prm.num_blocks, prm.tables + int64_t(b0) * prm.max_blocks, jb, je - jb, R, 0,
+  attend_rows<D, 64, false, true>(static_cast<const char*>(prm.K), static_cast<const char*>(prm.V), prm.Hkv, g,
+                            prm.num_blocks, prm.tables + int64_t(b0) * prm.max_blocks, jb, je - jb, R, 0, 0,
                             prm.scale_log2, qrow, no_limit, emit);
 }
 
@@ -658,11 +690,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
       *reinterpret_cast<half4_t*>(dst + 16 * i) = h;
     }
   };
-  attend_rows<D, PREFILL_MAX_TILES, true>(prm.K, prm.V, prm.Hkv, g, prm.num_blocks,
-                                          prm.tables + int64_t(b) * prm.max_blocks, 0, nt, R, n, prm.scale_log2,
-                                          qrow, limit, emit);
+  attend_rows<D, PREFILL_MAX_TILES, true, false>(prm.K, prm.V, prm.Hkv, g, prm.num_blocks,
+                                          prm.tables + int64_t(b) * prm.max_blocks, 0, nt, R, n, pos0 + 1,
+                                          prm.scale_log2, qrow, limit, emit);
 }
 
+// Two work-groups per CU are asked of the register allocator where they
+// fit without spills (G <= 4; fp16 at D = 64): the shared-prefix role would
+// otherwise push the fp16 kernels past 256 registers a lane. The other
+// G = 8 kernels keep the full register file.
+//
 // One work-group (4 wave64s) per (KV head g, sequence b, partition p), in
 // that grid order (x, y, z). Work-groups go to the eight XCDs round-robin by
 // linear id, so the partition index, the dimension along which work runs out
@@ -681,7 +718,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
 // query head for the merge kernel, or the final fp16 row when the sequence
 // has a single partition.
 template <int D, int G, bool I8>
-__global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams prm) {
+__global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void paged_decode_kernel(DecodeParams prm) {
   using S = Shape<D, G, I8>;
   const int g = blockIdx.x, b = blockIdx.y;
   // With a shared-prefix plan the first prefix_z planes of the grid are
