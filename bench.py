@@ -33,6 +33,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, 8 TB/s
+PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 B, HQ, HKV, D, CTX = 16, 32, 8, 128, 8192
 
 
@@ -49,11 +50,12 @@ def parse():
                     help="launch every layer directly instead of replaying layers 1.. as one HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--workload", choices=["headline", "c5", "prefix"], default="headline",
+    ap.add_argument("--workload", choices=["headline", "c5", "prefix", "prefill"], default="headline",
                     help="headline: the fp16 batch-16 8K decode step (the bench line); c5: the int8 "
                          "batch-16 8K decode-only step over 32 int8 layer pools; prefix: the decode step "
                          "of 32 sequences sharing a 2048-token prefix, with and without the shared-prefix "
-                         "plan (timing and profiling; parity is covered by the GPU tests)")
+                         "plan; prefill: 4 prompts of 2048 tokens appended and attended causally over 32 "
+                         "layer pools (timing and profiling; parity is covered by the GPU tests)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -121,6 +123,9 @@ def main():
         return
     if args.workload == "prefix":
         prefix_decode_bench(args, torch, pkv, C, workloads)
+        return
+    if args.workload == "prefill":
+        prefill_bench(args, torch, pkv, C, workloads)
         return
 
     dev = torch.device("cuda:0")
@@ -663,6 +668,98 @@ def prefix_decode_bench(args, torch, pkv, C, workloads):
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
                      "bytes_per_launch": int(unique_bytes)},
+        "cpu_baseline": None,
+    }), flush=True)
+
+
+def prefill_bench(args, torch, pkv, C, workloads):
+    """Prefill step: 4 fresh prompts of 2048 tokens, 32 q / 8 KV heads, d128,
+    fp16, over 32 layer pools. Per layer the prompts' K/V rows are appended
+    into their blocks (one bulk append of 8192 tokens) and attended
+    causally (one prefill launch). The blocks come from the library's
+    allocator in a seeded random order; K, V and q are seeded device noise
+    (values do not change the timing). The prefill launch of layer 0 is
+    bracketed by HIP events in every timed step."""
+    dev = torch.device("cuda:0")
+    K, W, L = args.steps, args.warmup, args.layers
+    Bp, T = 4, 2048
+    nblk = T // 16
+    N = Bp * nblk
+    order = np.random.default_rng(7).permutation(N).astype(np.int32)
+    cache = pkv.PagedKVCache(L, N, HKV, D, "f16", order, dev)
+    lib = C.load()
+    sp = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    seqs = [cache.create_seq() for _ in range(Bp)]
+    slots, _ = cache.reserve(seqs, [T] * Bp)
+    slots_d = torch.from_numpy(slots).to(dev)
+    tables_h, lens_h = cache.block_tables(seqs, nblk)
+    tables_d = torch.from_numpy(tables_h).to(dev)
+    lens_d = torch.from_numpy(lens_h).to(dev)
+    starts_h = (np.arange(Bp + 1) * T).astype(np.int32)
+    starts_d = torch.from_numpy(starts_h).to(dev)
+    kv = torch.empty((2, L, Bp * T, HKV, D), dtype=torch.float16, device=dev).normal_(generator=gen)
+    q = torch.empty((L, Bp * T, HQ, D), dtype=torch.float16, device=dev).normal_(generator=gen)
+    out = torch.empty_like(q)
+    argv = []
+    for layer in range(L):
+        a = C.pkv_prefill_args()
+        a.cfg = ctypes.pointer(cache.cfg)
+        a.pool_dev = cache.pool.data_ptr()
+        a.layer = layer
+        a.q_dev = q[layer].data_ptr()
+        a.num_seqs = Bp
+        a.num_q_heads = HQ
+        a.q_start_dev = starts_d.data_ptr()
+        a.q_start_host = C._i32p(starts_h)
+        a.block_tables_dev = tables_d.data_ptr()
+        a.max_blocks = nblk
+        a.ctx_lens_dev = lens_d.data_ptr()
+        a.ctx_lens_host = C._i32p(lens_h)
+        a.max_context = T
+        a.out_dev = out[layer].data_ptr()
+        a.scale = 1.0 / math.sqrt(D)
+        argv.append(a)
+
+    def step(ev=None):
+        for layer in range(L):
+            C._check(lib.pkv_append_kv(ctypes.byref(cache.cfg), cache.pool.data_ptr(), layer, kv[0, layer].data_ptr(),
+                                       kv[1, layer].data_ptr(), slots_d.data_ptr(), Bp * T, sp))
+            if layer == 0 and ev is not None:
+                ev[0].record()
+            C._check(lib.pkv_paged_prefill(ctypes.byref(argv[layer]), sp))
+            if layer == 0 and ev is not None:
+                ev[1].record()
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(K):
+        step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    pre = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3
+    flops = 4.0 * HQ * D * Bp * (T * (T + 1) / 2)
+    achieved = flops / (float(np.mean(pre)) * 1e-6) / 1e12
+    print(json.dumps({
+        "metric": "paged prefill tokens/s (4 x 2048-token prompts, causal, 32q/8kv d128 fp16)",
+        "value": round(Bp * T / (ms * 1e-3), 1), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"prefill step: {Bp} fresh prompts of {T} tokens appended into 16-token blocks "
+                               f"and attended causally, 32 q / 8 KV heads, head_dim 128, fp16, {L} layer pools",
+                   "layers": L},
+        "prefill_kernel_us": round(float(np.mean(pre)), 2),
+        "prefill_kernel_us_p10_p90": [round(float(np.percentile(pre, 10)), 2), round(float(np.percentile(pre, 90)), 2)],
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,4> (causal paged prefill)",
+                     "achieved": round(achieved, 1), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F16_MFMA_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops},
         "cpu_baseline": None,
     }), flush=True)
 
