@@ -24,6 +24,7 @@ Modules
 -------
 sizes      KV-cache byte counts (the size formula and its table).
 allocator  block pool: free list, refcounts, block tables, fork, COW.
+prefix_cache  cached full blocks matched by content, LRU eviction.
 cache      the paged K/V store: append, block copy, gather.
 attention  decode and causal prefill attention by definition (NumPy fp64), decode by brute force.
 quant      int8 absmax quantiser with one scale per (block, KV head).
@@ -42,6 +43,7 @@ from .sizes import (
     pool_bytes,
 )
 from .allocator import RefAllocator, NoBlocks, UnknownSeq
+from .prefix_cache import RefPrefixCache
 from .cache import RefCache
 from .attention import decode, decode_seq_head, brute_decode, gather, prefill
 from .quant import quantize_block_int8, quantize_pool_int8, dequantize_int8, append_row_int8
@@ -52,6 +54,7 @@ __all__ = [
     "kv_cache_bytes",
     "pool_bytes",
     "RefAllocator",
+    "RefPrefixCache",
     "NoBlocks",
     "UnknownSeq",
     "RefCache",

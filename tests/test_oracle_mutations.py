@@ -214,3 +214,76 @@ def test_prefill_grouping_mixup_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "prefill", prefill)
     with pytest.raises(AssertionError):
         check_prefill_against_sdpa(workloads.prefill_chunks(11, [5, 0], [12, 30], 8, 2, 64))
+
+
+# ---------------------------------------------------------------------------
+# prefix cache
+
+def test_prefix_match_without_predecessor_is_caught(monkeypatch):
+    """Matching a block by its ids alone would hand a request a block cached
+    after a different predecessor; the brute-force lookup pin fails."""
+    import oracle.prefix_cache as pcm
+    from test_oracle_prefix_cache import brute_lookup, toks
+
+    def create(self, tokens):
+        tokens = [int(t) for t in tokens]
+        sid = self.seq_create()
+        chain = []
+        for j in range(max(len(tokens) - 1, 0) // 16):
+            ids = tuple(tokens[j * 16:(j + 1) * 16])
+            hit = [b for b, (p, i) in self.entries.items() if i == ids]
+            if not hit:
+                break
+            chain.append(hit[0])
+        for b in chain:
+            self.ref[b] += 1
+        self.tables[sid] = chain
+        self.lens[sid] = 16 * len(chain)
+        return sid, self.lens[sid]
+
+    monkeypatch.setattr(pcm.RefPrefixCache, "seq_create_cached", create)
+    c = pcm.RefPrefixCache(8)
+    a, _ = c.seq_create_cached(toks((0, 33)))
+    c.seq_reserve(a, 33)
+    c.insert(a, toks((0, 33)))
+    prompt = toks((16, 16), (0, 5))  # the second block's ids, now in first position
+    expect = brute_lookup(c, prompt)
+    with pytest.raises(AssertionError):
+        sid, hit = c.seq_create_cached(prompt)
+        assert c.tables[sid] == expect
+
+
+def test_prefix_lookup_taking_the_last_token_is_caught(monkeypatch):
+    """Taking floor(n / 16) blocks leaves no token to compute for a prompt of
+    whole blocks; the hand-traced scenario fails."""
+    import oracle.prefix_cache as pcm
+    from test_oracle_prefix_cache import test_hand_traced_scenario
+    real = pcm.RefPrefixCache.seq_create_cached
+
+    def create(self, tokens):
+        return real(self, list(tokens) + [0])
+
+    monkeypatch.setattr(pcm.RefPrefixCache, "seq_create_cached", create)
+    with pytest.raises(AssertionError):
+        test_hand_traced_scenario()
+
+
+def test_eviction_of_a_block_with_followers_is_caught(monkeypatch):
+    """Evicting the least recently used block even when cached blocks follow
+    it leaves orphans; the invariants fail on a random program."""
+    import oracle.prefix_cache as pcm
+    from test_oracle_prefix_cache import random_program
+
+    def evictable(self):
+        return [b for b in self.entries if self.ref[b] == 1]
+
+    def touch(self, chain):  # root first: predecessors become the older ones
+        for blk in chain:
+            self.tick += 1
+            self.used[blk] = self.tick
+
+    monkeypatch.setattr(pcm.RefPrefixCache, "_evictable", evictable)
+    monkeypatch.setattr(pcm.RefPrefixCache, "_touch", touch)
+    with pytest.raises((AssertionError, KeyError)):
+        for seed in (1, 2, 3):
+            random_program(seed)
