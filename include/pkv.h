@@ -126,6 +126,44 @@ int pkv_free_list(const pkv_pool* pool, int32_t* out, int32_t cap, int32_t* n);
 int pkv_build_block_tables(const pkv_pool* pool, const int64_t* seqs, int32_t B, int32_t max_blocks,
                            int32_t* tables_host, int32_t* ctx_lens_host);
 
+/* ---- prefix cache (host) ([p2] §4.3: K/V kept block by block with the
+ * order of the blocks recorded, so a request whose prefix matches an earlier
+ * one reuses those blocks and computes only the rest) ------------------------
+ * Only full blocks are cached, each identified by its 16 token ids and the
+ * cached block before it; matching compares the ids. The cache holds one
+ * reference on every cached block. A block that only the cache holds and
+ * that no cached block follows is evictable; eviction takes the least
+ * recently used one first (a hit or an insert marks its chain used).
+ * pkv_seq_reserve evicts just enough cache-only blocks when the free list
+ * is short; if free plus cache-only blocks are still too few it returns
+ * PKV_ERR_NO_BLOCKS and changes nothing. */
+
+/* Create a sequence for a prompt of n token ids: its leading full blocks
+ * are taken from the cache while they match (at most floor((n-1)/16), so
+ * the last token is always computed), each gaining a reference. *n_cached
+ * receives the tokens the sequence now holds (a multiple of 16); the caller
+ * reserves and computes tokens n_cached .. n-1. */
+int pkv_seq_create_cached(pkv_pool* pool, const int32_t* tokens, int32_t n, int64_t* seq, int32_t* n_cached);
+
+/* Register seq's full blocks holding its first n tokens (token ids, K/V
+ * already written) in the cache, in order; stops at the first block whose
+ * content is already cached as another block. *n_added (optional) receives
+ * the blocks newly cached. */
+int pkv_prefix_cache_insert(pkv_pool* pool, int64_t seq, const int32_t* tokens, int32_t n, int32_t* n_added);
+
+/* Evict up to max_blocks evictable blocks, least recently used first;
+ * evicted_out (max_blocks ints) receives them in order, *n_evicted their
+ * count. The blocks go back to the free list. */
+int pkv_prefix_cache_evict(pkv_pool* pool, int32_t max_blocks, int32_t* evicted_out, int32_t* n_evicted);
+
+/* Cached blocks, and how many of them only the cache holds. */
+int pkv_prefix_cache_stats(const pkv_pool* pool, int32_t* n_cached, int32_t* n_reclaimable);
+
+/* Introspection for exact tests: whether `block` is cached, its predecessor
+ * (-1 for none), its 16 ids (ids[16]) and its last-use tick. */
+int pkv_prefix_cache_entry(const pkv_pool* pool, int32_t block, int32_t* is_cached, int32_t* pred, int32_t* ids,
+                           int64_t* last_use);
+
 /* ---- shared-prefix plan (host) ([p1] §三: requests with a common prefix
  * point at the same physical blocks) -------------------------------------- */
 

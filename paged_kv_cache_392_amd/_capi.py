@@ -89,6 +89,11 @@ _SIGS = {
     "pkv_num_free": (ctypes.c_int, [_vp, _p_i32]),
     "pkv_free_list": (ctypes.c_int, [_vp, _p_i32, _c_i32, _p_i32]),
     "pkv_build_block_tables": (ctypes.c_int, [_vp, _p_i64, _c_i32, _c_i32, _p_i32, _p_i32]),
+    "pkv_seq_create_cached": (ctypes.c_int, [_vp, _p_i32, _c_i32, _p_i64, _p_i32]),
+    "pkv_prefix_cache_insert": (ctypes.c_int, [_vp, _c_i64, _p_i32, _c_i32, _p_i32]),
+    "pkv_prefix_cache_evict": (ctypes.c_int, [_vp, _c_i32, _p_i32, _p_i32]),
+    "pkv_prefix_cache_stats": (ctypes.c_int, [_vp, _p_i32, _p_i32]),
+    "pkv_prefix_cache_entry": (ctypes.c_int, [_vp, _c_i32, _p_i32, _p_i32, _p_i32, _p_i64]),
     "pkv_plan_ints": (_c_i32, [_c_i32]),
     "pkv_plan_shared_prefix": (ctypes.c_int, [_vp, _p_i64, _c_i32, _c_i32, _c_i32, _p_i32, _c_i32, _p_i32]),
     "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(pkv_config), _vp, _vp, _c_i32, _vp]),
@@ -252,6 +257,44 @@ def pkv_build_block_tables(pool, seqs, max_blocks):
     _check(load().pkv_build_block_tables(pool, s.ctypes.data_as(_p_i64), len(s), max_blocks,
                                          _i32p(tables), _i32p(lens)))
     return tables[:, :max_blocks], lens[:len(s)]
+
+
+def pkv_seq_create_cached(pool, tokens):
+    """Returns ``(seq, n_cached)``: a new sequence holding the cached blocks
+    that match the prompt's leading full blocks."""
+    t = np.ascontiguousarray(tokens, np.int32)
+    s, nc = _c_i64(), _c_i32()
+    _check(load().pkv_seq_create_cached(pool, _i32p(t) if len(t) else None, len(t), ctypes.byref(s), ctypes.byref(nc)))
+    return s.value, nc.value
+
+
+def pkv_prefix_cache_insert(pool, seq, tokens):
+    t = np.ascontiguousarray(tokens, np.int32)
+    n = _c_i32()
+    _check(load().pkv_prefix_cache_insert(pool, seq, _i32p(t) if len(t) else None, len(t), ctypes.byref(n)))
+    return n.value
+
+
+def pkv_prefix_cache_evict(pool, max_blocks):
+    out = np.empty(max(max_blocks, 1), np.int32)
+    n = _c_i32()
+    _check(load().pkv_prefix_cache_evict(pool, max_blocks, _i32p(out), ctypes.byref(n)))
+    return [int(x) for x in out[:n.value]]
+
+
+def pkv_prefix_cache_stats(pool):
+    """Returns ``(cached blocks, blocks only the cache holds)``."""
+    a, b = _c_i32(), _c_i32()
+    _check(load().pkv_prefix_cache_stats(pool, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def pkv_prefix_cache_entry(pool, block):
+    """Returns ``(is_cached, predecessor, ids[16], last_use)``."""
+    c, p, t = _c_i32(), _c_i32(), _c_i64()
+    ids = np.empty(16, np.int32)
+    _check(load().pkv_prefix_cache_entry(pool, block, ctypes.byref(c), ctypes.byref(p), _i32p(ids), ctypes.byref(t)))
+    return bool(c.value), p.value, [int(x) for x in ids], t.value
 
 
 def pkv_plan_ints(B):

@@ -15,9 +15,27 @@
 //   - a write at a non-zero offset of a block with refcount > 1 moves the
 //     writer to a fresh block and reports the (old, new) pair to copy;
 //   - a reservation either succeeds whole or changes nothing.
+//
+// Prefix cache ([p2] §4.3: K/V kept block by block with the order of the
+// blocks recorded; a request whose prefix matches reuses those blocks and
+// computes only the rest; eviction left to tuning):
+//   - only full blocks are cached, each identified by its 16 token ids and
+//     its predecessor (the cached block before it, or none); matching
+//     compares the ids themselves, the 64-bit key only narrows the search;
+//   - a lookup takes the longest matching chain of a prompt's leading full
+//     blocks, at most floor((n - 1) / 16), so the last token is computed;
+//   - the cache holds one reference per cached block; a block only the cache
+//     holds, with no cached block after it, is evictable;
+//   - least recently used first: a hit or an insert marks its chain's blocks
+//     used, last block first, so a block is always newer than its followers;
+//   - a reservation short of free blocks evicts just enough first, or, if
+//     free plus cache-only blocks are too few, changes nothing.
 #include <algorithm>
+#include <array>
 #include <cstring>
+#include <set>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pkv_internal.h"
@@ -31,12 +49,39 @@ struct Seq {
 
 }  // namespace
 
+namespace {
+
+struct CacheEntry {
+  int32_t pred = -1;  // cached block before this one, -1 for a first block
+  std::array<int32_t, PKV_BLOCK_TOKENS> ids{};
+  uint64_t tick = 0;  // last use
+};
+
+uint64_t content_key(int32_t pred, const int32_t* ids) {
+  uint64_t h = 0x9E3779B97F4A7C15ull ^ uint64_t(uint32_t(pred));
+  for (int i = 0; i < PKV_BLOCK_TOKENS; ++i) {
+    h ^= uint64_t(uint32_t(ids[i])) + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+    h *= 0xBF58476D1CE4E5B9ull;
+    h ^= h >> 31;
+  }
+  return h;
+}
+
+}  // namespace
+
 struct pkv_pool {
   pkv_config cfg;
   std::vector<int32_t> free_stack;  // back() is handed out next
   std::vector<int32_t> ref;         // per physical block
   std::unordered_map<int64_t, Seq> seqs;
   int64_t next_id = 1;
+  // prefix cache
+  std::vector<char> cached;                                      // per block
+  std::vector<CacheEntry> entry;                                 // per block, valid if cached
+  std::vector<int32_t> children;                                 // cached blocks following each block
+  std::unordered_multimap<uint64_t, int32_t> by_key;             // content key -> cached block
+  std::set<std::pair<uint64_t, int32_t>> lru;                    // (tick, block) of cached blocks
+  uint64_t tick = 0;
 };
 
 namespace {
@@ -51,6 +96,55 @@ const Seq* find(const pkv_pool* p, int64_t id) {
 }
 
 int64_t ceil_blocks(int64_t tokens) { return (tokens + PKV_BLOCK_TOKENS - 1) / PKV_BLOCK_TOKENS; }
+
+// The cached block with these ids after `pred`, or -1.
+int32_t cache_find(const pkv_pool* p, int32_t pred, const int32_t* ids) {
+  auto range = p->by_key.equal_range(content_key(pred, ids));
+  for (auto it = range.first; it != range.second; ++it) {
+    const CacheEntry& e = p->entry[it->second];
+    if (e.pred == pred && std::equal(e.ids.begin(), e.ids.end(), ids)) return it->second;
+  }
+  return -1;
+}
+
+// Mark a chain used, last block first (a block stays newer than its followers).
+void cache_touch(pkv_pool* p, const std::vector<int32_t>& chain) {
+  for (auto it = chain.rbegin(); it != chain.rend(); ++it) {
+    CacheEntry& e = p->entry[*it];
+    p->lru.erase({e.tick, *it});
+    e.tick = ++p->tick;
+    p->lru.insert({e.tick, *it});
+  }
+}
+
+int32_t cache_reclaimable(const pkv_pool* p) {
+  int32_t n = 0;
+  for (const auto& tb : p->lru) n += p->ref[tb.second] == 1;
+  return n;
+}
+
+// Evict the least recently used block only the cache holds and no cached
+// block follows; returns it, or -1.
+int32_t cache_evict_one(pkv_pool* p) {
+  for (auto it = p->lru.begin(); it != p->lru.end(); ++it) {
+    const int32_t b = it->second;
+    if (p->ref[b] != 1 || p->children[b] != 0) continue;
+    CacheEntry& e = p->entry[b];
+    auto range = p->by_key.equal_range(content_key(e.pred, e.ids.data()));
+    for (auto k = range.first; k != range.second; ++k)
+      if (k->second == b) {
+        p->by_key.erase(k);
+        break;
+      }
+    if (e.pred >= 0) --p->children[e.pred];
+    p->lru.erase(it);
+    p->cached[b] = 0;
+    e = CacheEntry{};
+    if (--p->ref[b] == 0) p->free_stack.push_back(b);
+    return b;
+  }
+  return -1;
+}
 
 }  // namespace
 
@@ -81,6 +175,9 @@ int pkv_pool_create(const pkv_config* cfg, const int32_t* free_order, int32_t n,
   p->cfg = *cfg;
   p->free_stack.assign(order.rbegin(), order.rend());
   p->ref.assign(N, 0);
+  p->cached.assign(N, 0);
+  p->entry.assign(N, CacheEntry{});
+  p->children.assign(N, 0);
   *out = p;
   return PKV_OK;
 }
@@ -141,9 +238,14 @@ int pkv_seq_reserve(pkv_pool* pool, int64_t seq, int32_t n, int32_t* slots_out, 
     if (!cow_pairs_out || cow_cap < 1)
       return pkv::fail(PKV_ERR_INVALID_ARG, "copy-on-write needed but cow_cap < 1");
   }
-  if (need > int64_t(pool->free_stack.size()))
-    return pkv::fail(PKV_ERR_NO_BLOCKS, "need %lld blocks, %zu free", (long long)need,
-                     pool->free_stack.size());
+  if (need > int64_t(pool->free_stack.size())) {
+    const int64_t have = int64_t(pool->free_stack.size()) + cache_reclaimable(pool);
+    if (need > have)
+      return pkv::fail(PKV_ERR_NO_BLOCKS, "need %lld blocks, %zu free, %lld with the cache-only ones",
+                       (long long)need, pool->free_stack.size(), (long long)have);
+    while (need > int64_t(pool->free_stack.size()))
+      if (cache_evict_one(pool) < 0) return pkv::fail(PKV_ERR_REFCOUNT, "prefix cache bookkeeping is inconsistent");
+  }
   // Apply.
   int32_t ncow = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -238,6 +340,96 @@ int pkv_build_block_tables(const pkv_pool* pool, const int64_t* seqs, int32_t B,
     for (int32_t j = int32_t(nb); j < max_blocks; ++j) row[j] = -1;
     ctx_lens_host[b] = s->len;
   }
+  return PKV_OK;
+}
+
+int pkv_seq_create_cached(pkv_pool* pool, const int32_t* tokens, int32_t n, int64_t* seq, int32_t* n_cached) {
+  if (!pool || !seq || !n_cached || (n > 0 && !tokens)) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  if (n < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "n must be >= 0");
+  Seq s;
+  int32_t pred = -1;
+  const int32_t blocks = n > 0 ? (n - 1) / PKV_BLOCK_TOKENS : 0;
+  for (int32_t j = 0; j < blocks; ++j) {
+    const int32_t b = cache_find(pool, pred, tokens + int64_t(j) * PKV_BLOCK_TOKENS);
+    if (b < 0) break;
+    s.table.push_back(b);
+    pred = b;
+  }
+  for (int32_t b : s.table) ++pool->ref[b];
+  s.len = int32_t(s.table.size()) * PKV_BLOCK_TOKENS;
+  cache_touch(pool, s.table);
+  const int64_t id = pool->next_id++;
+  *n_cached = s.len;
+  pool->seqs.emplace(id, std::move(s));
+  *seq = id;
+  return PKV_OK;
+}
+
+int pkv_prefix_cache_insert(pkv_pool* pool, int64_t seq, const int32_t* tokens, int32_t n, int32_t* n_added) {
+  if (!pool || (n > 0 && !tokens)) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  if (n < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "n must be >= 0");
+  Seq* s = find(pool, seq);
+  if (!s) return pkv::fail(PKV_ERR_UNKNOWN_SEQ, "sequence %lld is not live", (long long)seq);
+  const int32_t nfull = std::min(n, s->len) / PKV_BLOCK_TOKENS;
+  std::vector<int32_t> chain;
+  int32_t pred = -1, added = 0;
+  for (int32_t j = 0; j < nfull; ++j) {
+    const int32_t b = s->table[j];
+    const int32_t* ids = tokens + int64_t(j) * PKV_BLOCK_TOKENS;
+    const int32_t have = cache_find(pool, pred, ids);
+    if (have < 0) {
+      if (pool->cached[b]) break;  // cached under other content: the ids do not describe this table
+      CacheEntry& e = pool->entry[b];
+      e.pred = pred;
+      std::copy(ids, ids + PKV_BLOCK_TOKENS, e.ids.begin());
+      e.tick = 0;
+      pool->cached[b] = 1;
+      pool->by_key.emplace(content_key(pred, ids), b);
+      pool->lru.insert({0, b});
+      ++pool->ref[b];
+      if (pred >= 0) ++pool->children[pred];
+      ++added;
+    } else if (have != b) {
+      break;  // this content is already cached as another block
+    }
+    chain.push_back(b);
+    pred = b;
+  }
+  cache_touch(pool, chain);
+  if (n_added) *n_added = added;
+  return PKV_OK;
+}
+
+int pkv_prefix_cache_evict(pkv_pool* pool, int32_t max_blocks, int32_t* evicted_out, int32_t* n_evicted) {
+  if (!pool || !n_evicted || (max_blocks > 0 && !evicted_out)) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  if (max_blocks < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks must be >= 0");
+  int32_t k = 0;
+  while (k < max_blocks) {
+    const int32_t b = cache_evict_one(pool);
+    if (b < 0) break;
+    evicted_out[k++] = b;
+  }
+  *n_evicted = k;
+  return PKV_OK;
+}
+
+int pkv_prefix_cache_stats(const pkv_pool* pool, int32_t* n_cached, int32_t* n_reclaimable) {
+  if (!pool || !n_cached || !n_reclaimable) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  *n_cached = int32_t(pool->lru.size());
+  *n_reclaimable = cache_reclaimable(pool);
+  return PKV_OK;
+}
+
+int pkv_prefix_cache_entry(const pkv_pool* pool, int32_t block, int32_t* is_cached, int32_t* pred, int32_t* ids,
+                           int64_t* last_use) {
+  if (!pool || !is_cached || !pred || !ids || !last_use) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL argument");
+  if (block < 0 || block >= pool->cfg.num_blocks)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "block %d out of range", block);
+  const CacheEntry& e = pool->entry[block];
+  *is_cached = pool->cached[block];
+  *pred = pool->cached[block] ? e.pred : -1;
+  for (int i = 0; i < PKV_BLOCK_TOKENS; ++i) ids[i] = pool->cached[block] ? e.ids[i] : 0;
+  *last_use = pool->cached[block] ? int64_t(e.tick) : 0;
   return PKV_OK;
 }
 
