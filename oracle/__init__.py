@@ -25,6 +25,7 @@ Modules
 sizes      KV-cache byte counts (the size formula and its table).
 allocator  block pool: free list, refcounts, block tables, fork, COW.
 prefix_cache  cached full blocks matched by content, LRU eviction.
+batching   continuous-batching step loop: decode, admission, chunked prefill.
 cache      the paged K/V store: append, block copy, gather.
 attention  decode and causal prefill attention by definition (NumPy fp64), decode by brute force.
 quant      int8 absmax quantiser with one scale per (block, KV head).
@@ -44,6 +45,7 @@ from .sizes import (
 )
 from .allocator import RefAllocator, NoBlocks, UnknownSeq
 from .prefix_cache import RefPrefixCache
+from .batching import RefScheduler
 from .cache import RefCache
 from .attention import decode, decode_seq_head, brute_decode, gather, prefill
 from .quant import quantize_block_int8, quantize_pool_int8, dequantize_int8, append_row_int8
@@ -55,6 +57,7 @@ __all__ = [
     "pool_bytes",
     "RefAllocator",
     "RefPrefixCache",
+    "RefScheduler",
     "NoBlocks",
     "UnknownSeq",
     "RefCache",

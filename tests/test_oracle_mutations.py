@@ -287,3 +287,63 @@ def test_eviction_of_a_block_with_followers_is_caught(monkeypatch):
     with pytest.raises((AssertionError, KeyError)):
         for seed in (1, 2, 3):
             random_program(seed)
+
+
+# ---------------------------------------------------------------------------
+# continuous batching
+
+def test_static_batching_is_caught(monkeypatch):
+    """Admitting only into an empty batch (wait for the whole batch to
+    finish) fails the hand trace: request 3 must start as soon as 1 and 2
+    have left."""
+    import oracle.batching as bm
+    from test_oracle_batching import test_hand_trace
+    real = bm.RefScheduler.step
+
+    # a batch that never takes new requests while any request runs
+    def step_static(self):
+        if self.running:
+            saved = self.waiting
+            self.waiting = bm.deque()
+            try:
+                return real(self)
+            finally:
+                self.waiting = saved
+        return real(self)
+
+    monkeypatch.setattr(bm.RefScheduler, "step", step_static)
+    with pytest.raises(AssertionError):
+        test_hand_trace()
+
+
+def test_preempting_the_oldest_is_caught(monkeypatch):
+    import oracle.batching as bm
+    from test_oracle_batching import test_preemption_recomputes_and_keeps_the_tokens
+
+    def preempt_oldest(self):
+        v = self.running.pop(0)
+        self.cache.seq_free(v.seq)
+        v.seq, v.computed, v.pending = None, 0, None
+        self.waiting.appendleft(v)
+        return v
+
+    monkeypatch.setattr(bm.RefScheduler, "_preempt_newest", preempt_oldest)
+    with pytest.raises((AssertionError, KeyError, ValueError)):
+        test_preemption_recomputes_and_keeps_the_tokens()
+
+
+def test_finishing_without_freeing_is_caught(monkeypatch):
+    import oracle.batching as bm
+    from test_oracle_batching import test_random_workloads_finish_and_keep_invariants
+
+    def advance(self, r, token, done):
+        r.tokens.append(int(token))
+        r.generated += 1
+        if r.generated >= r.max_new:
+            self.running.remove(r)  # leaves without releasing its sequence
+            self.finished.append(r.rid)
+            done.append(r.rid)
+
+    monkeypatch.setattr(bm.RefScheduler, "_advance", advance)
+    with pytest.raises(AssertionError):
+        test_random_workloads_finish_and_keep_invariants(1)
