@@ -164,6 +164,85 @@ int pkv_prefix_cache_stats(const pkv_pool* pool, int32_t* n_cached, int32_t* n_r
 int pkv_prefix_cache_entry(const pkv_pool* pool, int32_t block, int32_t* is_cached, int32_t* pred, int32_t* ids,
                            int64_t* last_use);
 
+/* ---- continuous batching (host) ([p2] §3.3: finished requests leave the
+ * batch after every step and free their blocks, waiting requests come in;
+ * [p2] §5.2: a full pool makes requests wait; [p2] §4.3: a request starts
+ * from the cached blocks of its prefix) -------------------------------------
+ * A request is its token list (prompt, then each generated token); its K/V
+ * are computed in order. pkv_sched_step plans one step:
+ *   1. decode: every running request with no chunk left whose newest token
+ *      still needs its K/V gets one slot, in admission order; if the pool
+ *      refuses, the newest running request is preempted (its sequence is
+ *      freed, it returns to the front of the queue and is recomputed later,
+ *      from whatever the prefix cache still holds), until the slot is
+ *      granted or the request itself yielded;
+ *   2. admission: while fewer than max_running run, the first waiting
+ *      request starts a sequence from the prefix cache and reserves slots
+ *      for the rest of its tokens, or stays first and admission stops;
+ *   3. prefill: running requests with tokens left get chunks in admission
+ *      order, prefill_budget tokens per step in all.
+ * The caller writes each item's K/V into its slots (after copying any
+ * copy-on-write pairs), attends, and passes pkv_sched_commit the next token
+ * of every item that computed its request's newest token (completes = 1),
+ * in item order. A request with max_new generated tokens then inserts its
+ * computed tokens into the prefix cache and frees its sequence; a request
+ * whose prompt is first computed inserts the prompt. */
+
+#define PKV_STEP_DECODE 0
+#define PKV_STEP_PREFILL 1
+#define PKV_REQ_WAITING 0
+#define PKV_REQ_RUNNING 1
+#define PKV_REQ_FINISHED 2
+
+typedef struct pkv_sched pkv_sched;
+
+typedef struct pkv_step_item {
+  int64_t req;         /* request id                                          */
+  int64_t seq;         /* its sequence in the pool                            */
+  int32_t kind;        /* PKV_STEP_DECODE or PKV_STEP_PREFILL                 */
+  int32_t start;       /* position of the item's first token                  */
+  int32_t count;       /* tokens (1 for a decode)                             */
+  int32_t slot_index;  /* index of its first slot in the plan's slots         */
+  int32_t completes;   /* 1: the item computes the request's newest token     */
+} pkv_step_item;
+
+typedef struct pkv_step_plan {  /* caller-owned arrays, capacities from
+                                   pkv_sched_limits; decode items come first */
+  pkv_step_item* items;
+  int32_t item_cap, n_items;
+  int32_t* slots;
+  int32_t slot_cap, n_slots;
+  int32_t* cow_pairs;          /* (src, dst) block pairs to copy first:
+                                  2 x cow_cap ints; cow_cap, n_cow in pairs   */
+  int32_t cow_cap, n_cow;
+  int64_t* preempted;
+  int32_t preempted_cap, n_preempted;
+  int64_t* admitted;
+  int32_t* admitted_cached;    /* tokens each admitted request took from the cache */
+  int32_t admitted_cap, n_admitted;
+} pkv_step_plan;
+
+/* The plan array sizes a step may need: items (also preempted, admitted and
+ * copy-on-write pairs) and slots. */
+int pkv_sched_limits(int32_t max_running, int32_t prefill_budget, int32_t* max_items, int32_t* max_slots);
+int pkv_sched_create(pkv_pool* pool, int32_t max_running, int32_t prefill_budget, pkv_sched** out);
+void pkv_sched_destroy(pkv_sched* sched);
+/* Queue a request (ids unique; n >= 1 prompt tokens; max_new >= 1). */
+int pkv_sched_submit(pkv_sched* sched, int64_t req, const int32_t* prompt, int32_t n, int32_t max_new);
+/* Plan one step into `plan` (INVALID_ARG, nothing changed, if its arrays
+ * are below the limits). */
+int pkv_sched_step(pkv_sched* sched, pkv_step_plan* plan);
+/* Hand out the next tokens of the last plan's completing items, in item
+ * order; finished (at least as many entries as next tokens) receives the
+ * requests that finished. */
+int pkv_sched_commit(pkv_sched* sched, const int32_t* next_tokens, int32_t n, int64_t* finished, int32_t fin_cap,
+                     int32_t* n_finished);
+/* A request's tokens (tokens may be NULL to query the count), computed
+ * tokens, sequence (0 if none) and PKV_REQ_* state. */
+int pkv_sched_request(const pkv_sched* sched, int64_t req, int32_t* tokens, int32_t cap, int32_t* n_tokens,
+                      int32_t* computed, int64_t* seq, int32_t* state);
+int pkv_sched_counts(const pkv_sched* sched, int32_t* n_waiting, int32_t* n_running, int32_t* n_finished);
+
 /* ---- shared-prefix plan (host) ([p1] §三: requests with a common prefix
  * point at the same physical blocks) -------------------------------------- */
 

@@ -65,6 +65,24 @@ class pkv_prefill_args(ctypes.Structure):
                 ("max_context", _c_i32), ("out_dev", _vp), ("scale", ctypes.c_float)]
 
 
+class pkv_step_item(ctypes.Structure):
+    _fields_ = [("req", _c_i64), ("seq", _c_i64), ("kind", _c_i32), ("start", _c_i32), ("count", _c_i32),
+                ("slot_index", _c_i32), ("completes", _c_i32)]
+
+
+class pkv_step_plan(ctypes.Structure):
+    _fields_ = [("items", ctypes.POINTER(pkv_step_item)), ("item_cap", _c_i32), ("n_items", _c_i32),
+                ("slots", _p_i32), ("slot_cap", _c_i32), ("n_slots", _c_i32),
+                ("cow_pairs", _p_i32), ("cow_cap", _c_i32), ("n_cow", _c_i32),
+                ("preempted", _p_i64), ("preempted_cap", _c_i32), ("n_preempted", _c_i32),
+                ("admitted", _p_i64), ("admitted_cached", _p_i32), ("admitted_cap", _c_i32), ("n_admitted", _c_i32)]
+
+
+PKV_STEP_DECODE = 0
+PKV_STEP_PREFILL = 1
+PKV_REQ_WAITING, PKV_REQ_RUNNING, PKV_REQ_FINISHED = 0, 1, 2
+
+
 class PkvError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"pkv error {status}: {message}")
@@ -94,6 +112,14 @@ _SIGS = {
     "pkv_prefix_cache_evict": (ctypes.c_int, [_vp, _c_i32, _p_i32, _p_i32]),
     "pkv_prefix_cache_stats": (ctypes.c_int, [_vp, _p_i32, _p_i32]),
     "pkv_prefix_cache_entry": (ctypes.c_int, [_vp, _c_i32, _p_i32, _p_i32, _p_i32, _p_i64]),
+    "pkv_sched_limits": (ctypes.c_int, [_c_i32, _c_i32, _p_i32, _p_i32]),
+    "pkv_sched_create": (ctypes.c_int, [_vp, _c_i32, _c_i32, ctypes.POINTER(_vp)]),
+    "pkv_sched_destroy": (None, [_vp]),
+    "pkv_sched_submit": (ctypes.c_int, [_vp, _c_i64, _p_i32, _c_i32, _c_i32]),
+    "pkv_sched_step": (ctypes.c_int, [_vp, ctypes.POINTER(pkv_step_plan)]),
+    "pkv_sched_commit": (ctypes.c_int, [_vp, _p_i32, _c_i32, _p_i64, _c_i32, _p_i32]),
+    "pkv_sched_request": (ctypes.c_int, [_vp, _c_i64, _p_i32, _c_i32, _p_i32, _p_i32, _p_i64, _p_i32]),
+    "pkv_sched_counts": (ctypes.c_int, [_vp, _p_i32, _p_i32, _p_i32]),
     "pkv_plan_ints": (_c_i32, [_c_i32]),
     "pkv_plan_shared_prefix": (ctypes.c_int, [_vp, _p_i64, _c_i32, _c_i32, _c_i32, _p_i32, _c_i32, _p_i32]),
     "pkv_copy_blocks": (ctypes.c_int, [ctypes.POINTER(pkv_config), _vp, _vp, _c_i32, _vp]),
@@ -295,6 +321,94 @@ def pkv_prefix_cache_entry(pool, block):
     ids = np.empty(16, np.int32)
     _check(load().pkv_prefix_cache_entry(pool, block, ctypes.byref(c), ctypes.byref(p), _i32p(ids), ctypes.byref(t)))
     return bool(c.value), p.value, [int(x) for x in ids], t.value
+
+
+def pkv_sched_limits(max_running, prefill_budget):
+    a, b = _c_i32(), _c_i32()
+    _check(load().pkv_sched_limits(max_running, prefill_budget, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def pkv_sched_create(pool, max_running, prefill_budget):
+    out = _vp()
+    _check(load().pkv_sched_create(pool, max_running, prefill_budget, ctypes.byref(out)))
+    return out.value
+
+
+def pkv_sched_destroy(sched):
+    if sched:
+        load().pkv_sched_destroy(sched)
+
+
+def pkv_sched_submit(sched, req, prompt, max_new):
+    t = np.ascontiguousarray(prompt, np.int32)
+    _check(load().pkv_sched_submit(sched, req, _i32p(t) if len(t) else None, len(t), max_new))
+
+
+class StepPlan:
+    """Caller-owned arrays of one step plan (sized by pkv_sched_limits)."""
+
+    def __init__(self, max_running, prefill_budget):
+        mi, ms = pkv_sched_limits(max_running, prefill_budget)
+        self.items = (pkv_step_item * mi)()
+        self.slots = np.zeros(ms, np.int32)
+        self.cow = np.zeros(2 * mi, np.int32)
+        self.pre = np.zeros(mi, np.int64)
+        self.adm = np.zeros(mi, np.int64)
+        self.adm_hit = np.zeros(mi, np.int32)
+        p = pkv_step_plan()
+        p.items, p.item_cap = self.items, mi
+        p.slots, p.slot_cap = _i32p(self.slots), ms
+        p.cow_pairs, p.cow_cap = _i32p(self.cow), mi
+        p.preempted, p.preempted_cap = self.pre.ctypes.data_as(_p_i64), mi
+        p.admitted, p.admitted_cached, p.admitted_cap = self.adm.ctypes.data_as(_p_i64), _i32p(self.adm_hit), mi
+        self.c = p
+
+    def decode(self):
+        """``{"items": [(req, seq, kind, start, count, slots, completes)], "cow": [(src, dst)],
+        "preempted": [req], "admitted": [(req, cached)]}``."""
+        p = self.c
+        items = []
+        for i in range(p.n_items):
+            it = self.items[i]
+            items.append((it.req, it.seq, it.kind, it.start, it.count,
+                          [int(x) for x in self.slots[it.slot_index:it.slot_index + it.count]], it.completes))
+        return {"items": items,
+                "cow": [(int(self.cow[2 * i]), int(self.cow[2 * i + 1])) for i in range(p.n_cow)],
+                "preempted": [int(x) for x in self.pre[:p.n_preempted]],
+                "admitted": [(int(self.adm[i]), int(self.adm_hit[i])) for i in range(p.n_admitted)]}
+
+
+def pkv_sched_step(sched, plan):
+    _check(load().pkv_sched_step(sched, ctypes.byref(plan.c)))
+    return plan.decode()
+
+
+def pkv_sched_commit(sched, next_tokens):
+    t = np.ascontiguousarray(next_tokens, np.int32)
+    fin = np.zeros(max(len(t), 1), np.int64)
+    n = _c_i32()
+    _check(load().pkv_sched_commit(sched, _i32p(t) if len(t) else None, len(t), fin.ctypes.data_as(_p_i64),
+                                   len(fin), ctypes.byref(n)))
+    return [int(x) for x in fin[:n.value]]
+
+
+def pkv_sched_request(sched, req):
+    """Returns ``(tokens, computed, seq, state)``."""
+    n, comp, st = _c_i32(), _c_i32(), _c_i32()
+    seq = _c_i64()
+    _check(load().pkv_sched_request(sched, req, None, 0, ctypes.byref(n), ctypes.byref(comp), ctypes.byref(seq),
+                                    ctypes.byref(st)))
+    out = np.zeros(max(n.value, 1), np.int32)
+    _check(load().pkv_sched_request(sched, req, _i32p(out), len(out), ctypes.byref(n), ctypes.byref(comp),
+                                    ctypes.byref(seq), ctypes.byref(st)))
+    return [int(x) for x in out[:n.value]], comp.value, seq.value, st.value
+
+
+def pkv_sched_counts(sched):
+    a, b, c = _c_i32(), _c_i32(), _c_i32()
+    _check(load().pkv_sched_counts(sched, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
 
 
 def pkv_plan_ints(B):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-HOST_SOURCES = ["errors.cpp", "pool.cpp"]
+HOST_SOURCES = ["errors.cpp", "pool.cpp", "sched.cpp"]
 HIP_SOURCES = ["kernels.hip"]
 
 ARCH = "gfx950"
