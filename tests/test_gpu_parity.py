@@ -642,3 +642,50 @@ def test_prefill_last_row_equals_decode():
     diff = float(np.abs(out.cpu().numpy().astype(np.float64) - rec["out"][ends].astype(np.float64)).max())
     assert diff <= F16_TOL, diff
     lib.close()
+
+
+# ---------------------------------------------------------------------------
+# continuous batching end to end: planner + prefix cache + kernels
+
+def test_serving_loop_attention_matches_the_definition():
+    """Requests sharing system prompts served by continuous batching on a
+    pool small enough to force prefix-cache evictions and preemption: every
+    attention row of every step (chunks and decodes, recomputed ones
+    included) equals softmax(q K^T / sqrt(d)) V over the request's own
+    tokens, whatever blocks the prefix cache handed it."""
+    from paged_kv_cache_392_amd.serving import ServingLoop
+    Hq, Hkv, D = 32, 8, 128
+    model = workloads.PrefixHashModel(Hq, Hkv, D)
+    reqs = workloads.serving_requests(5, n_req=12, max_new=(16, 48))
+    N = 24
+    order = np.random.default_rng(5).permutation(N).astype(np.int32)
+    cache = pkv.PagedKVCache(1, N, Hkv, D, "f16", order, DEV)
+    cache.pool.view(torch.float16).fill_(float("nan"))
+    loop = ServingLoop(cache, Hq, max_running=4, prefill_budget=64, model=model)
+    for r in reqs:
+        loop.submit(*r)
+    announce("serving loop: 12 requests, 24-block pool")
+    log = loop.run(max_steps=2000)
+    assert loop.pending() == 0
+    final = {rid: loop.tokens(rid) for rid, _, _ in reqs}
+    for rid, prompt, mx in reqs:
+        assert len(final[rid]) == len(prompt) + mx
+    hits = sum(1 for plan, _, _ in log for _, h in plan["admitted"] if h > 0)
+    preempted = sum(len(plan["preempted"]) for plan, _, _ in log)
+    announce(f"steps {len(log)}, admissions from the cache {hits}, preemptions {preempted}")
+    assert hits > 0 and preempted > 0
+    G = Hq // Hkv
+    worst = 0.0
+    for plan, outputs, _ in log:
+        for (req, _seq, _kind, start, count, _slots, _c), out in zip(plan["items"], outputs):
+            k, v, q = model.rows(req, final[req], 0, start + count)
+            k, v = k.astype(np.float64), v.astype(np.float64)
+            for j in range(count):
+                pos = start + j
+                for h in range(Hq):
+                    ref = oracle.decode_seq_head(k[:pos + 1, h // G], v[:pos + 1, h // G], q[pos, h], 1 / math.sqrt(D))
+                    worst = max(worst, float(np.abs(out[j, h].astype(np.float64) - ref).max()))
+    announce(f"serving max abs err {worst:.3g}")
+    assert worst <= F16_TOL
+    loop.close()
+    cache.close()

@@ -311,3 +311,53 @@ CONFIGS = {
     "c5": c5_int8,
     "headline": headline,
 }
+
+
+class PrefixHashModel:
+    """A stand-in for a model's projections and sampler in serving tests.
+
+    The K, V and q rows of the token at position t are seeded normal draws
+    keyed by a rolling hash of tokens 0..t, so they depend on the token
+    prefix only (as a model's would, and as prefix caching requires). The
+    next token depends on the request and its tokens only, never on the
+    attention output, so every schedule is reproducible."""
+
+    def __init__(self, Hq, Hkv, D, vocab=50):
+        self.Hq, self.Hkv, self.D, self.vocab = Hq, Hkv, D, vocab
+
+    @staticmethod
+    def _hashes(tokens, upto):
+        h, out = 0x51ED270B27C35C49, []
+        for t in tokens[:upto]:
+            h = ((h ^ (int(t) + 0x9E3779B9)) * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+            out.append(h)
+        return out
+
+    def rows(self, req, tokens, start, count):
+        hs = self._hashes(tokens, start + count)[start:]
+        k = np.empty((count, self.Hkv, self.D), np.float16)
+        v = np.empty_like(k)
+        q = np.empty((count, self.Hq, self.D), np.float16)
+        for i, h in enumerate(hs):
+            rng = np.random.default_rng(h)
+            k[i] = _normal(rng, (self.Hkv, self.D))
+            v[i] = _normal(rng, (self.Hkv, self.D))
+            q[i] = _normal(rng, (self.Hq, self.D))
+        return k, v, q
+
+    def next_token(self, req, tokens, out_row=None):
+        return (7 * int(req) + 3 * len(tokens) + int(tokens[-1])) % self.vocab
+
+
+def serving_requests(seed, n_req=12, systems=(40, 100), user=(1, 60), max_new=(1, 24)):
+    """Requests for serving tests: each prompt is one of a few shared system
+    prompts (lengths ``systems``) followed by U[user] private tokens;
+    ``max_new`` ~ U[max_new]. Returns [(req, prompt, max_new)]."""
+    rng = np.random.default_rng(seed)
+    sys_prompts = [list(range(1000 * (k + 1), 1000 * (k + 1) + n)) for k, n in enumerate(systems)]
+    out = []
+    for rid in range(1, n_req + 1):
+        base = sys_prompts[int(rng.integers(len(sys_prompts)))]
+        tail = rng.integers(0, 50, int(rng.integers(user[0], user[1] + 1))).tolist()
+        out.append((rid, base + tail, int(rng.integers(max_new[0], max_new[1] + 1))))
+    return out
