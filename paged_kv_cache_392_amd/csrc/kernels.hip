@@ -471,14 +471,15 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   };
 
   // Online softmax of one row block's scores of a step (two tiles), kept
-  // short because the VALU, not the matrix cores, sets this loop's pace:
-  // masking only on `masked` steps (the diagonal and the odd tail, a
-  // wave-uniform choice); the lazy-max test on the raw scores' maximum;
-  // one FMA into each exponential; row sums of the fp16 probabilities by
-  // v_dot2 against ones. Returns P in the value MFMA's k-slot order.
-  auto softmax = [&](const float4_t (&acc)[2], int step, int lim, bool masked, float4_t (&o)[NDB], float& m,
-                     float& l) {
-    float a[8];
+  // short because the VALU, not the matrix cores, sets this loop's pace, and
+  // split in two so the exponentials of one row block can issue beside the
+  // other's value MFMAs. prep: masking only on `masked` steps (the diagonal
+  // and the odd tail, a wave-uniform choice) and the lazy-max test on the
+  // raw scores' maximum (raising m and rescaling when needed). probs: one
+  // FMA into each exponential, row sums of the fp16 probabilities by v_dot2
+  // against ones; returns P in the value MFMA's k-slot order.
+  auto prep = [&](const float4_t (&acc)[2], int step, int lim, bool masked, float4_t (&o)[NDB], float& m,
+                  float& l, float (&a)[8]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -506,8 +507,10 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
 #pragma unroll
       for (int i = 0; i < NDB; ++i) o[i] *= alpha;
     }
-    // probabilities enter the value MFMA in fp16; the row sum adds the same
-    // rounded values, so weights and normaliser agree
+  };
+  // probabilities enter the value MFMA in fp16; the row sum adds the same
+  // rounded values, so weights and normaliser agree
+  auto probs = [&](const float (&a)[8], float m, float& l) {
     const float nm = -m;
     half8_t pt;
     const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
@@ -525,7 +528,9 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   // One step for both row blocks of the wave: every K and V fragment is
   // read from LDS once and used by both. Both blocks are always computed
   // (rows past R have zero q and are never emitted): guards around single
-  // MFMAs would become branches that split the scheduling regions.
+  // MFMAs would become branches that split the scheduling regions. After
+  // both prep branches the remaining work is one region, ordered so the
+  // second block's exponentials sit between the first block's value MFMAs.
   auto step_rows = [&](int st, int step) {
     float4_t acc0[2], acc1[2];
 #pragma unroll
@@ -541,19 +546,30 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
     }
     // tokens below full_tokens are visible to every row: no mask before them
     const bool masked = 2 * step + 1 >= nt || (MASK && (jb + 2 * step + 2) * BT > full_tokens);
-    const half8_t pt0 = softmax(acc0, step, lim0, masked, o0, m0, l0);
-    const half8_t pt1 = softmax(acc1, step, lim1, masked, o1, m1, l1);
+    float a0[8], a1[8];
+    prep(acc0, step, lim0, masked, o0, m0, l0, a0);
+    prep(acc1, step, lim1, masked, o1, m1, l1, a1);
+    const half8_t pt0 = probs(a0, m0, l0);
     // lane (n, j) addresses V[4j + n/4][16 i + 4 (n % 4)] of each tile
     const int vofs = (4 * lj + (ln >> 2)) * KROW + (ln & 3) * 8;
+    half8_t va[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) {
       const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) short4_t*)(vst[st][0] + vofs + 32 * i));
       const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) short4_t*)(vst[st][1] + vofs + 32 * i));
-      const half8_t va = __builtin_bit_cast(half8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      o0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt0, o0[i], 0, 0, 0);
-      o1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt1, o1[i], 0, 0, 0);
+      va[i] = __builtin_bit_cast(half8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      o0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[i], pt0, o0[i], 0, 0, 0);
+    }
+    const half8_t pt1 = probs(a1, m1, l1);
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) o1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[i], pt1, o1[i], 0, 0, 0);
+    // interleave: one MFMA, then a few VALU instructions, while they last
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
   };
 
