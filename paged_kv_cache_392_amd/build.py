@@ -26,10 +26,12 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CXX = os.environ.get("CXX", "g++")
 
-# Packed fp32 instructions are kept out of every code object.
+# Packed fp32 instructions are kept out of every code object. MFMA results
+# go to ordinary VGPRs: with accumulation registers the compiler copied the
+# multi-row attention's accumulators between the two files on every step.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC",
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
