@@ -39,6 +39,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 #include <cstdint>
 #include <cstdlib>
 
@@ -388,14 +389,16 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
                                             Emit emit) {
   constexpr int NCH = D / 32;           // score MFMA chunks
   constexpr int NDB = D / 16;           // value MFMA dim blocks
-  constexpr int KROW = D * 2 + 16;      // bytes per staged K row
+  constexpr int KROW = D * 2 + 16;      // bytes per staged K row (16 lanes read 16 rows without conflicts)
+  constexpr int VROW = D * 2 + 32;      // bytes per staged V row (the transpose read's 4-row groups
+                                        // start 8 banks apart)
   constexpr int PIECES = D / 8;         // 16-byte pieces per K/V row
   constexpr int LOADERS = BT * PIECES;  // pieces per K (or V) tile
   constexpr int TILE = BT * D * 2;
   constexpr int PFS = 2;                // steps (tile pairs) in flight per thread
   static_assert(PFS % 2 == 0, "LDS stages alternate with the ring slot");
   __shared__ __align__(16) char kst[2][2][BT * KROW];
-  __shared__ __align__(16) char vst[2][2][BT * KROW];
+  __shared__ __align__(16) char vst[2][2][BT * VROW];
   __shared__ int blk_ids[MAXT];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -463,7 +466,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
           *reinterpret_cast<uint4*>(kst[st][sub] + lrow * KROW + lpc * 16) = r[sub][j];
         } else {
           const bool live = !MASK || (jb + 2 * step + sub) * BT + lrow < nvalid;
-          *reinterpret_cast<uint4*>(vst[st][sub] + lrow * KROW + lpc * 16) =
+          *reinterpret_cast<uint4*>(vst[st][sub] + lrow * VROW + lpc * 16) =
               live ? r[sub][j] : make_uint4(0u, 0u, 0u, 0u);
         }
       }
@@ -473,18 +476,18 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   // Online softmax of one row block's scores of a step (two tiles), kept
   // short because the VALU, not the matrix cores, sets this loop's pace, and
   // split in two so the exponentials of one row block can issue beside the
-  // other's value MFMAs. prep: masking only on `masked` steps (the diagonal
-  // and the odd tail, a wave-uniform choice) and the lazy-max test on the
+  // other's value MFMAs. prep: masking only in the `masked` variant (the
+  // diagonal and the odd tail, chosen per step) and the lazy-max test on the
   // raw scores' maximum (raising m and rescaling when needed). probs: one
   // FMA into each exponential, row sums of the fp16 probabilities by v_dot2
   // against ones; returns P in the value MFMA's k-slot order.
-  auto prep = [&](const float4_t (&acc)[2], int step, int lim, bool masked, float4_t (&o)[NDB], float& m,
+  auto prep = [&](const float4_t (&acc)[2], int step, int lim, auto masked, float4_t (&o)[NDB], float& m,
                   float& l, float (&a)[8]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[sub * 4 + e] = acc[sub][e];
-    if (masked) {
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const int tile = 2 * step + sub;
@@ -531,7 +534,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   // MFMAs would become branches that split the scheduling regions. After
   // both prep branches the remaining work is one region, ordered so the
   // second block's exponentials sit between the first block's value MFMAs.
-  auto step_rows = [&](int st, int step) {
+  auto step_rows = [&](int st, int step, auto masked) {
     float4_t acc0[2], acc1[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -544,14 +547,12 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
         acc1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q1[c], acc1[sub], 0, 0, 0);
       }
     }
-    // tokens below full_tokens are visible to every row: no mask before them
-    const bool masked = 2 * step + 1 >= nt || (MASK && (jb + 2 * step + 2) * BT > full_tokens);
     float a0[8], a1[8];
     prep(acc0, step, lim0, masked, o0, m0, l0, a0);
     prep(acc1, step, lim1, masked, o1, m1, l1, a1);
     const half8_t pt0 = probs(a0, m0, l0);
     // lane (n, j) addresses V[4j + n/4][16 i + 4 (n % 4)] of each tile
-    const int vofs = (4 * lj + (ln >> 2)) * KROW + (ln & 3) * 8;
+    const int vofs = (4 * lj + (ln >> 2)) * VROW + (ln & 3) * 8;
     half8_t va[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) {
@@ -580,21 +581,32 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   gload(PFS, ring[0]);
   __syncthreads();
   // Step it sits in LDS stage it & 1 and its successor in ring slot
-  // (it + 1) % PFS. The loop runs whole rounds of PFS (unrolled, so every
-  // slot index is a constant); past the last step only the math is skipped:
+  // (it + 1) % PFS. A loop runs whole rounds of PFS (unrolled, so every slot
+  // index is a constant); past its last step only the math is skipped:
   // loads and stores stay unconditional, and the compiler's count of loads
-  // in flight stays exact across the loop.
-  for (int it0 = 0; it0 < nsteps; it0 += PFS) {
+  // in flight stays exact across the loop. Two loops: the leading steps no
+  // row masks (whole rounds of them), then the rest with masks (the
+  // diagonal and the odd tail); separate loops keep the two variants'
+  // registers apart.
+  auto run = [&](int from, int to, auto masked) {
+    for (int it0 = from; it0 < to; it0 += PFS) {
 #pragma unroll
-    for (int u = 0; u < PFS; ++u) {
-      const int it = it0 + u;
-      const int st = u & 1;  // == it & 1: PFS is even
-      if (it < nsteps) step_rows(st, it);
-      lstore(st ^ 1, ring[(u + 1) % PFS], it + 1);
-      gload(it + 1 + PFS, ring[(u + 1) % PFS]);
-      __syncthreads();
+      for (int u = 0; u < PFS; ++u) {
+        const int it = it0 + u;
+        const int st = u & 1;  // == it & 1: `from` and PFS are even
+        if (it < to) step_rows(st, it, masked);
+        lstore(st ^ 1, ring[(u + 1) % PFS], it + 1);
+        gload(it + 1 + PFS, ring[(u + 1) % PFS]);
+        __syncthreads();
+      }
     }
-  }
+  };
+  // steps with both tiles real and every token visible to every row
+  int nfree = nt / 2;
+  if (MASK) nfree = min(nfree, max(0, (full_tokens / BT - jb) / 2));
+  nfree -= nfree % PFS;
+  run(0, nfree, std::false_type{});
+  run(nfree, nsteps, std::true_type{});
 
   // the row sums over the four token groups
   l0 += xor_shfl(l0, 16);
