@@ -389,6 +389,7 @@ def main():
         "graph_matches_eager_bitwise": graph_matches_eager,
         "host_issue_ms_per_step": round(host_ms, 4),
         "probe_read_GBps": None if probe is None else round(probe, 1),
+        "split_kernel_pct_of_probe": None if not probe else round(100.0 * split_gbps / probe, 1),
         "roofline": {
             "bound": "hbm",
             "kernel": "paged_decode_kernel<128,4,f16> (split-K decode)",
