@@ -227,7 +227,10 @@ typedef struct pkv_step_plan {  /* caller-owned arrays, capacities from
 int pkv_sched_limits(int32_t max_running, int32_t prefill_budget, int32_t* max_items, int32_t* max_slots);
 int pkv_sched_create(pkv_pool* pool, int32_t max_running, int32_t prefill_budget, pkv_sched** out);
 void pkv_sched_destroy(pkv_sched* sched);
-/* Queue a request (ids unique; n >= 1 prompt tokens; max_new >= 1). */
+/* Queue a request (ids unique; n >= 1 prompt tokens; max_new >= 1).
+ * INVALID_ARG for a request whose n + max_new tokens need more blocks than
+ * the whole pool (it could never run). Requests that fit the pool but find
+ * it held by sequences outside the scheduler wait until those are freed. */
 int pkv_sched_submit(pkv_sched* sched, int64_t req, const int32_t* prompt, int32_t n, int32_t max_new);
 /* Plan one step into `plan` (INVALID_ARG, nothing changed, if its arrays
  * are below the limits). */

@@ -15,6 +15,9 @@ void clear_error();
 // PKV_OK or INVALID_ARG/UNSUPPORTED with a message.
 int validate_config(const pkv_config* cfg);
 
+// Blocks of a pool (its configuration's num_blocks).
+int32_t pool_num_blocks(const pkv_pool* pool);
+
 inline int64_t elem_bytes(int32_t dtype) { return dtype == PKV_I8 ? 1 : 2; }
 
 // Elements in one (layer, block, KV head) tile: 16 rows of D.

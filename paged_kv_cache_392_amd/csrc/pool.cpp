@@ -148,6 +148,10 @@ int32_t cache_evict_one(pkv_pool* p) {
 
 }  // namespace
 
+namespace pkv {
+int32_t pool_num_blocks(const pkv_pool* pool) { return pool->cfg.num_blocks; }
+}  // namespace pkv
+
 extern "C" {
 
 int pkv_pool_create(const pkv_config* cfg, const int32_t* free_order, int32_t n, pkv_pool** out) {

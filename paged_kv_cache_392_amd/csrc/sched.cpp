@@ -133,6 +133,11 @@ int pkv_sched_submit(pkv_sched* s, int64_t req, const int32_t* prompt, int32_t n
   if (!s || !prompt) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL argument");
   if (n < 1 || max_new < 1) return pkv::fail(PKV_ERR_INVALID_ARG, "need a prompt and max_new >= 1");
   if (s->reqs.count(req)) return pkv::fail(PKV_ERR_INVALID_ARG, "request %lld already submitted", (long long)req);
+  // a request that cannot fit the whole pool would wait at the head of the queue forever
+  const int64_t blocks = (int64_t(n) + max_new + PKV_BLOCK_TOKENS - 1) / PKV_BLOCK_TOKENS;
+  if (blocks > pkv::pool_num_blocks(s->pool))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "request %lld needs %lld blocks, the pool has %d", (long long)req,
+                     (long long)blocks, pkv::pool_num_blocks(s->pool));
   auto r = std::make_unique<Request>();
   r->id = req;
   r->prompt_len = n;

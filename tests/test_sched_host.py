@@ -95,10 +95,13 @@ def test_planner_argument_checks():
         pkv.pkv_sched_submit(s, 1, [4], 1)
     with pytest.raises(pkv.PkvError):
         pkv.pkv_sched_submit(s, 2, [], 1)
+    with pytest.raises(pkv.PkvError):  # 120 + 9 tokens need 9 blocks, the pool has 8
+        pkv.pkv_sched_submit(s, 3, list(range(120)), 9)
+    pkv.pkv_sched_submit(s, 4, list(range(120)), 8)  # exactly 8 blocks: accepted
     small = pkv.StepPlan(1, 1)  # arrays sized for a smaller planner
     with pytest.raises(pkv.PkvError):
         pkv.pkv_sched_step(s, small)
-    assert pkv.pkv_sched_counts(s) == (1, 0, 0)  # nothing changed
+    assert pkv.pkv_sched_counts(s) == (2, 0, 0)  # nothing changed
     plan = pkv.StepPlan(2, 8)
     p = pkv.pkv_sched_step(s, plan)
     assert p["admitted"] == [(1, 0)] and p["items"][0][2:5] == (1, 0, 3)
