@@ -382,7 +382,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 // group j pointing at V[4j + s/4][16 i + 4 (s % 4)], lane (n, j) receives
 // V[4j..4j+3][16 i + n]: the A operand, 4 tokens of one dim. Online
 // softmax per row in base 2 with the lazy running max of the split kernel.
-template <int D, int MAXT, bool MASK, bool STREAM, typename QRow, typename Limit, typename Emit>
+template <int D, int MAXT, bool MASK, bool STREAM, int PFS, typename QRow, typename Limit, typename Emit>
 __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int Hkv, int g, int num_blocks,
                                             const int32_t* trow, int jb, int nt, int R, int nvalid,
                                             int full_tokens, float scale_log2, QRow qrow, Limit limit,
@@ -395,7 +395,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   constexpr int PIECES = D / 8;         // 16-byte pieces per K/V row
   constexpr int LOADERS = BT * PIECES;  // pieces per K (or V) tile
   constexpr int TILE = BT * D * 2;
-  constexpr int PFS = 2;                // steps (tile pairs) in flight per thread
+  // PFS: steps (tile pairs) in flight per thread
   static_assert(PFS % 2 == 0, "LDS stages alternate with the ring slot");
   __shared__ __align__(16) char kst[2][2][BT * KROW];
   __shared__ __align__(16) char vst[2][2][BT * VROW];
@@ -656,7 +656,7 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
       prm.part_l[pi] = l;
     }
   };
-  attend_rows<D, 64, false, true>(static_cast<const char*>(prm.K), static_cast<const char*>(prm.V), prm.Hkv, g,
+  attend_rows<D, 64, false, true, 2>(static_cast<const char*>(prm.K), static_cast<const char*>(prm.V), prm.Hkv, g,
                             prm.num_blocks, prm.tables + int64_t(b0) * prm.max_blocks, jb, je - jb, R, 0, 0,
                             prm.scale_log2, qrow, no_limit, emit);
 }
@@ -667,6 +667,8 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
 // Context a prefill work-group walks: at most 1024 tiles (16384 tokens), its
 // block ids staged in LDS.
 constexpr int PREFILL_MAX_TILES = 1024;
+// Steps (pairs of tiles) a prefill work-group keeps in flight.
+constexpr int PREFILL_PFS = 2;
 
 struct PrefillParams {
   const char* K;  // this layer's K region: [N][Hkv][16][D] fp16
@@ -718,7 +720,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
       *reinterpret_cast<half4_t*>(dst + 16 * i) = h;
     }
   };
-  attend_rows<D, PREFILL_MAX_TILES, true, false>(prm.K, prm.V, prm.Hkv, g, prm.num_blocks,
+  attend_rows<D, PREFILL_MAX_TILES, true, false, PREFILL_PFS>(prm.K, prm.V, prm.Hkv, g, prm.num_blocks,
                                           prm.tables + int64_t(b) * prm.max_blocks, 0, nt, R, n, pos0 + 1,
                                           prm.scale_log2, qrow, limit, emit);
 }
