@@ -315,6 +315,13 @@ __device__ __forceinline__ float row16_sum(float x) {
 __device__ __forceinline__ float read_lane(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
+// Entries 0..3 or 4..7 of an 8-entry per-head array, chosen by a flag that
+// varies across lanes, as one select between two vector values (a select
+// between two addresses in the array would move the array to scratch memory).
+__device__ __forceinline__ float4_t half_of8(const float (&x)[8], bool upper) {
+  const float4_t lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
+  return upper ? hi : lo;
+}
 
 // ---------------------------------------------------------------------------
 // shared-prefix attention
@@ -889,10 +896,16 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     for (int i = 0; i < S::NI; ++i) t.v[i] = load_nt(vb + (vt + S::RPI * i) * (D * S::E) + vd * 16);
   };
 
-  // running max of the head of score row e of this lane
-  auto mrow = [&](int e) -> float {
-    if constexpr (G == 8) return odd ? mh[4 + e] : mh[e];
-    else return mh[e % G];
+  // running max of the head of each of this lane's 4 score rows
+  auto mrows = [&]() -> float4_t {
+    if constexpr (G == 8) {
+      return half_of8(mh, odd);
+    } else {
+      float4_t r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = mh[e % G];
+      return r;
+    }
   };
 
   // int8: the K codes enter the MFMA as 1152 + x, so every score of head h
@@ -909,10 +922,16 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
 #pragma unroll
     for (int h = 0; h < G; ++h) qb[h] = I8_BIAS * read_lane(part, h);
   }
-  auto krow_bias = [&](int e) -> float {
-    if constexpr (G == 8) return odd ? qb[4 + e] : qb[e];
-    else return qb[e % G];
-  };
+  // (fixed for the whole stream: taken once per lane)
+  float4_t kbias = {0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (I8) {
+    if constexpr (G == 8) {
+      kbias = half_of8(qb, odd);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kbias[e] = qb[e % G];
+    }
+  }
   // int8 values: pairs of rows (i, i + 1) are contracted with v_dot2 on fp16
   // probabilities and biased codes; vb[h] collects the bias part to remove.
   constexpr bool PAIRS = I8 && S::NI >= 2;
@@ -947,12 +966,13 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     const bool tvalid = blk_ok && (j * BT + kn) < ctx;
     float s[4];
     bool need = false;
+    float4_t mr = mrows();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float raw = acc[e];
-      if constexpr (I8) raw -= krow_bias(e);  // remove 1152 * sum(q) of the biased codes
+      if constexpr (I8) raw -= kbias[e];  // remove 1152 * sum(q) of the biased codes
       s[e] = tvalid ? raw * kscale : -INFINITY;
-      need |= s[e] > mrow(e) + LAZY_MAX;
+      need |= s[e] > mr[e] + LAZY_MAX;
     }
     if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first tile
       float mx[G];
@@ -972,16 +992,20 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
         for (int e = 0; e < S::CE; ++e) o[h][e] *= alpha[h];
         vb[h] *= alpha[h];
       }
+      if constexpr (G == 8) {
+        const float4_t a4 = half_of8(alpha, odd);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (G == 8) lrow[e] *= odd ? alpha[4 + e] : alpha[e];
-        else lrow[e] *= alpha[e % G];
+        for (int e = 0; e < 4; ++e) lrow[e] *= a4[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lrow[e] *= alpha[e % G];
       }
+      mr = mrows();
     }
     float pr[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      pr[e] = tvalid ? exp2_fast(s[e] - mrow(e)) : 0.0f;
+      pr[e] = tvalid ? exp2_fast(s[e] - mr[e]) : 0.0f;
       lrow[e] += pr[e];
     }
     // hand the probabilities to the V lane mapping through LDS
