@@ -581,3 +581,42 @@ def test_c3_kv_utilisation_paged_vs_contiguous():
     print(f"C3 KV utilisation: paged {paged:.4f}, contiguous max-length {contiguous:.4f}")
     assert paged > 0.99 and contiguous < 0.7
     lib.close()
+
+
+def test_kernel_resource_report_parser():
+    """The build reads hipcc's kernel-resource-usage remarks into one row per
+    kernel (a hand-written remark block)."""
+    from paged_kv_cache_392_amd import build as B
+    text = "\n".join([
+        "k.hip:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
+        "    1 | void kern_a() {",
+        "      | ^",
+        "k.hip:1:1: remark:     VGPRs: 202 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     AGPRs: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     Occupancy [waves/SIMD]: 2 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     VGPRs Spill: 3 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     LDS Size [bytes/block]: 9472 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark:     VGPRs: 12 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    rows = B.parse_resources(text)
+    assert [r["name"] for r in rows] == ["kern_a", "kern_b"]
+    assert rows[0] == {"name": "kern_a", "vgprs": 202, "agprs": 0, "scratch": 16, "occupancy": 2,
+                       "vgpr_spill": 3, "lds": 9472}
+    assert rows[1] == {"name": "kern_b", "vgprs": 12}
+
+
+def test_kernels_use_no_scratch_memory():
+    """Every kernel of the built library, each decode, prefill and helper
+    instantiation, keeps its state in registers and LDS: no scratch memory,
+    no spills (from the resource report the build writes)."""
+    from paged_kv_cache_392_amd import build as B
+    if not os.path.exists(B.RESOURCES):
+        pytest.skip("library not built in this tree")
+    rows = [l.rstrip("\n").split("\t") for l in open(B.RESOURCES) if not l.startswith("#")]
+    names = [r[0] for r in rows]
+    assert sum("paged_decode_kernel" in n for n in names) == 16  # D in {64, 128} x G in {1, 2, 4, 8} x {f16, i8}
+    assert sum("prefill_kernel" in n for n in names) == 8
+    for r in rows:
+        assert r[3] == "0" and r[4] == "0" and r[5] == "0", r
