@@ -1196,23 +1196,34 @@ struct MergeParams {
 // M = max_p m_p, out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), in
 // logical order: the shared-prefix partials of the sequence's group (if it
 // has one), then its own split-K partitions, which follow them in the
-// sequence's partial row. One thread per output dim. Partials are read 16
-// at a time, all loads of a group in flight together (the first 16 with the
-// context length and the plan); across groups the running max is raised as
-// in the split kernel (up to 16 partials in all, this is exactly the
-// two-pass formula above). Sequences with a single partial were finished by
-// the split kernel.
-__global__ __launch_bounds__(128) void lse_reduce_kernel(MergeParams prm) {
+// sequence's partial row. A work-group of D x W threads (W = blockDim.y,
+// the number of partial streams): thread (d, w) folds output dim d of
+// partials w, w + W, ... (16 at a time, all loads of a group in flight
+// together, the first group with the context length and the plan; across
+// groups the running max is raised as in the split kernel), and with W > 1
+// the W results are combined through LDS in order w = 0, 1, ... by the same
+// formula. Several streams keep the chain of dependent loads short when
+// rows have many partials (short sequences cut into many partitions); with
+// few, one stream is cheaper. Sequences with a single partial were finished
+// by the split kernel.
+constexpr int MERGE_MAX_WAYS = 8;
+// Partial streams per merged row for launches whose rows hold up to
+// max_parts partials (measured on MI355X: one stream up to 32 partials).
+int merge_ways(int max_parts) { return max_parts <= 32 ? 1 : max_parts <= 128 ? 4 : MERGE_MAX_WAYS; }
+
+__global__ __launch_bounds__(1024) void lse_reduce_kernel(MergeParams prm) {
   constexpr int CH = 16;
   const int h = blockIdx.x, b = blockIdx.y, Hq = gridDim.x;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x, w = threadIdx.y, W = blockDim.y;  // blockDim = (D, W), D <= 128, W <= 8
   const int D = prm.D;
-  if (d >= D) return;
+  __shared__ float part_mo[MERGE_MAX_WAYS][128];
+  __shared__ float part_ml[MERGE_MAX_WAYS][2];
   const int64_t base = (int64_t(b) * Hq + h) * prm.max_parts;
   float m0[CH], l0[CH], o0[CH];
 #pragma unroll
   for (int u = 0; u < CH; ++u) {
-    const int64_t pi = base + (u < prm.max_parts ? u : 0);
+    const int p = w + W * u;
+    const int64_t pi = base + (p < prm.max_parts ? p : 0);
     m0[u] = prm.part_m[pi];
     l0[u] = prm.part_l[pi];
     o0[u] = prm.part_o[pi * D + d];
@@ -1220,24 +1231,25 @@ __global__ __launch_bounds__(128) void lse_reduce_kernel(MergeParams prm) {
   int sb, pre;
   seq_prefix(prm.plan, b, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
   const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
-  if (ctx <= 0) return;
+  if (ctx <= 0) return;  // uniform over the work-group
   const int nblk = (ctx + BT - 1) / BT;
   const int nparts = nblk > sb ? (nblk - sb + prm.part_blocks - 1) / prm.part_blocks : 0;
   if (pre == 0 && nparts <= 1) return;
   const int count = min(pre + nparts, prm.max_parts);
 
   float M = -INFINITY, L = 0.0f, O = 0.0f;
-  for (int p0 = 0; p0 < count; p0 += CH) {
+  for (int k0 = 0; w + W * k0 < count; k0 += CH) {
     float mv[CH], lv[CH], ov[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const bool ok = p0 + u < count;
-      if (p0 == 0) {
+      const int p = w + W * (k0 + u);
+      const bool ok = p < count;
+      if (k0 == 0) {
         mv[u] = ok ? m0[u] : -INFINITY;
         lv[u] = ok ? l0[u] : 0.0f;
         ov[u] = ok ? o0[u] : 0.0f;
       } else {
-        const int64_t pi = base + (ok ? p0 + u : 0);
+        const int64_t pi = base + (ok ? p : 0);
         mv[u] = ok ? prm.part_m[pi] : -INFINITY;
         lv[u] = ok ? prm.part_l[pi] : 0.0f;
         ov[u] = ok ? prm.part_o[pi * D + d] : 0.0f;
@@ -1259,7 +1271,28 @@ __global__ __launch_bounds__(128) void lse_reduce_kernel(MergeParams prm) {
       O += ov[u] * wt;
     }
   }
-  prm.out[(int64_t(b) * Hq + h) * D + d] = (_Float16)(L > 0.0f ? O / L : 0.0f);
+  const int64_t oi = (int64_t(b) * Hq + h) * D + d;
+  if (W == 1) {  // uniform over the launch
+    prm.out[oi] = (_Float16)(L > 0.0f ? O / L : 0.0f);
+    return;
+  }
+  part_mo[w][d] = O;
+  if (d == 0) {
+    part_ml[w][0] = M;
+    part_ml[w][1] = L;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  float Mt = -INFINITY;
+  for (int v = 0; v < W; ++v) Mt = fmaxf(Mt, part_ml[v][0]);
+  float Lt = 0.0f, Ot = 0.0f;
+  for (int v = 0; v < W; ++v) {
+    const float mw = part_ml[v][0];
+    const float wt = (mw == -INFINITY) ? 0.0f : exp2_fast(mw - Mt);
+    Lt += part_ml[v][1] * wt;
+    Ot += part_mo[v][d] * wt;
+  }
+  prm.out[oi] = (_Float16)(Lt > 0.0f ? Ot / Lt : 0.0f);
 }
 
 // Host -> device staging of small host metadata (block tables, lengths): one
@@ -1628,9 +1661,9 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   mg.prefix_pp = prm.prefix_pp;
   const dim3 rgrid(a->num_q_heads, a->num_seqs);
   if (ev[2] && ev[3])
-    hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, ev[2], ev[3], 0, mg);
+    hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(mp)), 0, s, ev[2], ev[3], 0, mg);
   else
-    hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim), 0, s, mg);
+    hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(mp)), 0, s, mg);
   return hip_status(hipGetLastError(), "lse_reduce launch");
 }
 
