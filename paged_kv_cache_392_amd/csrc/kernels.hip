@@ -1344,7 +1344,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 // 528-token partitions at 8K context, 86 us against 91-97 us for 1024-2048)
 // and about 512 for int8 (one round: 2048-token partitions, 49 us against
 // 64 us at 528, where a work-group's first-tile latency weighs on half the
-// bytes per tile). At least 4 blocks (one per wave) per partition.
+// bytes per tile). Partitions keep at least 16 blocks (four tiles per wave):
+// small launches cut finer spend their time starting work-groups (8
+// sequences at 1025 tokens: 14.0 us at 64-token partitions, 10.0 at 256; a
+// 16-sequence 8K batch on one KV head: 20.5 us at 80 tokens, 14.4 at 512).
+// The partitions of the longest sequence are then made equal.
+constexpr int MIN_PART_BLOCKS = 16;
 int choose_part_blocks(const pkv_config& c, int B, int max_context, int partition_tokens) {
   if (partition_tokens == 0) {
     if (const char* env = std::getenv("PKV_PARTITION_TOKENS")) partition_tokens = std::atoi(env);
@@ -1356,8 +1361,10 @@ int choose_part_blocks(const pkv_config& c, int B, int max_context, int partitio
   int64_t want_parts = (want_wgs + groups - 1) / groups;
   if (want_parts < 1) want_parts = 1;
   int pb = int((nblk + want_parts - 1) / want_parts);
-  if (pb < 4) pb = 4;
-  return std::min(pb, MAX_PARTITION_TOKENS / BT);
+  pb = std::min(std::max(pb, MIN_PART_BLOCKS), MAX_PARTITION_TOKENS / BT);
+  const int parts = (nblk + pb - 1) / pb;
+  pb = (nblk + parts - 1) / parts;
+  return std::max(pb, WAVES);  // at least one block per wave
 }
 
 int max_parts_for(int max_context, int part_blocks) {
