@@ -1407,6 +1407,12 @@ int64_t workspace_bytes_for(const pkv_config& c, int B, int Hq, int max_parts) {
 // a 2048-token prefix run best at 96 work-groups of 11 blocks, 64 over two
 // 4096-token prefixes at 160 of 26).
 constexpr int PREFIX_TARGET_WGS = 128;
+// With the plan's host copy the launch knows each group's shared blocks and
+// cuts the longest run into partitions of about this many blocks (at most
+// as many as the workspace holds): 32 sequences over a 2048-token prefix
+// 25.8 -> 23.7-24.5 us at 16-22 blocks, one 4096-token prefix 26.9 -> 25.7
+// at 32, two 3000-token prefixes best at 32.
+constexpr int PREFIX_PART_BLOCKS = 28;
 int prefix_partitions(int Hkv, int n_groups, int max_blocks) {
   const int64_t lo = (int64_t(max_blocks) + 63) / 64;  // <= 64 blocks: the block ids staged in LDS
   const int64_t hi = std::max<int64_t>(lo, (max_blocks + 15) / 16);
@@ -1588,7 +1594,19 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
     return pkv::fail(PKV_ERR_INVALID_ARG, "workspace too small: need %lld bytes", (long long)need);
   if (need > 0 && !aligned16(a->workspace_dev))
     return pkv::fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if (int64_t(wl.prefix_z) + mp0 > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many partitions for one launch");
+  // prefix partitions of this launch: the workspace's count, or fewer when
+  // the plan's host copy shows shorter shared runs
+  int pp = wl.prefix_pp, pz = wl.prefix_z;
+  if (plan && a->prefix_plan_host) {
+    int max_np = 1;
+    for (int gi = 0; gi < a->prefix_groups; ++gi)
+      max_np = std::max(max_np, std::min(a->prefix_plan_host[2 * int64_t(a->num_seqs) +
+                                                           int64_t(gi) * PKV_PREFIX_GROUP_INTS],
+                                         a->max_blocks));
+    pp = std::min(pp, std::max(1, (max_np + PREFIX_PART_BLOCKS - 1) / PREFIX_PART_BLOCKS));
+    pz = int((int64_t(pp) * a->prefix_groups + a->num_seqs - 1) / a->num_seqs);
+  }
+  if (int64_t(pz) + mp0 > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many partitions for one launch");
 
   // With a plan and both host copies, partitions are sized for the longest
   // stretch the split role covers (a grouped sequence's unshared tail, an
@@ -1627,8 +1645,8 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   prm.part_o = parts ? ws + 2 * rows : nullptr;
   prm.out = static_cast<_Float16*>(a->out_dev);
   prm.plan = plan ? a->prefix_plan_dev : nullptr;
-  prm.prefix_z = wl.prefix_z;
-  prm.prefix_pp = wl.prefix_pp;
+  prm.prefix_z = pz;
+  prm.prefix_pp = pp;
   prm.num_groups = plan ? a->prefix_groups : 0;
   prm.max_blocks = a->max_blocks;
   prm.num_blocks = c.num_blocks;
@@ -1645,7 +1663,7 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
 
   // The fused append (if any) writes into private tail blocks only, which no
   // shared-prefix work-group reads.
-  const dim3 grid(c.num_kv_heads, a->num_seqs, wl.prefix_z + mp0);
+  const dim3 grid(c.num_kv_heads, a->num_seqs, pz + mp0);
   if (ev[0] && ev[1])
     hipExtLaunchKernelGGL(fn, grid, dim3(256), 0, s, ev[0], ev[1], 0, prm);
   else
