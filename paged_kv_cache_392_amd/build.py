@@ -2,8 +2,9 @@
 
 Host files (allocator, errors) are plain C++17 built with g++; the kernels
 and their launchers are HIP built with hipcc for --offload-arch=gfx950; the
-shared library is linked by hipcc against the HIP runtime. Run as
-``python -m paged_kv_cache_392_amd.build`` or through
+shared library is linked by hipcc against the HIP runtime. Run as a script,
+``python paged_kv_cache_392_amd/build.py`` (importing the package opens the
+library, so ``python -m`` cannot build it the first time), or through
 ``__graft_entry__.build()``.
 """
 

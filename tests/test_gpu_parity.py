@@ -543,6 +543,59 @@ def test_c4_prefix_plan_and_fused_append():
     fused.close()
 
 
+def test_shared_prefix_plan_without_host_copies():
+    """The host copies of the plan and of the lengths are optional: without
+    them a plan launch keeps the workspace's prefix-partition count and sizes
+    split partitions from max_context alone. The output still matches the
+    oracle."""
+    import ctypes
+    from paged_kv_cache_392_amd import _capi as C
+    from paged_kv_cache_392_amd.cache import PrefixPlan
+    w = workloads.prefix_forest(49, groups=((1500, 12), (600, 5)), singles=2, suffix=(0, 500))
+    lib, o = run_pair(w, prefix_plan={})
+    rec, ref = lib.decodes[0], o.decodes[0]["out"]
+    plan_host, ng = rec["plan"]
+    assert ng == 2
+    B, Hq, D = len(rec["lens"]), w.num_q_heads, w.head_dim
+    plan = PrefixPlan(plan_host, ng, B, DEV)
+    td = torch.from_numpy(rec["tables"]).to(DEV)
+    ld = torch.from_numpy(rec["lens"]).to(DEV)
+    qd = torch.from_numpy(rec["q"]).to(DEV)
+    max_blocks, max_context = rec["tables"].shape[1], int(rec["lens"].max())
+    nb = pkv.pkv_prefix_decode_workspace_bytes(lib.cache.cfg, B, Hq, max_context, max_blocks, 0, ng)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device=DEV)
+    a = C.pkv_decode_args()
+    a.cfg = ctypes.pointer(lib.cache.cfg)
+    a.pool_dev = lib.cache.pool.data_ptr()
+    a.layer = 0
+    a.q_dev = qd.data_ptr()
+    a.num_seqs = B
+    a.num_q_heads = Hq
+    a.block_tables_dev = td.data_ptr()
+    a.max_blocks = max_blocks
+    a.ctx_lens_dev = ld.data_ptr()
+    a.ctx_lens_host = None
+    a.max_context = max_context
+    a.out_dev = out.data_ptr()
+    a.scale = 1.0 / math.sqrt(D)
+    a.workspace_dev = ws.data_ptr()
+    a.workspace_bytes = nb
+    a.prefix_plan_dev = plan.dev.data_ptr()
+    a.prefix_plan_host = None
+    a.prefix_groups = ng
+    announce(f"plan without host copies: B={B} groups={ng}")
+    C.pkv_paged_decode(a, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    err = float(np.abs(got.astype(np.float64) - ref).max())
+    assert err <= F16_TOL, err
+    with_host = float(np.abs(got.astype(np.float64) - rec["out"].astype(np.float64)).max())
+    assert with_host <= F16_TOL, with_host
+    lib.close()
+
+
 def test_shared_prefix_plan_graph_replay_and_determinism():
     """A plan decode captured into a HIP graph: every replay (with eager
     decodes of another batch between them) gives the eager result bit for
