@@ -386,7 +386,10 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * it the plan is trusted: a wrong plan gives wrong results, never an
  * out-of-bounds access). With both host copies (lengths and plan) and
  * automatic partitions, split-K partitions are sized for the longest
- * unshared stretch instead of max_context.
+ * unshared stretch instead of max_context. With the plan's host copy the
+ * launch also cuts shared runs into prefix partitions of about 28 blocks
+ * (never more partitions than the workspace holds); without it, into as
+ * many as the workspace holds. The output is the same up to rounding.
  *
  * With k_new_dev/v_new_dev set, the call also performs the append step of
  * [p2] §2.2 for every sequence (one token each) before attending: the

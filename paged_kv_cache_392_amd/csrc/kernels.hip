@@ -1,5 +1,6 @@
 // gfx950 kernels of libpkv and their C-ABI launchers: KV append, block copy,
-// paged decode (split-K, fp16 or int8 K/V) and the log-sum-exp merge.
+// paged decode (split-K, fp16 or int8 K/V, optionally with shared-prefix
+// work-groups), the log-sum-exp merge, and causal paged prefill.
 //
 // Paged decode follows the pages' statement of the problem: one new query
 // token per sequence attends, softmax(q K^T / sqrt(d)) V ([p2]
@@ -20,9 +21,9 @@
 //     with 16-byte loads, double-buffered so the next tile is in flight
 //     while the current one is used; the loaded K tile serves all G query
 //     heads of the group;
-//   * scores: lane (t = lane/4, kq = lane%4) holds row t and one quarter of
-//     the head dimension, does fp16 pair dot products into fp32
-//     (v_dot2_f32_f16) and a 2-step DPP quad reduction;
+//   * scores on the matrix cores: one v_mfma_f32_16x16x32_f16 per 32 head
+//     dims gives the G heads' scores of the tile's 16 tokens, each lane
+//     receiving fully reduced scores of its token;
 //   * softmax: base-2 online softmax with a wave-uniform running max that is
 //     raised only when a score exceeds it by more than 8 (in log2 units), so
 //     the rescale of the accumulators is a rare, wave-uniform branch;
@@ -34,6 +35,11 @@
 //     partition; a second kernel merges partitions by log-sum-exp.
 // The reduction order depends only on logical token positions, so the result
 // is bitwise independent of where the blocks live.
+//
+// With a shared-prefix plan, extra work-groups of the same launch attend the
+// shared blocks of a group of sequences once for all their query rows
+// (attend_rows, on the matrix cores); the paged prefill kernel runs the same
+// multi-row attention, causally, for a chunk of new tokens.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
