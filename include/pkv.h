@@ -338,8 +338,8 @@ typedef struct pkv_decode_args {
                                      pkv_plan_shared_prefix's output for these
                                      sequences in this order, uploaded. Each
                                      group's shared blocks are read once for all
-                                     its members (fp16 pools). Same result up to
-                                     rounding.                                   */
+                                     its members (fp16 and int8 pools). Same
+                                     result up to rounding.                      */
   const int32_t* prefix_plan_host;/* optional host copy, validated if non-NULL    */
   int32_t prefix_groups;          /* groups in the plan (0 = no plan)             */
   void* const* timing_events;     /* optional (NULL = none): 4 hipEvent_t recorded
@@ -381,7 +381,8 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * sequence from its first unshared block, and the merge combines prefix and
  * suffix partials in logical order. The workspace must hold
  * pkv_prefix_decode_workspace_bytes() bytes. Members x (Hq/Hkv) must not
- * exceed 128; a plan with prefix_groups > 0 on an int8 pool is UNSUPPORTED;
+ * exceed 128. On int8 pools the shared tiles are dequantised (code x block
+ * scale, rounded to fp16) as they are staged for the matrix cores;
  * INVALID_ARG for an inconsistent plan when the host copy is given (without
  * it the plan is trusted: a wrong plan gives wrong results, never an
  * out-of-bounds access). With both host copies (lengths and plan) and
@@ -444,11 +445,13 @@ typedef struct pkv_prefill_args {
  * h / (Hq/Hkv). The K/V rows are read in place through the block table.
  * fp32 accumulation, fp16 probabilities in the value product, fp16 output
  * (nearest even). The chunk's K/V must already be in the cache
- * (pkv_append_kv). fp16 pools; head_dim 64 or 128. No workspace.
+ * (pkv_append_kv). fp16 or int8 pools (int8 tiles dequantised, code x
+ * block scale rounded to fp16, as they are staged); head_dim 64 or 128. No
+ * workspace.
  * INVALID_ARG: null pointers, q_start not starting at 0 or decreasing,
  * misalignment, a chunk longer than its context or a context out of range
- * (host copies). UNSUPPORTED: int8 pools, group size or head_dim not built,
- * a context above 16384 tokens. Sequences with qlen_b = 0 are skipped. */
+ * (host copies). UNSUPPORTED: group size or head_dim not built, a context
+ * above 16384 tokens. Sequences with qlen_b = 0 are skipped. */
 int pkv_paged_prefill(const pkv_prefill_args* args, void* stream);
 
 /* Upload host metadata for the next step (block tables, lengths: the

@@ -116,6 +116,22 @@ __device__ __forceinline__ void i8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t
   hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, b) - bias);
 }
 
+// Sixteen int8 codes (one 16-byte piece of a row) times their block's scale
+// (both halves of s2), as sixteen fp16 values in two 16-byte pieces, in
+// order. The codes are exact in fp16; the product is rounded once.
+__device__ __forceinline__ void dequant16(const uint4& c, uint32_t s2, uint4& a, uint4& b) {
+  const half2_t s = __builtin_bit_cast(half2_t, s2);
+  uint32_t x[8];
+  i8x4_to_f16x4(c.x, x[0], x[1]);
+  i8x4_to_f16x4(c.y, x[2], x[3]);
+  i8x4_to_f16x4(c.z, x[4], x[5]);
+  i8x4_to_f16x4(c.w, x[6], x[7]);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, x[k]) * s);
+  a = make_uint4(x[0], x[1], x[2], x[3]);
+  b = make_uint4(x[4], x[5], x[6], x[7]);
+}
+
 // The same codes biased by 1152: two halves holding 1152 + x, exact (no
 // subtraction). Sums over biased codes are corrected once per head.
 __device__ __forceinline__ void i8x4_to_f16x4_biased(uint32_t w, uint32_t& lo, uint32_t& hi) {
@@ -395,9 +411,9 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 // group j pointing at V[4j + s/4][16 i + 4 (s % 4)], lane (n, j) receives
 // V[4j..4j+3][16 i + n]: the A operand, 4 tokens of one dim. Online
 // softmax per row in base 2 with the lazy running max of the split kernel.
-template <int D, int MAXT, bool MASK, bool STREAM, int PFS, typename QRow, typename Limit, typename Emit>
-__device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int Hkv, int g, int num_blocks,
-                                            const int32_t* trow, int jb, int nt, int R, int nvalid,
+template <int D, int MAXT, bool MASK, bool STREAM, int PFS, bool I8, typename QRow, typename Limit, typename Emit>
+__device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, const uint32_t* scales, int Hkv, int g,
+                                            int num_blocks, const int32_t* trow, int jb, int nt, int R, int nvalid,
                                             int full_tokens, float scale_log2, QRow qrow, Limit limit,
                                             Emit emit) {
   constexpr int NCH = D / 32;           // score MFMA chunks
@@ -405,19 +421,29 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   constexpr int KROW = D * 2 + 16;      // bytes per staged K row (16 lanes read 16 rows without conflicts)
   constexpr int VROW = D * 2 + 32;      // bytes per staged V row (the transpose read's 4-row groups
                                         // start 8 banks apart)
-  constexpr int PIECES = D / 8;         // 16-byte pieces per K/V row
+  constexpr int E = I8 ? 1 : 2;         // bytes per element in the pool
+  constexpr int PIECES = D * E / 16;    // 16-byte pieces per K/V row in the pool
   constexpr int LOADERS = BT * PIECES;  // pieces per K (or V) tile
-  constexpr int TILE = BT * D * 2;
+  constexpr int TILE = BT * D * E;      // pool bytes per (block, KV head) tile
   // PFS: steps (tile pairs) in flight per thread
   static_assert(PFS % 2 == 0, "LDS stages alternate with the ring slot");
   __shared__ __align__(16) char kst[2][2][BT * KROW];
   __shared__ __align__(16) char vst[2][2][BT * VROW];
   __shared__ int blk_ids[MAXT];
+  __shared__ uint32_t tile_sc[I8 ? MAXT : 1];  // int8: each tile's (K, V) fp16 scales
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lj = lane >> 4;
-  for (int i = tid; i < nt; i += 256) blk_ids[i] = trow[jb + i];
+  if constexpr (I8) {
+    for (int i = tid; i < nt; i += 256) {
+      const int blk = trow[jb + i];
+      blk_ids[i] = blk;
+      tile_sc[i] = unsigned(blk) < unsigned(num_blocks) ? scales[int64_t(blk) * Hkv + g] : 0u;
+    }
+  } else {
+    for (int i = tid; i < nt; i += 256) blk_ids[i] = trow[jb + i];
+  }
   const int nsteps = (nt + 1) / 2;
 
   // q^T as the B operand of the score MFMA, per row block of this wave
@@ -442,10 +468,13 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
   float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.0f, l1 = 0.0f;
 
   // Tile staging: a tile is 2 x LOADERS 16-byte pieces (K, then V), each
-  // piece along a row; thread t moves pieces t + 256 j. Steps are fetched
-  // PFS ahead into a register ring; the loads are unconditional (tiles past
-  // the last re-read it) so the compiler counts outstanding loads statically.
-  constexpr int NLD = 2 * LOADERS / 256;
+  // piece along a row; thread t moves pieces t + 256 j (int8 at D = 64: only
+  // threads below 2 x LOADERS). Steps are fetched PFS ahead into a register
+  // ring; the loads are unconditional (tiles past the last re-read it) so the
+  // compiler counts outstanding loads statically. int8 pieces are
+  // dequantised with their tile's scale as they are stored, so LDS always
+  // holds fp16.
+  constexpr int NLD = (2 * LOADERS + 255) / 256;
   uint4 ring[PFS][2][NLD];
   auto piece = [&](int q, int& lrow, int& lpc) {
     const int pc = q % LOADERS;
@@ -461,9 +490,10 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int q = tid + 256 * j;
+        if (I8 && q >= 2 * LOADERS) continue;  // int8 at D = 64 only; uniform per wave
         int lrow, lpc;
         piece(q, lrow, lpc);
-        r[sub][j] = load_tile<STREAM>((q < LOADERS ? Kc : Vc) + base + lrow * (D * 2) + lpc * 16);
+        r[sub][j] = load_tile<STREAM>((q < LOADERS ? Kc : Vc) + base + lrow * (D * E) + lpc * 16);
       }
     }
   };
@@ -474,13 +504,26 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
       for (int j = 0; j < NLD; ++j) {
         const int q = tid + 256 * j;
         int lrow, lpc;
-        piece(q, lrow, lpc);
-        if (q < LOADERS) {
-          *reinterpret_cast<uint4*>(kst[st][sub] + lrow * KROW + lpc * 16) = r[sub][j];
+        if constexpr (I8) {
+          if (q >= 2 * LOADERS) continue;
+          piece(q, lrow, lpc);
+          const bool live = q < LOADERS || !MASK || (jb + 2 * step + sub) * BT + lrow < nvalid;
+          char* dst = q < LOADERS ? kst[st][sub] + lrow * KROW : vst[st][sub] + lrow * VROW;
+          const uint32_t sc = tile_sc[min(2 * step + sub, nt - 1)];
+          const uint32_t s1 = q < LOADERS ? (sc & 0xffffu) : (sc >> 16);  // K or V scale
+          uint4 a, b;
+          dequant16(r[sub][j], s1 | (s1 << 16), a, b);
+          *reinterpret_cast<uint4*>(dst + lpc * 32) = live ? a : make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(dst + lpc * 32 + 16) = live ? b : make_uint4(0u, 0u, 0u, 0u);
         } else {
-          const bool live = !MASK || (jb + 2 * step + sub) * BT + lrow < nvalid;
-          *reinterpret_cast<uint4*>(vst[st][sub] + lrow * VROW + lpc * 16) =
-              live ? r[sub][j] : make_uint4(0u, 0u, 0u, 0u);
+          piece(q, lrow, lpc);
+          if (q < LOADERS) {
+            *reinterpret_cast<uint4*>(kst[st][sub] + lrow * KROW + lpc * 16) = r[sub][j];
+          } else {
+            const bool live = !MASK || (jb + 2 * step + sub) * BT + lrow < nvalid;
+            *reinterpret_cast<uint4*>(vst[st][sub] + lrow * VROW + lpc * 16) =
+                live ? r[sub][j] : make_uint4(0u, 0u, 0u, 0u);
+          }
         }
       }
     }
@@ -636,7 +679,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, int 
 // by all R = members x G query rows. Shared blocks are full, so nothing is
 // masked. Each row ends as one (m, l, o[D]) partial, written into slot
 // `part` of the member's own partial row, ahead of its split-K partials.
-template <int D, int G>
+template <int D, int G, bool I8>
 __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int grp, int part) {
   constexpr int NDB = D / 16;
   const int lj = (threadIdx.x & 63) >> 4;
@@ -669,9 +712,10 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
       prm.part_l[pi] = l;
     }
   };
-  attend_rows<D, 64, false, true, 2>(static_cast<const char*>(prm.K), static_cast<const char*>(prm.V), prm.Hkv, g,
-                            prm.num_blocks, prm.tables + int64_t(b0) * prm.max_blocks, jb, je - jb, R, 0, 0,
-                            prm.scale_log2, qrow, no_limit, emit);
+  attend_rows<D, 64, false, true, 2, I8>(static_cast<const char*>(prm.K), static_cast<const char*>(prm.V),
+                                         reinterpret_cast<const uint32_t*>(prm.scales), prm.Hkv, g, prm.num_blocks,
+                                         prm.tables + int64_t(b0) * prm.max_blocks, jb, je - jb, R, 0, 0,
+                                         prm.scale_log2, qrow, no_limit, emit);
 }
 
 // ---------------------------------------------------------------------------
@@ -691,6 +735,7 @@ struct PrefillParams {
   const int32_t* tables;    // [B][max_blocks]
   const int32_t* ctx_lens;  // [B]: cached tokens, the chunk's own included
   _Float16* out;            // [T][Hq][D]
+  const uint32_t* scales;   // int8: this layer's (K, V) fp16 scales [N][Hkv]; else null
   int Hkv, max_blocks, num_blocks, max_context, qtiles;
   float scale_log2;
 };
@@ -704,7 +749,7 @@ struct PrefillParams {
 // chunk sits at logical position ctx - qlen + i and sees tokens 0..itself;
 // the work-group walks tiles 0 .. that of its last token, masking per row.
 // Query tiles are dispatched latest first (they walk the most tiles).
-template <int D, int G>
+template <int D, int G, bool I8>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
   constexpr int NDB = D / 16;
   constexpr int QT = PREFIX_ROWS / G;  // query tokens per work-group
@@ -733,9 +778,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
       *reinterpret_cast<half4_t*>(dst + 16 * i) = h;
     }
   };
-  attend_rows<D, PREFILL_MAX_TILES, true, false, PREFILL_PFS>(prm.K, prm.V, prm.Hkv, g, prm.num_blocks,
-                                          prm.tables + int64_t(b) * prm.max_blocks, 0, nt, R, n, pos0 + 1,
-                                          prm.scale_log2, qrow, limit, emit);
+  attend_rows<D, PREFILL_MAX_TILES, true, false, PREFILL_PFS, I8>(prm.K, prm.V, prm.scales, prm.Hkv, g,
+                                                                  prm.num_blocks,
+                                                                  prm.tables + int64_t(b) * prm.max_blocks, 0, nt,
+                                                                  R, n, pos0 + 1, prm.scale_log2, qrow, limit, emit);
 }
 
 // Two work-groups per CU are asked of the register allocator where they
@@ -767,12 +813,10 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
   // With a shared-prefix plan the first prefix_z planes of the grid are
   // shared-prefix work-groups: dispatched first, they run beside the split
   // work-groups of the same launch.
-  if constexpr (!I8) {
-    if (int(blockIdx.z) < prm.prefix_z) {
-      const int k = blockIdx.y + gridDim.y * blockIdx.z;
-      if (k < prm.prefix_pp * prm.num_groups) prefix_role<D, G>(prm, g, k / prm.prefix_pp, k % prm.prefix_pp);
-      return;
-    }
+  if (int(blockIdx.z) < prm.prefix_z) {
+    const int k = blockIdx.y + gridDim.y * blockIdx.z;
+    if (k < prm.prefix_pp * prm.num_groups) prefix_role<D, G, I8>(prm, g, k / prm.prefix_pp, k % prm.prefix_pp);
+    return;
   }
   const int p = blockIdx.z - prm.prefix_z;
   const int Hkv = prm.Hkv, Hq = Hkv * G;
@@ -1571,7 +1615,6 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   const bool plan = a->prefix_groups > 0;
   if (a->prefix_groups < 0) return pkv::fail(PKV_ERR_INVALID_ARG, "prefix_groups must be >= 0");
   if (plan && !a->prefix_plan_dev) return pkv::fail(PKV_ERR_INVALID_ARG, "prefix_groups > 0 needs prefix_plan_dev");
-  if (plan && c.dtype != PKV_F16) return pkv::fail(PKV_ERR_UNSUPPORTED, "shared-prefix plans need fp16 pools");
   if (plan && a->prefix_groups > a->num_seqs / 2)
     return pkv::fail(PKV_ERR_INVALID_ARG, "more groups (%d) than pairs of sequences", a->prefix_groups);
   if (plan && a->prefix_plan_host) {
@@ -1722,7 +1765,6 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   if (a->num_q_heads < 1 || a->num_q_heads % c.num_kv_heads)
     return pkv::fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", a->num_q_heads,
                      c.num_kv_heads);
-  if (c.dtype != PKV_F16) return pkv::fail(PKV_ERR_UNSUPPORTED, "paged prefill reads fp16 pools");
   if (a->max_blocks < 1 || a->max_context < 1)
     return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks and max_context must be >= 1");
   if (std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context) > int64_t(PREFILL_MAX_TILES) * BT)
@@ -1741,12 +1783,17 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   }
   typedef void (*fn_t)(PrefillParams);
   fn_t fn = nullptr;
+  const bool i8 = c.dtype == PKV_I8;
   if (c.head_dim == 128) {
-    fn = G == 1 ? prefill_kernel<128, 1> : G == 2 ? prefill_kernel<128, 2> : G == 4 ? prefill_kernel<128, 4>
-       : G == 8 ? prefill_kernel<128, 8> : nullptr;
+    fn = G == 1 ? (i8 ? prefill_kernel<128, 1, true> : prefill_kernel<128, 1, false>)
+       : G == 2 ? (i8 ? prefill_kernel<128, 2, true> : prefill_kernel<128, 2, false>)
+       : G == 4 ? (i8 ? prefill_kernel<128, 4, true> : prefill_kernel<128, 4, false>)
+       : G == 8 ? (i8 ? prefill_kernel<128, 8, true> : prefill_kernel<128, 8, false>) : nullptr;
   } else if (c.head_dim == 64) {
-    fn = G == 1 ? prefill_kernel<64, 1> : G == 2 ? prefill_kernel<64, 2> : G == 4 ? prefill_kernel<64, 4>
-       : G == 8 ? prefill_kernel<64, 8> : nullptr;
+    fn = G == 1 ? (i8 ? prefill_kernel<64, 1, true> : prefill_kernel<64, 1, false>)
+       : G == 2 ? (i8 ? prefill_kernel<64, 2, true> : prefill_kernel<64, 2, false>)
+       : G == 4 ? (i8 ? prefill_kernel<64, 4, true> : prefill_kernel<64, 4, false>)
+       : G == 8 ? (i8 ? prefill_kernel<64, 8, true> : prefill_kernel<64, 8, false>) : nullptr;
   }
   if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", G);
   const int QT = PREFIX_ROWS / G;
@@ -1763,6 +1810,9 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   prm.tables = a->block_tables_dev;
   prm.ctx_lens = a->ctx_lens_dev;
   prm.out = static_cast<_Float16*>(a->out_dev);
+  prm.scales = i8 ? reinterpret_cast<const uint32_t*>(base + 2 * pkv::region_bytes(c) +
+                                                     int64_t(a->layer) * c.num_blocks * c.num_kv_heads * 2 * 2)
+                  : nullptr;
   prm.Hkv = c.num_kv_heads;
   prm.max_blocks = a->max_blocks;
   prm.num_blocks = c.num_blocks;

@@ -512,6 +512,29 @@ def test_shared_prefix_plan_matches_oracle(seed, groups, singles, Hq, Hkv, D, ma
     lib.close()
 
 
+@pytest.mark.parametrize("seed,groups,singles,Hq,Hkv,D", [
+    (51, ((700, 6), (333, 3)), 2, 32, 8, 128),
+    (52, ((517, 5),), 1, 4, 2, 64),
+])
+def test_shared_prefix_plan_int8(seed, groups, singles, Hq, Hkv, D):
+    """A shared-prefix plan on an int8 pool: the prefix work-groups dequantise
+    the shared tiles as they stage them; the output is within the int8 bar
+    of the oracle and of the same decode without a plan."""
+    w = workloads.prefix_forest(seed, groups=groups, singles=singles, Hq=Hq, Hkv=Hkv, D=D, suffix=(0, 400),
+                                dtype="i8")
+    lib, o = run_pair(w, prefix_plan={})
+    assert lib.decodes[0]["plan"][1] >= len(groups)
+    check_stored_int8(lib, o)
+    err = max_err(lib, o)
+    announce(f"int8 plan max abs err {err:.3g}")
+    assert err <= I8_TOL
+    plain = LibRun(w, device=DEV, quantised=o.q8).run()
+    diff = float(np.abs(plain.decodes[0]["out"].astype(np.float64) - lib.decodes[0]["out"].astype(np.float64)).max())
+    assert diff <= I8_TOL, diff
+    plain.close()
+    lib.close()
+
+
 @pytest.mark.parametrize("ptok", [16, 64, 512])
 def test_shared_prefix_plan_partition_sizes(ptok):
     w = workloads.prefix_forest(47, groups=((1200, 8),), singles=2, suffix=(0, 900))
@@ -660,6 +683,26 @@ def test_prefill_matches_oracle(seed, cached, chunk, Hq, Hkv, D):
     err = prefill_err(lib, o)
     announce(f"prefill max abs err {err:.3g}")
     assert err <= F16_TOL
+    lib.close()
+
+
+@pytest.mark.parametrize("seed,cached,chunk,Hq,Hkv,D", [
+    (71, [0, 40, 700], [300, 33, 129], 32, 8, 128),  # fresh and chunked, int8 pool
+    (72, [5, 0], [100, 64], 8, 2, 64),  # d64: half the threads stage the tiles
+    (73, [0], [257], 16, 2, 128),  # 8 q heads per KV head
+])
+def test_prefill_int8_matches_oracle(seed, cached, chunk, Hq, Hkv, D):
+    """Paged prefill over an int8 pool (every token quantised on write): the
+    tiles are dequantised with their block's scales as they are staged; the
+    stored codes and scales are bit-exact and the output is within the int8
+    bar of the oracle on the dequantised values."""
+    w = workloads.prefill_chunks(seed, cached, chunk, Hq, Hkv, D, dtype="i8")
+    lib, o = run_pair(w)
+    check_host_records(lib, o)
+    check_stored_int8(lib, o)
+    err = prefill_err(lib, o)
+    announce(f"int8 prefill max abs err {err:.3g}")
+    assert err <= I8_TOL
     lib.close()
 
 

@@ -506,8 +506,6 @@ def test_decode_plan_validated_before_launch():
     bad = plan()
     bad[2] = 1  # member 1's run differs from the group's
     assert call(bad) == C.PKV_ERR_INVALID_ARG
-    i8 = pkv.make_config(1, 64, 2, 64, "i8")
-    assert call(plan(), c=i8) == C.PKV_ERR_UNSUPPORTED
     # 8 query heads per KV head: 17 members are 136 query rows, over 128
     assert call(plan(members=tuple(range(17))), Hq=16) == C.PKV_ERR_INVALID_ARG
     bad = plan(members=tuple(range(32)))
@@ -547,7 +545,6 @@ def test_prefill_validated_before_launch():
     assert call([0, 5, 8], layer=1) == C.PKV_ERR_INVALID_ARG
     assert call([0, 5, 8], Hq=6) == C.PKV_ERR_UNSUPPORTED  # 3 q heads per KV head
     assert call([0, 5, 8], Hq=5) == C.PKV_ERR_INVALID_ARG
-    assert call([0, 5, 8], c=pkv.make_config(1, 64, 2, 64, "i8")) == C.PKV_ERR_UNSUPPORTED
     assert call([0, 5, 8], max_context=20000, max_blocks=2000, host_lens=False) == C.PKV_ERR_UNSUPPORTED
     lens[0] = 0
     assert call([0, 0, 8]) == C.PKV_ERR_INVALID_ARG  # a context of 0 tokens
@@ -617,7 +614,7 @@ def test_kernels_use_no_scratch_memory():
     rows = [l.rstrip("\n").split("\t") for l in open(B.RESOURCES) if not l.startswith("#")]
     names = [r[0] for r in rows]
     assert sum("paged_decode_kernel" in n for n in names) == 16  # D in {64, 128} x G in {1, 2, 4, 8} x {f16, i8}
-    assert sum("prefill_kernel" in n for n in names) == 8
+    assert sum("prefill_kernel" in n for n in names) == 16  # the same for the prefill
     for r in rows:
         assert r[3] == "0" and r[4] == "0" and r[5] == "0", r
 

@@ -196,13 +196,14 @@ def c4_prefix(seed=4, sharers=32, prefix=2048, dtype="f16"):
 
 
 def prefix_forest(seed, groups=((700, 6),), singles=2, Hq=32, Hkv=8, D=128, suffix=(1, 300), N=None,
-                  shuffle=True):
+                  shuffle=True, dtype="f16"):
     """Several shared prefixes in one batch: for each ``(prefix, sharers)`` a
     root prefilled to ``prefix`` tokens and forked ``sharers - 1`` times; every
     member (root included) then prefills a private suffix of U[suffix]
     tokens (0 allowed); ``singles`` unrelated sequences of U[1, max prefix]
     tokens; one appended token each; one decode over all of them in a
-    shuffled batch order (members of a group not adjacent)."""
+    shuffled batch order (members of a group not adjacent). ``dtype="i8"``:
+    every token is quantised as it is written."""
     rng = np.random.default_rng(seed)
     sizes = [(int(p), int(n)) for p, n in groups]
     top = max([p for p, _ in sizes] + [1])
@@ -213,7 +214,8 @@ def prefix_forest(seed, groups=((700, 6),), singles=2, Hq=32, Hkv=8, D=128, suff
         need += sum(-(-(n + 1) // 16) for n in single_lens)
         N = need + 8
     order = rng.permutation(N).astype(np.int32)
-    w = Workload("prefix_forest", N, Hq, Hkv, D, "f16", order)
+    w = Workload("prefix_forest", N, Hq, Hkv, D, dtype, order)
+    w.i8_write = "append"
     names = []
     for gi, ((p, n), sf) in enumerate(zip(sizes, suf)):
         root = f"g{gi}m0"
@@ -239,12 +241,13 @@ def prefix_forest(seed, groups=((700, 6),), singles=2, Hq=32, Hkv=8, D=128, suff
     return w
 
 
-def prefill_chunks(seed, cached, chunk, Hq=32, Hkv=8, D=128, N=None, shuffle=True):
+def prefill_chunks(seed, cached, chunk, Hq=32, Hkv=8, D=128, N=None, shuffle=True, dtype="f16"):
     """Paged prefill: sequence i holds ``cached[i]`` earlier tokens (0 = a
     fresh prompt), then a chunk of ``chunk[i]`` new tokens is written and
     attended causally over the whole cache. Pool blocks in random order
     (``shuffle``); the earlier tokens and the chunk are written in separate
-    steps, so a chunk may start inside a partly filled block."""
+    steps, so a chunk may start inside a partly filled block. ``dtype="i8"``:
+    every token is quantised as it is written."""
     rng = np.random.default_rng(seed)
     B = len(chunk)
     if N is None:
@@ -252,7 +255,8 @@ def prefill_chunks(seed, cached, chunk, Hq=32, Hkv=8, D=128, N=None, shuffle=Tru
     order = rng.permutation(N).astype(np.int32)  # drawn either way: the values that follow stay the same
     if not shuffle:
         order = np.arange(N, dtype=np.int32)
-    w = Workload("prefill_chunks", N, Hq, Hkv, D, "f16", order)
+    w = Workload("prefill_chunks", N, Hq, Hkv, D, dtype, order)
+    w.i8_write = "append"
     names = [f"s{i}" for i in range(B)]
     for s_ in names:
         w.steps.append(("create", s_))
