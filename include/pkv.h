@@ -317,7 +317,9 @@ typedef struct pkv_decode_args {
   const int32_t* block_tables_dev;/* int32 [B][max_blocks], -1 padded             */
   int32_t max_blocks;             /* row stride of the tables                     */
   const int32_t* ctx_lens_dev;    /* int32 [B], tokens attended (>= 1)            */
-  const int32_t* ctx_lens_host;   /* optional host copy, validated if non-NULL    */
+  const int32_t* ctx_lens_host;   /* optional host copy of ctx_lens_dev (same
+                                     values), validated if non-NULL; with
+                                     automatic partitions it also sizes them */
   int32_t max_context;            /* >= every ctx_len; sizes the grid             */
   void* out_dev;                  /* fp16 [B][Hq][D], written by the call         */
   float scale;                    /* softmax scale, usually 1/sqrt(D)             */
@@ -351,8 +353,9 @@ typedef struct pkv_decode_args {
 
 /* Workspace bytes pkv_paged_decode needs for these sizes (0 when every
  * sequence fits one partition). Returns < 0 (a status) on bad arguments.
- * partition_tokens 0 = the same automatic choice pkv_paged_decode makes.
- * Layout: fp32 partials m [B][Hq][P], l [B][Hq][P], o [B][Hq][P][D]. */
+ * partition_tokens 0 = room for the finest automatic cut (partitions for
+ * about 2048 work-groups at max_context; an automatic launch never cuts
+ * finer). Layout: fp32 partials m [B][Hq][P], l [B][Hq][P], o [B][Hq][P][D]. */
 int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int32_t num_q_heads,
                                    int32_t max_context, int32_t partition_tokens);
 
@@ -363,7 +366,13 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * partition_tokens (a multiple of 16); each partition runs an online
  * softmax ([p1] §四) and writes a (max, sum, weighted-V) partial, and a
  * second kernel merges the partials by log-sum-exp in partition order
- * (skipped when every sequence fits one partition). Accumulation is fp32 and
+ * (skipped when every sequence fits one partition). Automatic partitions
+ * (partition_tokens 0): the fewest rounds of work-groups resident on the
+ * device at once, over each sequence's blocks (from ctx_lens_host when
+ * given, else every sequence at max_context), and among those the finest
+ * cut; 16 to 256 blocks per partition, never finer than the workspace's
+ * cut. The partition size changes the result only by rounding.
+ * Accumulation is fp32 and
  * the output is rounded to fp16 (nearest even). The result depends only on
  * logical token order, not on physical block ids, and is bitwise
  * reproducible. Slots past ctx_len in a tail block are never used. Block ids

@@ -48,6 +48,9 @@
 #include <type_traits>
 #include <cstdint>
 #include <cstdlib>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "pkv_internal.h"
 
@@ -1388,26 +1391,23 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Tokens per split-K partition: explicit, from PKV_PARTITION_TOKENS, or
-// chosen for a number of work-groups measured best on MI355X (256 CUs, two
-// decode work-groups resident per CU): about 2048 for fp16 (four rounds:
-// 528-token partitions at 8K context, 86 us against 91-97 us for 1024-2048)
-// and about 512 for int8 (one round: 2048-token partitions, 49 us against
-// 64 us at 528, where a work-group's first-tile latency weighs on half the
-// bytes per tile). Partitions keep at least 16 blocks (four tiles per wave):
-// small launches cut finer spend their time starting work-groups (8
+// Blocks per split-K partition: explicit, from PKV_PARTITION_TOKENS, or
+// about want_wgs work-groups over B x Hkv (sequence, KV head) pairs at
+// max_context. The workspace is sized for 2048 work-groups; a launch never
+// cuts finer than the workspace (its grid and partial rows stay within it)
+// and usually cuts coarser, see launch_part_blocks. Partitions keep at least 16 blocks (four tiles per
+// wave): small launches cut finer spend their time starting work-groups (8
 // sequences at 1025 tokens: 14.0 us at 64-token partitions, 10.0 at 256; a
 // 16-sequence 8K batch on one KV head: 20.5 us at 80 tokens, 14.4 at 512).
 // The partitions of the longest sequence are then made equal.
 constexpr int MIN_PART_BLOCKS = 16;
-int choose_part_blocks(const pkv_config& c, int B, int max_context, int partition_tokens) {
+int choose_part_blocks(int Hkv, int B, int max_context, int partition_tokens, int64_t want_wgs) {
   if (partition_tokens == 0) {
     if (const char* env = std::getenv("PKV_PARTITION_TOKENS")) partition_tokens = std::atoi(env);
   }
   if (partition_tokens > 0) return std::min(partition_tokens, MAX_PARTITION_TOKENS) / BT;
   const int nblk = (max_context + BT - 1) / BT;
-  const int64_t groups = int64_t(B) * c.num_kv_heads;
-  const int64_t want_wgs = c.dtype == PKV_I8 ? 512 : 2048;
+  const int64_t groups = int64_t(B) * Hkv;
   int64_t want_parts = (want_wgs + groups - 1) / groups;
   if (want_parts < 1) want_parts = 1;
   int pb = int((nblk + want_parts - 1) / want_parts);
@@ -1415,6 +1415,67 @@ int choose_part_blocks(const pkv_config& c, int B, int max_context, int partitio
   const int parts = (nblk + pb - 1) / pb;
   pb = (nblk + parts - 1) / parts;
   return std::max(pb, WAVES);  // at least one block per wave
+}
+
+// Decode work-groups the current device holds at once (CUs x work-groups
+// per CU at the kernel's register and LDS use), per device and kernel.
+int resident_wgs(const void* fn) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> known;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, fn);
+  const auto it = known.find(key);
+  if (it != known.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  (void)hipGetLastError();  // a failed query above must not be reported by the launch
+  return known[key] = per_cu * cus;
+}
+
+// Blocks per partition for one launch. Each partition is one work-group and
+// the decode is HBM-bound, so the fewest rounds of resident work-groups win:
+// among the partition counts of the longest span (its partitions equal, at
+// most 256 blocks, at least 16 and at least pb_min) that need the fewest
+// rounds of `slots` work-groups, take the finest, which spreads the bytes over
+// the most work-groups. span(b) is the number of blocks the split role
+// covers for sequence b. Measured on MI355X against the workspace's
+// 2048-work-group cut: batch 16 x 8193 tokens 86.1 -> 84.0 us (4 partitions,
+// one round), lengths U[128, 8193] 46.2 -> 39.7 us, the same in int8 37.3 ->
+// 30.0 us, 64 q heads 120.6 -> 90.1 us (two rounds of one work-group per CU),
+// 16 sequences on 4 / 2 / 1 KV heads 48.6 / 25.6 / 15.7 -> 44.3 / 24.4 /
+// 14.8 us, 4 x 32K tokens 88.3 -> 83.9 us; 64 x 2049 and 64 x 300 tokens
+// drop the merge kernel (one partition each).
+template <typename Span>
+int launch_part_blocks(int Hkv, int B, Span span, int slots, int pb_min) {
+  int nmax = 0;
+  for (int b = 0; b < B; ++b) nmax = std::max(nmax, span(b));
+  if (nmax < 1) return std::max(pb_min, 1);
+  const int max_pb = MAX_PARTITION_TOKENS / BT;
+  auto wgs = [&](int pb) {
+    int64_t n = 0;
+    for (int b = 0; b < B; ++b) n += (span(b) + pb - 1) / pb;
+    return n * Hkv;
+  };
+  const int p_lo = std::max(1, (nmax + max_pb - 1) / max_pb);
+  const int p_hi = std::max(p_lo, (nmax + MIN_PART_BLOCKS - 1) / MIN_PART_BLOCKS);
+  auto blocks = [&](int parts) { return (nmax + parts - 1) / parts; };
+  if (blocks(p_lo) < pb_min) return pb_min;
+  const int64_t rounds = (wgs(blocks(p_lo)) + slots - 1) / slots;
+  int best = p_lo;
+  // past 4 rounds of pairs alone, finer cuts only add work-groups
+  if (int64_t(B) * Hkv < 4 * int64_t(slots)) {
+    for (int parts = p_lo + 1; parts <= p_hi; ++parts) {
+      const int pb = blocks(parts);
+      if (pb < pb_min) break;
+      if (pb == blocks(best)) continue;
+      if (wgs(pb) <= rounds * slots) best = parts;
+    }
+  }
+  return blocks(best);
 }
 
 int max_parts_for(int max_context, int part_blocks) {
@@ -1484,7 +1545,7 @@ struct WsLayout {
 WsLayout ws_layout(const pkv_config& c, int B, int Hq, int max_context, int max_blocks, int partition_tokens,
                    int n_groups) {
   WsLayout w;
-  w.part_blocks = choose_part_blocks(c, B, max_context, partition_tokens);
+  w.part_blocks = choose_part_blocks(c.num_kv_heads, B, max_context, partition_tokens, 2048);
   w.grid_parts = max_parts_for(max_context, w.part_blocks);
   w.prefix_pp = n_groups > 0 ? prefix_partitions(c.num_kv_heads, n_groups, max_blocks) : 0;
   w.prefix_z = n_groups > 0 ? int((int64_t(w.prefix_pp) * n_groups + B - 1) / B) : 0;
@@ -1570,8 +1631,7 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
     return pkv::fail(PKV_ERR_INVALID_ARG, "num_seqs, num_q_heads and max_context must be >= 1");
   st = check_partition_tokens(partition_tokens);
   if (st != PKV_OK) return st;
-  const int pb = choose_part_blocks(*cfg, num_seqs, max_context, partition_tokens);
-  return workspace_bytes_for(*cfg, num_seqs, num_q_heads, max_parts_for(max_context, pb));
+  return ws_layout(*cfg, num_seqs, num_q_heads, max_context, 1, partition_tokens, 0).bytes;
 }
 
 int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
@@ -1657,18 +1717,37 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   }
   if (int64_t(pz) + mp0 > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many partitions for one launch");
 
-  // With a plan and both host copies, partitions are sized for the longest
-  // stretch the split role covers (a grouped sequence's unshared tail, an
-  // ungrouped sequence's whole context) instead of max_context; never more
-  // partitions than the grid and the workspace hold.
-  int pb = wl.part_blocks;
-  if (plan && a->ctx_lens_host && a->prefix_plan_host && a->partition_tokens == 0) {
-    int span = 1;
-    for (int b = 0; b < a->num_seqs; ++b) {
-      const int nb = (a->ctx_lens_host[b] + BT - 1) / BT;
-      span = std::max(span, nb - std::max(0, std::min(a->prefix_plan_host[2 * b], a->max_blocks)));
+  // Partition size of this launch, unless the caller fixed it.
+  // - Without a plan: the one-round rule over each sequence's blocks (every
+  //   sequence at max_context when the host lengths are not given), never
+  //   finer than the workspace's cut, so that the grid covers max_context
+  //   within the workspace's partial rows.
+  // - With a plan and both host copies: the longest stretch the split role
+  //   covers (a grouped sequence's unshared tail, an ungrouped sequence's
+  //   whole context) cut for about 2048 work-groups (512 for int8), in at
+  //   most as many partitions as the grid and the workspace hold. The
+  //   shared-prefix work-groups are the launch's longest chains, and split
+  //   work-groups cut this finely finish beside them (32 sequences over a
+  //   2048-token prefix: 22.7 us, against 23.7 us with the one-round rule).
+  int pb = wl.part_blocks, gparts = mp0;
+  if (a->partition_tokens == 0 && !std::getenv("PKV_PARTITION_TOKENS")) {
+    if (!plan) {
+      const int64_t cap = std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context);
+      const int cap_blocks = int((cap + BT - 1) / BT);
+      const int32_t* lens = a->ctx_lens_host;
+      auto span = [&](int b) { return lens ? int((std::min<int64_t>(lens[b], cap) + BT - 1) / BT) : cap_blocks; };
+      pb = launch_part_blocks(c.num_kv_heads, a->num_seqs, span, resident_wgs(reinterpret_cast<const void*>(fn)),
+                              (cap_blocks + mp0 - 1) / mp0);
+      gparts = std::min(mp0, (cap_blocks + pb - 1) / pb);
+    } else if (a->ctx_lens_host && a->prefix_plan_host) {
+      int span = 1;
+      for (int b = 0; b < a->num_seqs; ++b) {
+        const int nb = (a->ctx_lens_host[b] + BT - 1) / BT;
+        span = std::max(span, nb - std::max(0, std::min(a->prefix_plan_host[2 * b], a->max_blocks)));
+      }
+      pb = std::max(choose_part_blocks(c.num_kv_heads, a->num_seqs, span * BT, 0, c.dtype == PKV_I8 ? 512 : 2048),
+                    (span + mp0 - 1) / mp0);
     }
-    pb = std::max(choose_part_blocks(c, a->num_seqs, span * BT, 0), (span + mp0 - 1) / mp0);
   }
 
   const int64_t E = pkv::elem_bytes(c.dtype);
@@ -1712,13 +1791,13 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
 
   // The fused append (if any) writes into private tail blocks only, which no
   // shared-prefix work-group reads.
-  const dim3 grid(c.num_kv_heads, a->num_seqs, pz + mp0);
+  const dim3 grid(c.num_kv_heads, a->num_seqs, pz + gparts);
   if (ev[0] && ev[1])
     hipExtLaunchKernelGGL(fn, grid, dim3(256), 0, s, ev[0], ev[1], 0, prm);
   else
     hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, prm);
   st = hip_status(hipGetLastError(), "paged_decode launch");
-  if (st != PKV_OK || (mp0 <= 1 && !plan)) return st;
+  if (st != PKV_OK || (gparts <= 1 && !plan)) return st;
   MergeParams mg;
   mg.part_m = prm.part_m;
   mg.part_l = prm.part_l;
@@ -1735,9 +1814,10 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   mg.prefix_pp = prm.prefix_pp;
   const dim3 rgrid(a->num_q_heads, a->num_seqs);
   if (ev[2] && ev[3])
-    hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(mp)), 0, s, ev[2], ev[3], 0, mg);
+    hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(pp + gparts)), 0, s, ev[2], ev[3], 0,
+                          mg);
   else
-    hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(mp)), 0, s, mg);
+    hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(pp + gparts)), 0, s, mg);
   return hip_status(hipGetLastError(), "lse_reduce launch");
 }
 

@@ -299,6 +299,34 @@ def test_physical_permutation_is_bitwise_invariant():
         assert np.array_equal(out.view(np.uint16), outs[0][1].view(np.uint16))
 
 
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8), (4, 1)])
+def test_partition_cut_with_and_without_host_lengths(hq, hkv):
+    """The launch cuts partitions from the host lengths when it has them
+    (ragged lengths: coarser cuts, one round of work-groups), else from
+    max_context; a wider max_context or an explicit cut changes only the
+    partial sums. Every variant is checked against the oracle."""
+    w = workloads.tiny_random(1111 + hq, B=12, Hq=hq, Hkv=hkv, D=128, max_len=6000)
+    lib, o = run_pair(w)
+    assert max_err(lib, o) <= F16_TOL
+    rec, want = lib.decodes[0], o.decodes[0]["out"]
+    td = torch.from_numpy(rec["tables"]).to(DEV)
+    ld = torch.from_numpy(rec["lens"]).to(DEV)
+    qd = torch.from_numpy(rec["q"]).to(DEV)
+    width = rec["tables"].shape[1] * 16
+    variants = {
+        "no host lengths": dict(),
+        "host lengths, table-width max_context": dict(context_lens_host=rec["lens"], max_context=width),
+        "explicit 256-token partitions": dict(context_lens_host=rec["lens"], partition_tokens=256),
+        "explicit 4096-token partitions": dict(context_lens_host=rec["lens"], partition_tokens=4096),
+    }
+    for name, kw in variants.items():
+        announce(f"partition cut Hq={hq} Hkv={hkv}: {name}")
+        got = lib.cache.paged_decode(qd, td, ld, **kw).cpu().numpy()
+        assert np.isfinite(got).all(), name
+        assert np.abs(got.astype(np.float64) - want).max() <= F16_TOL, name
+    lib.close()
+
+
 def test_run_to_run_bitwise_determinism():
     w = workloads.tiny_random(1002, B=4, Hq=32, Hkv=8, D=128, max_len=3000)
     announce("determinism")
