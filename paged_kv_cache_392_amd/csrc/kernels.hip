@@ -913,33 +913,39 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     uint4 k[S::KL];
     uint4 v[S::NI];
     int blk;
-    uint32_t sc;  // int8: the tile's (K, V) fp16 scales
+    int it;  // int8: the tile's lane in sc_lane, which holds its (K, V) fp16 scales
   };
 
   // int8: the scales of this wave's tiles, one (K, V) pair per lane like the
-  // block ids, loaded once; each tile takes its pair with readlane. The value
+  // block ids, loaded once; each tile takes its pair with readlane when it is
+  // consumed, so the first tile's loads do not wait for them. The value
   // probabilities enter v_dot2 in fp16, pre-scaled by the tile's V scale and
   // 2^-vexp, with vexp chosen from the wave's largest V scale so that
-  // p * scale_V * 2^-vexp <= 2^8 * 2^7 (p <= 2^8 under the lazy max).
+  // p * scale_V * 2^-vexp <= 2^8 * 2^7 (p <= 2^8 under the lazy max); vexp is
+  // taken after the first tile's loads are issued.
   uint32_t sc_lane = 0;
   float vexp_scale = 1.0f, vexp_unscale = 1.0f;
   if constexpr (I8) {
     const bool ok = unsigned(blk_lane) < unsigned(prm.num_blocks);
     sc_lane = ok ? reinterpret_cast<const uint32_t*>(prm.scales)[int64_t(blk_lane) * Hkv + g] : 0u;
-    float vmax = fabsf(hi_half(sc_lane));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) vmax = fmaxf(vmax, xor_shfl(vmax, m));
-    const int ve = vmax > 128.0f ? int(ceilf(__builtin_log2f(vmax))) - 7 : 0;
-    vexp_scale = __builtin_ldexpf(1.0f, -ve);
-    vexp_unscale = __builtin_ldexpf(1.0f, ve);
   }
+  auto take_vexp = [&]() {
+    if constexpr (I8) {
+      float vmax = fabsf(hi_half(sc_lane));
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) vmax = fmaxf(vmax, xor_shfl(vmax, m));
+      const int ve = vmax > 128.0f ? int(ceilf(__builtin_log2f(vmax))) - 7 : 0;
+      vexp_scale = __builtin_ldexpf(1.0f, -ve);
+      vexp_unscale = __builtin_ldexpf(1.0f, ve);
+    }
+  };
 
   // A bad id (outside the pool) still loads block 0, which exists; compute()
   // then masks every row of that tile.
   auto load = [&](int it, Tile& t) {
     const int blk = __builtin_amdgcn_readlane(blk_lane, it);
     t.blk = blk;
-    if constexpr (I8) t.sc = __builtin_amdgcn_readlane(sc_lane, it);
+    if constexpr (I8) t.it = it;
     const int safe = unsigned(blk) < unsigned(prm.num_blocks) ? blk : 0;
     const char* kb = Kc + safe * blk_stride + head_off;
     const char* vb = Vc + safe * blk_stride + head_off;
@@ -996,8 +1002,9 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     const bool blk_ok = unsigned(t.blk) < unsigned(prm.num_blocks);
     float kscale = prm.scale_log2, vscale = 1.0f;
     if constexpr (I8) {
-      kscale *= lo_half(t.sc);
-      vscale = PAIRS ? hi_half(t.sc) * vexp_scale : hi_half(t.sc);
+      const uint32_t sc = __builtin_amdgcn_readlane(sc_lane, t.it);
+      kscale *= lo_half(sc);
+      vscale = PAIRS ? hi_half(sc) * vexp_scale : hi_half(sc);
     }
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -1156,6 +1163,7 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     Tile ta, tb;
     int it = 0;
     load(0, ta);
+    take_vexp();
     for (; it + 2 < n_my; it += 2) {
       load(it + 1, tb);
       compute(first + WAVES * it, ta);
