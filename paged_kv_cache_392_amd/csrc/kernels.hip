@@ -1251,6 +1251,7 @@ struct MergeParams {
   _Float16* out;
   int D, max_blocks, max_context, part_blocks, max_parts;
   int num_groups, prefix_pp;
+  int row_parts;  // partials any row of this launch can hold (<= max_parts)
 };
 
 // Merge the partials of one (sequence, query head) by log-sum-exp:
@@ -1266,7 +1267,9 @@ struct MergeParams {
 // formula. Several streams keep the chain of dependent loads short when
 // rows have many partials (short sequences cut into many partitions); with
 // few, one stream is cheaper. Sequences with a single partial were finished
-// by the split kernel.
+// by the split kernel. The first group loads only slots below row_parts (the
+// launch's prefix partitions + split planes): slots past it were not written
+// by this launch.
 constexpr int MERGE_MAX_WAYS = 8;
 // Partial streams per merged row for launches whose rows hold up to
 // max_parts partials (measured on MI355X: one stream up to 32 partials).
@@ -1284,10 +1287,16 @@ __global__ __launch_bounds__(1024) void lse_reduce_kernel(MergeParams prm) {
 #pragma unroll
   for (int u = 0; u < CH; ++u) {
     const int p = w + W * u;
-    const int64_t pi = base + (p < prm.max_parts ? p : 0);
-    m0[u] = prm.part_m[pi];
-    l0[u] = prm.part_l[pi];
-    o0[u] = prm.part_o[pi * D + d];
+    if (p < prm.row_parts) {  // uniform over the launch
+      const int64_t pi = base + p;
+      m0[u] = prm.part_m[pi];
+      l0[u] = prm.part_l[pi];
+      o0[u] = prm.part_o[pi * D + d];
+    } else {
+      m0[u] = -INFINITY;
+      l0[u] = 0.0f;
+      o0[u] = 0.0f;
+    }
   }
   int sb, pre;
   seq_prefix(prm.plan, b, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
@@ -1296,7 +1305,7 @@ __global__ __launch_bounds__(1024) void lse_reduce_kernel(MergeParams prm) {
   const int nblk = (ctx + BT - 1) / BT;
   const int nparts = nblk > sb ? (nblk - sb + prm.part_blocks - 1) / prm.part_blocks : 0;
   if (pre == 0 && nparts <= 1) return;
-  const int count = min(pre + nparts, prm.max_parts);
+  const int count = min(pre + nparts, prm.row_parts);
 
   float M = -INFINITY, L = 0.0f, O = 0.0f;
   for (int k0 = 0; w + W * k0 < count; k0 += CH) {
@@ -1820,6 +1829,7 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   mg.max_parts = mp;
   mg.num_groups = prm.num_groups;
   mg.prefix_pp = prm.prefix_pp;
+  mg.row_parts = std::min(mp, (plan ? pp : 0) + gparts);
   const dim3 rgrid(a->num_q_heads, a->num_seqs);
   if (ev[2] && ev[3])
     hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(pp + gparts)), 0, s, ev[2], ev[3], 0,

@@ -433,6 +433,33 @@ def test_edge_lengths(lens):
         lib.close()
 
 
+@pytest.mark.parametrize("lens,Hq,ptoks", [([131073, 5], 4, (0, 16)), ([65537, 3, 16], 8, (0, 4096))])
+def test_long_context_many_partitions(lens, Hq, ptoks):
+    """One very long sequence beside short ones, on a single KV head: the
+    automatic cut (hundreds of partitions), 16-token partitions (8193 partials
+    per row through the merge kernel) and the largest partition size."""
+    rng = np.random.default_rng(lens[0])
+    Hkv, D = 1, 128
+    N = sum(-(-n // 16) for n in lens) + 3
+    w = workloads.Workload("long", N, Hq, Hkv, D, "f16", rng.permutation(N).astype(np.int32))
+    names = [f"s{i}" for i in range(len(lens))]
+    for s in names:
+        w.steps.append(("create", s))
+    for s, n in zip(names, lens):
+        k = rng.standard_normal((n, Hkv, D), dtype=np.float32).astype(np.float16)
+        w.steps.append(("prefill", s, k, rng.standard_normal((n, Hkv, D), dtype=np.float32).astype(np.float16)))
+    w.steps.append(("decode", names, rng.standard_normal((len(lens), Hq, D), dtype=np.float32).astype(np.float16)))
+    o = OracleRun(w).run()
+    for ptok in ptoks:
+        announce(f"long context lens={lens} Hq={Hq} Hkv={Hkv} partition_tokens={ptok}")
+        lib = LibRun(w, device=DEV, poison=True).run(partition_tokens=ptok)
+        check_host_records(lib, o)
+        err = max_err(lib, o)
+        announce(f"long context max abs err {err:.3g}")
+        assert err <= F16_TOL
+        lib.close()
+
+
 def test_copy_blocks_all_layers_and_scales():
     rng = np.random.default_rng(9)
     for dtype in ("f16", "i8"):
