@@ -52,12 +52,28 @@ def parse():
                     help="launch every layer directly instead of replaying layers 1.. as one HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
-    ap.add_argument("--workload", choices=["headline", "c5", "prefix", "prefill"], default="headline",
+    ap.add_argument("--workload", choices=["headline", "c5", "c3", "shape", "prefix", "prefill"],
+                    default="headline",
                     help="headline: the fp16 batch-16 8K decode step (the bench line); c5: the int8 "
-                         "batch-16 8K decode-only step over 32 int8 layer pools; prefix: the decode step "
+                         "batch-16 8K decode-only step over 32 int8 layer pools; c3: the decode-only step "
+                         "of the continuous-batching mix (16 sequences at seeded U[128, 8192] lengths); "
+                         "shape: a decode-only step of the shape given by --batch, --context or --lengths, "
+                         "--q-heads, --kv-heads, --dtype; prefix: the decode step "
                          "of 32 sequences sharing a 2048-token prefix, with and without the shared-prefix "
                          "plan; prefill: 4 prompts of 2048 tokens appended and attended causally over 32 "
                          "layer pools (timing and profiling; parity is covered by the GPU tests)")
+    ap.add_argument("--batch", type=int, default=16, help="shape workload: sequences")
+    ap.add_argument("--context", type=int, default=8192, help="shape workload: tokens per sequence")
+    ap.add_argument("--lengths", type=int, nargs=2, metavar=("LO", "HI"),
+                    help="shape workload: seeded uniform lengths in [LO, HI] instead of --context")
+    ap.add_argument("--context-list", type=str, default=None,
+                    help="shape workload: comma-separated context lengths, one per sequence")
+    ap.add_argument("--q-heads", type=int, default=32, help="shape workload")
+    ap.add_argument("--kv-heads", type=int, default=8, help="shape workload")
+    ap.add_argument("--dtype", choices=["f16", "i8"], default="f16", help="shape workload")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="shape workload: lengths and block order (default 7); c3: block order (default: "
+                         "the config's seed)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB three times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -141,6 +157,12 @@ def main():
 
     if args.workload == "c5":
         int8_decode_bench(args, torch, pkv, C, workloads)
+        return
+    if args.workload == "c3":
+        c3_decode_bench(args, torch, pkv, C, workloads)
+        return
+    if args.workload == "shape":
+        shape_decode_bench(args, torch, pkv, C, workloads)
         return
     if args.workload == "prefix":
         prefix_decode_bench(args, torch, pkv, C, workloads)
@@ -431,39 +453,46 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def int8_decode_bench(args, torch, pkv, C, workloads):
-    """int8 decode-only step (the int8 long-context config): batch 16 at
-    context 8192, 32 q / 8 KV heads, d128, one fp16 scale per (block, KV
-    head) for K and V, over 32 layer pools (8 GiB of codes). Codes and scales
-    are seeded device noise (values do not change the timing); tables come
-    from the library's allocator in the config's seeded block order. Layer 0
-    is launched directly with timing events, layers 1..31 are replayed from
-    one HIP graph and checked against direct launches bit for bit."""
+def decode_only_bench(args, torch, pkv, C, lens, hq, hkv, dtype, free_order, seed, metric, workload):
+    """Decode-only step (no append) over `args.layers` layer pools: one
+    paged decode per layer for sequences of the given context lengths, q
+    heads, KV heads and element type (d128). K/V (codes and scales for int8)
+    are seeded device noise: values do not change the timing, and parity of
+    every shape is covered by the GPU tests. Tables come from the library's
+    allocator in the given block order. Layer 0 is launched directly with
+    timing events around the split and merge kernels, layers 1.. are
+    replayed from one HIP graph and checked against direct launches bit for
+    bit."""
     dev = torch.device("cuda:0")
     K, W, L = args.steps, args.warmup, args.layers
-    w = workloads.c5_int8()
-    ctx = 8192
-    N = w.num_blocks
-    cache = pkv.PagedKVCache(L, N, HKV, D, "i8", w.free_order, dev)
+    lens = [int(n) for n in lens]
+    nb = len(lens)
+    N = len(free_order)
+    cache = pkv.PagedKVCache(L, N, hkv, D, dtype, free_order, dev)
     lib = C.load()
     sp = torch.cuda.current_stream().cuda_stream
     gen = torch.Generator(device=dev)
-    gen.manual_seed(w.seed)
+    gen.manual_seed(seed)
     for layer in range(L):
         for which in (0, 1):
             r = cache.region(which, layer)
-            r.copy_(torch.randint(-127, 128, r.shape, dtype=torch.int8, device=dev, generator=gen))
-    cache.scales().uniform_(0.01, 0.03, generator=gen)
-    seqs = [cache.create_seq() for _ in range(B)]
-    for s in seqs:
-        cache.reserve([s], [ctx])
-    max_blocks = ctx // 16
+            if dtype == "i8":
+                r.copy_(torch.randint(-127, 128, r.shape, dtype=torch.int8, device=dev, generator=gen))
+            else:
+                r.normal_(generator=gen)
+    if dtype == "i8":
+        cache.scales().uniform_(0.01, 0.03, generator=gen)
+    seqs = [cache.create_seq() for _ in range(nb)]
+    for s, n in zip(seqs, lens):
+        cache.reserve([s], [n])
+    ctx = max(lens)
+    max_blocks = -(-ctx // 16)
     tables_h, lens_h = cache.block_tables(seqs, max_blocks)
     tables_d = torch.from_numpy(tables_h).to(dev)
     lens_d = torch.from_numpy(lens_h).to(dev)
-    q = torch.empty((L, B, HQ, D), dtype=torch.float16, device=dev).normal_(generator=gen)
+    q = torch.empty((L, nb, hq, D), dtype=torch.float16, device=dev).normal_(generator=gen)
     out = torch.empty_like(q)
-    ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, HQ, ctx, args.partition_tokens)
+    ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, nb, hq, ctx, args.partition_tokens)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     argv = []
     for layer in range(L):
@@ -472,8 +501,8 @@ def int8_decode_bench(args, torch, pkv, C, workloads):
         a.pool_dev = cache.pool.data_ptr()
         a.layer = layer
         a.q_dev = q[layer].data_ptr()
-        a.num_seqs = B
-        a.num_q_heads = HQ
+        a.num_seqs = nb
+        a.num_q_heads = hq
         a.block_tables_dev = tables_d.data_ptr()
         a.max_blocks = max_blocks
         a.ctx_lens_dev = lens_d.data_ptr()
@@ -528,29 +557,89 @@ def int8_decode_bench(args, torch, pkv, C, workloads):
     same = all(torch.equal(got[l].view(torch.int16), out[l].view(torch.int16)) for l in check)
     split_ms = np.array([g[0].elapsed_time(g[1]) for g in ev])
     merge_ms = np.array([g[2].elapsed_time(g[3]) for g in ev])
-    nblk = ctx // 16
-    kernel_bytes = B * ctx * 2 * HKV * D + B * nblk * HKV * 4 + B * HQ * D * 2 + B * nblk * 4 + B * 4
-    step_bytes = L * (kernel_bytes + B * HQ * D * 2)
+    # a launch with one partition per sequence has no merge: its merge events
+    # then still hold their set-up record, from before the timed loop
+    merged = all(t0.elapsed_time(g[2]) > 0 for g in ev)
+    E = 1 if dtype == "i8" else 2
+    nblk = sum(-(-n // 16) for n in lens)
+    kernel_bytes = (sum(lens) * 2 * hkv * D * E + (nblk * hkv * 4 if dtype == "i8" else 0)
+                    + nb * hq * D * 2 + nblk * 4 + nb * 4)
+    step_bytes = L * (kernel_bytes + nb * hq * D * 2)
     achieved = kernel_bytes / (float(np.mean(split_ms)) * 1e-3) / 1e9
+    G = hq // hkv
     print(json.dumps({
-        "metric": "paged decode HBM GB/s (% of peak), int8 K/V, 32q/8kv d128",
+        "metric": metric,
         "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "int8 decode-only step, batch 16, context 8192, 32 q heads / 8 KV heads, "
-                               "head_dim 128, int8 K/V with one fp16 scale per (block, KV head), "
-                               "32 layer pools", "layers": L, "partition_tokens": args.partition_tokens or "auto"},
-        "decode_tok_s": round(B / (ms_per_step * 1e-3), 1),
+        "config": {"workload": workload, "layers": L, "batch": nb, "q_heads": hq, "kv_heads": hkv,
+                   "head_dim": D, "context_min": min(lens), "context_max": ctx, "context_sum": sum(lens),
+                   "partition_tokens": args.partition_tokens or "auto"},
+        "decode_tok_s": round(nb / (ms_per_step * 1e-3), 1),
         "split_kernel_us": round(float(np.mean(split_ms)) * 1e3, 2),
-        "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2),
+        "split_kernel_us_p10_p90": [round(float(np.percentile(split_ms, 10)) * 1e3, 2),
+                                    round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
+        "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2) if merged else None,
         "graph_matches_eager_bitwise": same,
-        "roofline": {"bound": "hbm", "kernel": "paged_decode_kernel<128,4,i8> (split-K decode)",
+        "roofline": {"bound": "hbm", "kernel": f"paged_decode_kernel<128,{G},{dtype}> (split-K decode)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
                      "bytes_per_launch": int(kernel_bytes)},
         "cpu_baseline": None,
     }), flush=True)
+
+
+def int8_decode_bench(args, torch, pkv, C, workloads):
+    """int8 decode-only step (the int8 long-context config): batch 16 at
+    context 8192, 32 q / 8 KV heads, d128, one fp16 scale per (block, KV
+    head) for K and V, over 32 layer pools (8 GiB of codes), in the config's
+    seeded block order."""
+    w = workloads.c5_int8()
+    decode_only_bench(args, torch, pkv, C, [8192] * B, HQ, HKV, "i8", w.free_order, w.seed,
+                      "paged decode HBM GB/s (% of peak), int8 K/V, 32q/8kv d128",
+                      "int8 decode-only step, batch 16, context 8192, 32 q heads / 8 KV heads, head_dim 128, "
+                      "int8 K/V with one fp16 scale per (block, KV head), 32 layer pools")
+
+
+def c3_decode_bench(args, torch, pkv, C, workloads):
+    """Decode-only step of the continuous-batching mix: 16 sequences at the
+    config's seeded lengths U[128, 8192] + the appended token, fp16, 32 q / 8
+    KV heads, over 32 layer pools in a seeded random block order (the
+    config's fragmentation: a scrambled pool)."""
+    w = workloads.c3_mixed()
+    lens = [len(st[2]) + 1 for st in w.steps if st[0] == "prefill"]
+    N = sum(-(-n // 16) for n in lens) + 16
+    seed = w.seed if args.seed is None else args.seed
+    order = np.random.default_rng(seed).permutation(N).astype(np.int32)
+    decode_only_bench(args, torch, pkv, C, lens, HQ, HKV, "f16", order, seed,
+                      "paged decode HBM GB/s (% of peak), fp16, continuous-batching mix",
+                      "decode-only step, 16 sequences at U[128, 8192] + 1 tokens (seeded), 32 q heads / "
+                      "8 KV heads, head_dim 128, fp16, scrambled block order, 32 layer pools")
+
+
+def shape_decode_bench(args, torch, pkv, C, workloads):
+    """Decode-only step of any shape given on the command line."""
+    if args.seed is None:
+        args.seed = 7
+    if args.context_list:
+        lens = [int(x) for x in args.context_list.split(",")]
+        args.batch = len(lens)
+    elif args.lengths:
+        lo, hi = args.lengths
+        lens = np.random.default_rng(args.seed).integers(lo, hi + 1, args.batch).tolist()
+    else:
+        lens = [args.context] * args.batch
+    N = sum(-(-n // 16) for n in lens) + 16
+    order = np.random.default_rng(args.seed).permutation(N).astype(np.int32)
+    desc = (f"decode-only step, {args.batch} sequences at "
+            + (f"{args.context_list} tokens" if args.context_list
+               else f"U[{args.lengths[0]}, {args.lengths[1]}] tokens (seed {args.seed})" if args.lengths
+               else f"{args.context} tokens")
+            + f", {args.q_heads} q heads / {args.kv_heads} KV heads, head_dim 128, {args.dtype}, "
+            f"{args.layers} layer pools")
+    decode_only_bench(args, torch, pkv, C, lens, args.q_heads, args.kv_heads, args.dtype, order, args.seed,
+                      f"paged decode HBM GB/s (% of peak), {args.dtype}, decode-only shape", desc)
 
 
 def prefix_decode_bench(args, torch, pkv, C, workloads):

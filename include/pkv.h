@@ -371,7 +371,13 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * device at once, over each sequence's blocks (from ctx_lens_host when
  * given, else every sequence at max_context), and among those the finest
  * cut; 16 to 256 blocks per partition, never finer than the workspace's
- * cut. The partition size changes the result only by rounding.
+ * cut. The partition size changes the result only by rounding. With
+ * ctx_lens_host, no shared-prefix plan and at most 1024 sequences, a launch
+ * whose grid of (sequence, partition) slots at max_context would hold slots
+ * past some sequence's last partition launches only the pairs that hold
+ * blocks (same partitions, bit for bit the same output); ctx_lens_host must
+ * then equal the device lengths (a mismatch gives wrong output for the
+ * sequences it misstates, never an access out of bounds).
  * Accumulation is fp32 and
  * the output is rounded to fp16 (nearest even). The result depends only on
  * logical token order, not on physical block ids, and is bitwise

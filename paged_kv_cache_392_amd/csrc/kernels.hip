@@ -293,10 +293,79 @@ struct DecodeParams {
   int max_parts;
   int max_context;
   float scale_log2;  // softmax scale * log2(e)
+  int num_seqs;
 };
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int max_context) {
   return min(ctx, min(max_blocks * BT, max_context));
+}
+
+// Sequences a compact split grid can enumerate (each work-group scans the
+// partition counts of all of them).
+constexpr int COMPACT_MAX_SEQS = 1024;
+
+// Exclusive prefix sum of v over the 256 threads of a work-group (thread
+// order), and the work-group's total. part: WAVES ints of LDS. Every thread
+// must call it.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* part, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) part[wave] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {
+    const int t = part[w];
+    off += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();  // part is rewritten by the next call
+  total = tot;
+  return off + x - v;
+}
+
+// Compact split grid: the (sequence, partition) pair of work-group k, from
+// the partition counts of every sequence (the same rule as the plain grid's
+// early exit; a sequence with no tokens keeps one work-group, which writes
+// its zero output). b = -1 when k is past the last pair. lds: WAVES + 2 ints
+// of the caller's LDS, free until the barrier that ends this call.
+__device__ __forceinline__ void compact_pair(const DecodeParams& prm, int k, int* lds, int& b, int& p) {
+  int* part = lds;
+  int* pick = lds + WAVES;
+  const int tid = threadIdx.x;
+  constexpr int PER = COMPACT_MAX_SEQS / 256;
+  int n[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {  // all lengths in flight together
+    const int t = tid + 256 * i;
+    n[i] = 0;
+    if (t < prm.num_seqs) {
+      const int ctx = clamp_ctx(prm.ctx_lens[t], prm.max_blocks, prm.max_context);
+      n[i] = ctx > 0 ? ((ctx + BT - 1) / BT + prm.part_blocks - 1) / prm.part_blocks : 1;
+    }
+  }
+  if (tid == 0) pick[0] = -1;  // ordered before the writes below by the scan's barriers
+  int carry = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (256 * i >= prm.num_seqs) break;  // uniform
+    int tot;
+    const int ex = carry + wg_exclusive_scan(n[i], part, tot);
+    if (k >= ex && k < ex + n[i]) {  // exactly one thread, if any
+      pick[0] = tid + 256 * i;
+      pick[1] = k - ex;
+    }
+    carry += tot;
+  }
+  __syncthreads();
+  b = __builtin_amdgcn_readfirstlane(pick[0]);
+  p = __builtin_amdgcn_readfirstlane(pick[1]);
+  __syncthreads();  // every wave has its pair before lds is reused
 }
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -809,19 +878,38 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
 // After its last tile the work-group writes one (m, l, o[D]) partial per
 // query head for the merge kernel, or the final fp16 row when the sequence
 // has a single partition.
-template <int D, int G, bool I8>
+// COMPACT: the split grid holds the (sequence, partition) pairs that have
+// blocks and nothing else (no plan). The plain grid holds max-context
+// partitions for every sequence, and a work-group past its sequence's last
+// partition exits once its length has arrived; under a full HBM stream that
+// holds its slot for microseconds, and real work-groups queue behind such
+// exits. The compact grid is chosen by the host from its copy of the lengths
+// and is a separate instantiation, so the plain grid's code is untouched by
+// the scan (sharing one body cost the shared-prefix launch 8%).
+template <int D, int G, bool I8, bool COMPACT>
 __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void paged_decode_kernel(DecodeParams prm) {
   using S = Shape<D, G, I8>;
-  const int g = blockIdx.x, b = blockIdx.y;
-  // With a shared-prefix plan the first prefix_z planes of the grid are
-  // shared-prefix work-groups: dispatched first, they run beside the split
-  // work-groups of the same launch.
-  if (int(blockIdx.z) < prm.prefix_z) {
-    const int k = blockIdx.y + gridDim.y * blockIdx.z;
-    if (k < prm.prefix_pp * prm.num_groups) prefix_role<D, G, I8>(prm, g, k / prm.prefix_pp, k % prm.prefix_pp);
-    return;
+  const int g = blockIdx.x;
+  __shared__ float p_lds[WAVES][BT][G];
+  __shared__ float merge_o[WAVES][G][D];
+  __shared__ float merge_ml[WAVES][G][2];
+  int bc = 0, pc = 0;
+  if constexpr (COMPACT) {
+    static_assert(sizeof(merge_o) >= (WAVES + 2) * sizeof(int), "compact scan scratch");
+    compact_pair(prm, blockIdx.y + gridDim.y * blockIdx.z, reinterpret_cast<int*>(&merge_o[0][0][0]), bc, pc);
+    if (bc < 0) return;  // uniform over the work-group
+  } else {
+    // With a shared-prefix plan the first prefix_z planes of the grid are
+    // shared-prefix work-groups: dispatched first, they run beside the split
+    // work-groups of the same launch.
+    if (int(blockIdx.z) < prm.prefix_z) {
+      const int k = blockIdx.y + gridDim.y * blockIdx.z;
+      if (k < prm.prefix_pp * prm.num_groups) prefix_role<D, G, I8>(prm, g, k / prm.prefix_pp, k % prm.prefix_pp);
+      return;
+    }
   }
-  const int p = blockIdx.z - prm.prefix_z;
+  const int b = COMPACT ? bc : int(blockIdx.y);
+  const int p = COMPACT ? pc : int(blockIdx.z) - prm.prefix_z;
   const int Hkv = prm.Hkv, Hq = Hkv * G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -878,9 +966,6 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
 #pragma unroll
   for (int e = 0; e < 4; ++e) lrow[e] = 0.0f;
 
-  __shared__ float p_lds[WAVES][BT][G];
-  __shared__ float merge_o[WAVES][G][D];
-  __shared__ float merge_ml[WAVES][G][2];
 
   const char* Kc = static_cast<const char*>(prm.K);
   const char* Vc = static_cast<const char*>(prm.V);
@@ -1502,21 +1587,26 @@ int max_parts_for(int max_context, int part_blocks) {
 
 typedef void (*decode_fn)(DecodeParams);
 
-template <int D, bool I8>
+template <int D, bool I8, bool COMPACT>
 decode_fn pick_g(int G) {
   switch (G) {
-    case 1: return paged_decode_kernel<D, 1, I8>;
-    case 2: return paged_decode_kernel<D, 2, I8>;
-    case 4: return paged_decode_kernel<D, 4, I8>;
-    case 8: return paged_decode_kernel<D, 8, I8>;
+    case 1: return paged_decode_kernel<D, 1, I8, COMPACT>;
+    case 2: return paged_decode_kernel<D, 2, I8, COMPACT>;
+    case 4: return paged_decode_kernel<D, 4, I8, COMPACT>;
+    case 8: return paged_decode_kernel<D, 8, I8, COMPACT>;
     default: return nullptr;
   }
 }
 
-decode_fn pick_kernel(int D, int G, bool i8) {
-  if (D == 128) return i8 ? pick_g<128, true>(G) : pick_g<128, false>(G);
-  if (D == 64) return i8 ? pick_g<64, true>(G) : pick_g<64, false>(G);
+template <bool COMPACT>
+decode_fn pick_dt(int D, int G, bool i8) {
+  if (D == 128) return i8 ? pick_g<128, true, COMPACT>(G) : pick_g<128, false, COMPACT>(G);
+  if (D == 64) return i8 ? pick_g<64, true, COMPACT>(G) : pick_g<64, false, COMPACT>(G);
   return nullptr;
+}
+
+decode_fn pick_kernel(int D, int G, bool i8, bool compact = false) {
+  return compact ? pick_dt<true>(D, G, i8) : pick_dt<false>(D, G, i8);
 }
 
 // Split-K workspace: m [B][Hq][P], l [B][Hq][P], o [B][Hq][P][D] (fp32); none
@@ -1767,6 +1857,28 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
     }
   }
 
+  // Compact split grid (no plan, host lengths given): the (sequence,
+  // partition) pairs that hold blocks, and nothing else, when the plain grid
+  // would launch work-groups past some sequence's last partition. Measured on
+  // MI355X, 16 sequences of 1024..8192 tokens cut into 512 full 64-block
+  // partitions: 66.3 us on the plain grid (512 of its 1024 work-groups
+  // empty), 46.5 us compact, 45.5 us for 16 x 4096 tokens (the same
+  // partitions, no empty work-group); the continuous-batching mix (16 x
+  // U[128, 8192]) 68.2 -> 53.0 us, int8 48.9 -> 37.7 us. Dispatching the
+  // plain grid's planes last-first instead is no cure (64.0 and 67.2 us).
+  // The scan costs the compact launch ~1 us at its start, so a ragged batch
+  // whose plain grid has few empty work-groups runs ~2% slower.
+  int64_t pairs = 0;
+  bool compact = false;
+  if (!plan && a->ctx_lens_host && a->num_seqs <= COMPACT_MAX_SEQS) {
+    const int64_t cap = std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context);
+    for (int b = 0; b < a->num_seqs; ++b) {
+      const int64_t ctx = std::min<int64_t>(a->ctx_lens_host[b], cap);
+      pairs += ctx > 0 ? ((ctx + BT - 1) / BT + pb - 1) / pb : 1;
+    }
+    compact = pairs < int64_t(a->num_seqs) * gparts;
+  }
+
   const int64_t E = pkv::elem_bytes(c.dtype);
   const int64_t layer_bytes = pkv::layer_elems(c) * E;
   const char* base = static_cast<const char*>(a->pool_dev);
@@ -1800,6 +1912,8 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   prm.max_parts = mp;
   prm.max_context = a->max_context;
   prm.scale_log2 = a->scale * LOG2E;
+  prm.num_seqs = a->num_seqs;
+  if (compact) fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, true);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -1808,7 +1922,9 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
 
   // The fused append (if any) writes into private tail blocks only, which no
   // shared-prefix work-group reads.
-  const dim3 grid(c.num_kv_heads, a->num_seqs, pz + gparts);
+  const int cy = int(std::min<int64_t>(pairs, 65535));
+  const dim3 grid = compact ? dim3(c.num_kv_heads, cy, unsigned((pairs + cy - 1) / cy))
+                            : dim3(c.num_kv_heads, a->num_seqs, pz + gparts);
   if (ev[0] && ev[1])
     hipExtLaunchKernelGGL(fn, grid, dim3(256), 0, s, ev[0], ev[1], 0, prm);
   else

@@ -327,6 +327,34 @@ def test_partition_cut_with_and_without_host_lengths(hq, hkv):
     lib.close()
 
 
+@pytest.mark.parametrize("seed,B,max_len,hq,hkv,ptoks", [
+    (2001, 12, 6000, 32, 8, (256, 1024)),   # ragged: short sequences leave plain-grid planes empty
+    (2002, 300, 200, 8, 2, (16, 64)),       # more sequences than one 256-thread scan covers
+    (2003, 1100, 40, 4, 1, (16,)),          # past the compact grid's sequence limit: plain grid
+])
+def test_compact_grid_matches_plain_grid_bitwise(seed, B, max_len, hq, hkv, ptoks):
+    """With host lengths and ragged sequences the launch enumerates only the
+    (sequence, partition) pairs that hold blocks; the partitions are those
+    of the plain grid, so the outputs are bit for bit those of a launch
+    without host lengths at the same partition size and max_context."""
+    w = workloads.tiny_random(seed, B=B, Hq=hq, Hkv=hkv, D=128, max_len=max_len)
+    lib, o = run_pair(w)
+    assert max_err(lib, o) <= F16_TOL
+    rec, want = lib.decodes[0], o.decodes[0]["out"]
+    td = torch.from_numpy(rec["tables"]).to(DEV)
+    ld = torch.from_numpy(rec["lens"]).to(DEV)
+    qd = torch.from_numpy(rec["q"]).to(DEV)
+    width = rec["tables"].shape[1] * 16
+    for pt in ptoks:
+        announce(f"compact vs plain grid B={B} Hq={hq} Hkv={hkv} partition_tokens={pt}")
+        plain = lib.cache.paged_decode(qd, td, ld, max_context=width, partition_tokens=pt).cpu().numpy()
+        compact = lib.cache.paged_decode(qd, td, ld, context_lens_host=rec["lens"], max_context=width,
+                                         partition_tokens=pt).cpu().numpy()
+        assert np.array_equal(plain.view(np.uint16), compact.view(np.uint16)), pt
+        assert np.abs(compact.astype(np.float64) - want).max() <= F16_TOL, pt
+    lib.close()
+
+
 def test_run_to_run_bitwise_determinism():
     w = workloads.tiny_random(1002, B=4, Hq=32, Hkv=8, D=128, max_len=3000)
     announce("determinism")

@@ -613,7 +613,8 @@ def test_kernels_use_no_scratch_memory():
         pytest.skip("library not built in this tree")
     rows = [l.rstrip("\n").split("\t") for l in open(B.RESOURCES) if not l.startswith("#")]
     names = [r[0] for r in rows]
-    assert sum("paged_decode_kernel" in n for n in names) == 16  # D in {64, 128} x G in {1, 2, 4, 8} x {f16, i8}
+    # D in {64, 128} x G in {1, 2, 4, 8} x {f16, i8} x {plain, compact grid}
+    assert sum("paged_decode_kernel" in n for n in names) == 32
     assert sum("prefill_kernel" in n for n in names) == 16  # the same for the prefill
     for r in rows:
         assert r[3] == "0" and r[4] == "0" and r[5] == "0", r
