@@ -755,7 +755,7 @@ template <int D, int G, bool I8>
 __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int grp, int part) {
   constexpr int NDB = D / 16;
   const int lj = (threadIdx.x & 63) >> 4;
-  const int B = gridDim.y, Hq = prm.Hkv * G;
+  const int B = prm.num_seqs, Hq = prm.Hkv * G;
   const int32_t* gd = prm.plan + 2 * int64_t(B) + int64_t(grp) * PKV_PREFIX_GROUP_INTS;
   const int np = min(gd[0], prm.max_blocks);
   const int members = min(gd[1], PKV_MAX_SHARERS);
