@@ -1520,10 +1520,14 @@ int choose_part_blocks(int Hkv, int B, int max_context, int partition_tokens, in
 }
 
 // Decode work-groups the current device holds at once (CUs x work-groups
-// per CU at the kernel's register and LDS use), per device and kernel.
-int resident_wgs(const void* fn) {
+// per CU at the kernel's register and LDS use) and its CU count, per device
+// and kernel.
+struct Residency {
+  int slots, cus;
+};
+Residency resident_wgs(const void* fn) {
   static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> known;
+  static std::map<std::pair<int, const void*>, Residency> known;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = -1;
   std::lock_guard<std::mutex> lock(mu);
@@ -1535,7 +1539,7 @@ int resident_wgs(const void* fn) {
   if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
   (void)hipGetLastError();  // a failed query above must not be reported by the launch
-  return known[key] = per_cu * cus;
+  return known[key] = Residency{per_cu * cus, cus};
 }
 
 // Blocks per partition for one launch. Each partition is one work-group and
@@ -1551,8 +1555,20 @@ int resident_wgs(const void* fn) {
 // 16 sequences on 4 / 2 / 1 KV heads 48.6 / 25.6 / 15.7 -> 44.3 / 24.4 /
 // 14.8 us, 4 x 32K tokens 88.3 -> 83.9 us; 64 x 2049 and 64 x 300 tokens
 // drop the merge kernel (one partition each).
+// When that one-round cut puts two work-groups on some CUs, the finest cut
+// with at most one work-group per CU is taken instead if its partitions are
+// at most twice as long (the load of a doubled CU): a CU holding two
+// work-groups of a small launch streams them no faster than one longer one,
+// and a partly filled second layer is a tail (measured on MI355X, split us,
+// one-round cut -> this rule: 8 x 1025 tokens 11.9 -> 9.7 (13 -> 17 blocks,
+// 320 -> 256 work-groups), 4 x 2049 11.7 -> 9.5, 8 x 2049 15.7 -> 14.6, two
+// KV heads x 16 x 8193 25.1 -> 24.4). Large launches have no such cut (the
+// batch-16 8K step would need 257-block partitions), and a ragged batch's
+// is usually far coarser (the continuous-batching mix: 245 blocks against
+// 82), so both keep the one-round cut.
 template <typename Span>
-int launch_part_blocks(int Hkv, int B, Span span, int slots, int pb_min) {
+int launch_part_blocks(int Hkv, int B, Span span, Residency res, int pb_min) {
+  const int slots = res.slots;
   int nmax = 0;
   for (int b = 0; b < B; ++b) nmax = std::max(nmax, span(b));
   if (nmax < 1) return std::max(pb_min, 1);
@@ -1577,7 +1593,19 @@ int launch_part_blocks(int Hkv, int B, Span span, int slots, int pb_min) {
       if (wgs(pb) <= rounds * slots) best = parts;
     }
   }
-  return blocks(best);
+  const int pb_round = blocks(best);
+  const int64_t w_round = wgs(pb_round);
+  if (rounds == 1 && w_round > res.cus) {
+    // the finest cut with at most one work-group per CU, if its partitions
+    // are no longer than what the doubled CUs of the one-round cut carry
+    // (a ragged batch's longest sequence can make them far longer)
+    for (int parts = p_hi; parts >= p_lo; --parts) {  // finest first
+      const int pb = blocks(parts);
+      if (pb < pb_min) continue;
+      if (wgs(pb) <= res.cus) return pb <= 2 * pb_round ? pb : pb_round;
+    }
+  }
+  return pb_round;
 }
 
 int max_parts_for(int max_context, int part_blocks) {
