@@ -334,7 +334,8 @@ typedef struct pkv_decode_args {
                                      slot pkv_seq_reserve gave that token; any
                                      copy-on-write pairs already copied), then
                                      attended like every other token. Same bytes
-                                     as pkv_append_kv. fp16 pools only.          */
+                                     as pkv_append_kv (int8 pools: quantised on
+                                     write by the same rule).                    */
   const void* v_new_dev;
   const int32_t* prefix_plan_dev; /* optional shared-prefix plan (NULL = none):
                                      pkv_plan_shared_prefix's output for these
@@ -414,7 +415,7 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * INVALID_ARG: null pointers, ctx_len == 0 or > 16*max_blocks or >
  * max_context (host copy), workspace too small or misaligned,
  * partition_tokens not a multiple of 16, only one of k_new/v_new given.
- * UNSUPPORTED: head_dim/group size not built, fused append on int8. */
+ * UNSUPPORTED: head_dim/group size not built. */
 int pkv_paged_decode(const pkv_decode_args* args, void* stream);
 
 /* Workspace bytes pkv_paged_decode needs with a shared-prefix plan of

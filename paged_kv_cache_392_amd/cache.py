@@ -51,6 +51,30 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def _check_on(dev, **tensors):
+    """Every tensor must live on ``dev``, the cache's GPU: the library reads
+    them through raw device addresses."""
+    if dev.type != "cuda":
+        raise ValueError(f"the cache's pool is on {dev}: device calls need it on a GPU")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the cache on {dev}")
+
+
+def _check_host_lens(host, B):
+    if host is not None and host.shape != (B,):
+        raise ValueError(f"context_lens_host must hold {B} lengths (got shape {host.shape})")
+
+
+def _check_tables(block_tables, context_lens, B):
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or block_tables.shape[1] < 1:
+        raise ValueError(f"block_tables must be [{B}, max_blocks] (got {list(block_tables.shape)})")
+    if context_lens.numel() != B:
+        raise ValueError(f"context_lens must hold {B} lengths (got {context_lens.numel()})")
+
+
 def _dev_i32(a, device):
     t = torch.from_numpy(np.ascontiguousarray(a, np.int32))
     if t.numel() == 0:
@@ -71,6 +95,8 @@ class PagedKVCache:
         self.cfg = C.make_config(num_layers, num_blocks, num_kv_heads, head_dim, dtype)
         self.dtype = dtype
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.num_layers, self.num_blocks = num_layers, num_blocks
         self.num_kv_heads, self.head_dim = num_kv_heads, head_dim
         self.nbytes = C.pkv_pool_bytes(self.cfg)
@@ -179,6 +205,11 @@ class PagedKVCache:
             raise ValueError(f"k, v must be [n, {self.num_kv_heads}, {self.head_dim}]")
         if slots_dev.numel() != n:
             raise ValueError("one slot per token")
+        if slots_dev.dtype != torch.int32 or not slots_dev.is_contiguous():
+            raise TypeError("slots must be a contiguous int32 tensor")
+        if not 0 <= layer < self.num_layers:
+            raise ValueError(f"layer {layer} out of range [0, {self.num_layers})")
+        _check_on(self.device, k=k, v=v, slots=slots_dev)
         C.pkv_append_kv(self.cfg, self.pool.data_ptr(), layer, k.data_ptr(), v.data_ptr(),
                         slots_dev.data_ptr(), n, _stream())
 
@@ -190,6 +221,10 @@ class PagedKVCache:
         leading layer axis ``[L, ...]`` every layer is written; without it
         the pool must have one layer. Returns the device slot tensor."""
         seqs = [seq] if isinstance(seq, (int, np.integer)) else list(seq)
+        if len(set(int(x) for x in seqs)) != len(seqs):
+            # one token per sequence: a sequence named twice would have two
+            # appends racing on its tail block (and, for int8, on its scale)
+            raise ValueError("append_kv: a sequence appears more than once in the list")
         per_layer = k.dim() == 4
         n = k.shape[1] if per_layer else k.shape[0]
         counts = [n] if len(seqs) == 1 and isinstance(seq, (int, np.integer)) else [1] * len(seqs)
@@ -237,19 +272,27 @@ class PagedKVCache:
             raise TypeError("q must be float16 [T, Hq, D]")
         q = q.contiguous()
         T, Hq, D = q.shape
+        if D != self.head_dim or Hq % self.num_kv_heads:
+            raise ValueError(f"q must be [T, Hq, {self.head_dim}] with Hq a multiple of {self.num_kv_heads}")
         ql = np.ascontiguousarray(q_lens, np.int64)
-        if ql.sum() != T:
-            raise ValueError("q_lens must add up to the rows of q")
+        if ql.ndim != 1 or ql.sum() != T or (ql < 0).any():
+            raise ValueError("q_lens must be non-negative and add up to the rows of q")
         B = len(ql)
-        starts = np.zeros(B + 1, np.int32)
-        starts[1:] = np.cumsum(ql)
-        starts_dev = _dev_i32(starts, self.device)
-        if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-            raise TypeError("block_tables and context_lens must be int32")
+        _check_tables(block_tables, context_lens, B)
         block_tables = block_tables.contiguous()
         context_lens = context_lens.contiguous()
         max_blocks = block_tables.shape[1]
         host = None if context_lens_host is None else np.ascontiguousarray(context_lens_host, np.int32)
+        _check_host_lens(host, B)
+        if out is not None and (tuple(out.shape) != (T, Hq, D) or out.dtype != torch.float16
+                                or not out.is_contiguous()):
+            raise ValueError(f"out must be a contiguous float16 [{T}, {Hq}, {D}] tensor")
+        if not 0 <= layer < self.num_layers:
+            raise ValueError(f"layer {layer} out of range [0, {self.num_layers})")
+        _check_on(self.device, q=q, block_tables=block_tables, context_lens=context_lens, out=out)
+        starts = np.zeros(B + 1, np.int32)
+        starts[1:] = np.cumsum(ql)
+        starts_dev = _dev_i32(starts, self.device)
         if max_context is None:
             max_context = int(host.max()) if host is not None else max_blocks * 16
         if scale is None:
@@ -305,14 +348,25 @@ def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=
         raise TypeError("q must be float16 [B, Hq, D]")
     q = q.contiguous()
     B, Hq, D = q.shape
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise TypeError("block_tables and context_lens must be int32")
+    if D != cache.head_dim or Hq % cache.num_kv_heads:
+        raise ValueError(f"q must be [B, Hq, {cache.head_dim}] with Hq a multiple of {cache.num_kv_heads}")
+    _check_tables(block_tables, context_lens, B)
     block_tables = block_tables.contiguous()
     context_lens = context_lens.contiguous()
     max_blocks = block_tables.shape[1]
     host = None
     if context_lens_host is not None:
         host = np.ascontiguousarray(context_lens_host, np.int32)
+    _check_host_lens(host, B)
+    if out is not None and (tuple(out.shape) != (B, Hq, D) or out.dtype != torch.float16 or not out.is_contiguous()):
+        raise ValueError(f"out must be a contiguous float16 [{B}, {Hq}, {D}] tensor")
+    if not 0 <= layer < cache.num_layers:
+        raise ValueError(f"layer {layer} out of range [0, {cache.num_layers})")
+    if k_new is not None and v_new is not None:
+        k_new, v_new = k_new.contiguous(), v_new.contiguous()
+    _check_on(cache.device, q=q, block_tables=block_tables, context_lens=context_lens, out=out,
+              workspace=workspace, k_new=k_new, v_new=v_new,
+              prefix_plan=None if prefix_plan is None else prefix_plan.dev)
     if max_context is None:
         max_context = int(host.max()) if host is not None else max_blocks * 16
     if scale is None:
@@ -325,7 +379,7 @@ def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=
                                                        partition_tokens, n_groups)
     else:
         ws_bytes = C.pkv_decode_workspace_bytes(cache.cfg, B, Hq, max_context, partition_tokens)
-    if workspace is None or workspace.numel() < ws_bytes:
+    if workspace is None or workspace.numel() * workspace.element_size() < ws_bytes:
         workspace = cache.decode_workspace(ws_bytes)
     args = C.pkv_decode_args()
     args.cfg = C.ctypes.pointer(cache.cfg)
@@ -342,12 +396,11 @@ def paged_decode(cache, q, block_tables, context_lens, layer=0, out=None, scale=
     args.out_dev = out.data_ptr()
     args.scale = scale
     args.workspace_dev = workspace.data_ptr()
-    args.workspace_bytes = workspace.numel()
+    args.workspace_bytes = workspace.numel() * workspace.element_size()
     args.partition_tokens = partition_tokens
     if (k_new is None) != (v_new is None):
         raise ValueError("give both k_new and v_new, or neither")
     if k_new is not None:
-        k_new, v_new = k_new.contiguous(), v_new.contiguous()
         shape = (B, cache.num_kv_heads, D)
         if k_new.dtype != torch.float16 or tuple(k_new.shape) != shape or tuple(v_new.shape) != shape \
                 or v_new.dtype != torch.float16:

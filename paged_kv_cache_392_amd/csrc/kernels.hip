@@ -172,18 +172,50 @@ __global__ __launch_bounds__(256) void append_kv_f16_kernel(uint4* __restrict__ 
   Vl[dst] = v[src];
 }
 
-// int8 quantise-on-write. One wave per (token i, KV head h, K or V); the
-// wave whose token opens a run of consecutive tokens writing the same block
-// appends the whole run in order (a block's scale depends on the order). Per
-// token, with a = max |x| of its row and s the block's scale:
+// int8 quantise-on-write of one fp16 row x into offset `off` of a (block,
+// KV head) tile whose scale is sc, by one wave (lane l owns dims l + 64 e).
+// With a = max |x| of the row:
 //   offset 0:        s' = fp16(a / 127)           (the block is opened)
 //   a <= 127 * s:    s' = s                       (the row fits the range)
 //   otherwise:       s' = fp16(a / 127), and the earlier rows' codes are
 //                    re-expressed: rint(code * s / s')
 // then the row's codes are rint(x / s'), clipped to [-127, 127]; a zero
-// scale gives zero codes. Divisions are IEEE fp32, rint rounds half to
-// even. Each lane owns the same D/64 dims of every row, so it only reads
-// back bytes it wrote itself.
+// scale gives zero codes. Divisions are IEEE fp32, rint rounds half to even.
+// Each lane reads back only bytes it wrote itself. Returns s'.
+template <int D>
+__device__ __forceinline__ float quantise_row_i8(int8_t* tile, int off, const float (&x)[D / 64], float sc) {
+  constexpr int PER = D / 64;  // dims per lane
+  const int lane = threadIdx.x & 63;
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) a = fmaxf(a, fabsf(x[e]));
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) a = fmaxf(a, xor_shfl(a, m));
+  float sn = sc;
+  bool requant = false;
+  if (off == 0 || !(a <= 127.0f * sc)) {
+    sn = float(_Float16(a / 127.0f));
+    requant = off > 0;
+  }
+  if (requant) {
+    for (int r = 0; r < off; ++r)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        int8_t& c = tile[r * D + lane + 64 * e];
+        c = sn == 0.0f ? int8_t(0) : int8_t(fminf(fmaxf(__builtin_rintf(float(c) * sc / sn), -127.0f), 127.0f));
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e)
+    tile[off * D + lane + 64 * e] =
+        sn == 0.0f ? int8_t(0) : int8_t(fminf(fmaxf(__builtin_rintf(x[e] / sn), -127.0f), 127.0f));
+  return sn;
+}
+
+// int8 append. One wave per (token i, KV head h, K or V); the wave whose
+// token opens a run of consecutive tokens writing the same block appends the
+// whole run in order (a block's scale depends on the order), each token by
+// quantise_row_i8.
 template <int D>
 __global__ __launch_bounds__(64) void append_kv_i8_kernel(int8_t* __restrict__ Kl, int8_t* __restrict__ Vl,
                                                           _Float16* __restrict__ Sl,
@@ -209,35 +241,10 @@ __global__ __launch_bounds__(64) void append_kv_i8_kernel(int8_t* __restrict__ K
   for (int t = i; t < n; ++t) {
     const int sl = slots[t];
     if (t > i && (sl < 0 || sl >= nslots || sl / BT != blk)) break;
-    const int off = sl % BT;
     float x[PER];
-    float a = 0.0f;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      x[e] = float(src[(int64_t(t) * Hkv + h) * D + lane + 64 * e]);
-      a = fmaxf(a, fabsf(x[e]));
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) a = fmaxf(a, xor_shfl(a, m));
-    float sn = sc;
-    bool requant = false;
-    if (off == 0 || !(a <= 127.0f * sc)) {
-      sn = float(_Float16(a / 127.0f));
-      requant = off > 0;
-    }
-    if (requant) {
-      for (int r = 0; r < off; ++r)
-#pragma unroll
-        for (int e = 0; e < PER; ++e) {
-          int8_t& c = tile[r * D + lane + 64 * e];
-          c = sn == 0.0f ? int8_t(0) : int8_t(fminf(fmaxf(__builtin_rintf(float(c) * sc / sn), -127.0f), 127.0f));
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-      tile[off * D + lane + 64 * e] =
-          sn == 0.0f ? int8_t(0) : int8_t(fminf(fmaxf(__builtin_rintf(x[e] / sn), -127.0f), 127.0f));
-    sc = sn;
+    for (int e = 0; e < PER; ++e) x[e] = float(src[(int64_t(t) * Hkv + h) * D + lane + 64 * e]);
+    sc = quantise_row_i8<D>(tile, sl % BT, x, sc);
   }
   if (lane == 0) *sp = _Float16(sc);
 }
@@ -856,6 +863,244 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
                                                                   R, n, pos0 + 1, prm.scale_log2, qrow, limit, emit);
 }
 
+// ---------------------------------------------------------------------------
+// int8 decode stream: both products on the matrix cores
+
+// One wave's stream over its int8 tiles (logical blocks first, first + 4,
+// ..., n_my of them; block ids one per lane in blk_lane), two tiles per step:
+//   * scores S^T (16 tokens x 16 rows) = K (16 x D) . Q^T (D x 16) per tile,
+//     v_mfma_f32_16x16x32_f16 over D/32 chunks, with the codes entering as
+//     fp16 1152 + x (exact; the term 1152 * sum_d q[h][d] is removed from
+//     every score of head h). Row r of Q^T is query head r % G of the group,
+//     so rows repeat when G < 16; lane (n, j) receives tokens 4j..4j+3 of
+//     row n, and every lane works on the single head n % G;
+//   * base-2 online softmax per row, the running max raised only when a
+//     score beats it by more than 2^8 (a rare, wave-uniform branch);
+//   * values O^T (D x 16 rows) += V^T (D x 32 tokens) . P^T (32 tokens x 16
+//     rows), one v_mfma_f32_16x16x32_f16 per 16 dims for the two tiles. The
+//     k slots 8j..8j+7 of lane (n, j) are tokens 4j..4j+3 of the first tile,
+//     then of the second: the scores the lane already holds, so P goes from
+//     the score MFMA to the value MFMA without leaving the lane. P enters in
+//     fp16, pre-scaled by its tile's V scale and 2^-ve (ve from the wave's
+//     largest V scale, so that p * scale_V * 2^-ve <= 2^15 with p <= 2^8);
+//     the V codes, biased like K, are staged in LDS row-major and read
+//     transposed with ds_read_b64_tr_b8 (within a 16-lane group, output lane
+//     i receives byte i % 8 of source lanes i / 8 + 2k, k = 0..7: checked on
+//     gfx950 with a one-wave probe); the bias part 1152 * sum_t P[t] is kept
+//     in vb and removed at the end.
+// Masked tokens (past the context, or of a tile whose id is out of range)
+// get probability 0; their codes are finite, so they add exact zeros. The
+// wave's (m, l, o[D]) per head go to mo ([G][D]) and mml ([G][2]).
+template <int D, int G>
+__device__ __forceinline__ void wave_stream_i8(const DecodeParams& prm, int g, int blk_lane, int n_my, int first,
+                                               int ctx, const half8_t (&qa)[D / 32], float* mo, float* mml) {
+  constexpr int NCH = D / 32;   // score MFMA chunks of 32 dims
+  constexpr int NDB = D / 16;   // value MFMA blocks of 16 dims
+  constexpr int KL = D / 64;    // K 16-byte loads per lane per tile
+  constexpr int VL = D / 64;    // V 16-byte loads per lane per tile
+  constexpr int VPR = D / 16;   // 16-byte pieces per V row
+  constexpr int VR = D + 16;    // bytes per staged V row: the 16 rows of a tile on distinct bank offsets
+  constexpr int TILE = BT * D;  // bytes per (block, KV head) tile
+  __shared__ __align__(16) char vst_all[WAVES][2 * BT * VR];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lj = lane >> 4;
+  char* vst = vst_all[wave];
+  const int Hkv = prm.Hkv;
+  const char* Kc = static_cast<const char*>(prm.K);
+  const char* Vc = static_cast<const char*>(prm.V);
+  const int64_t head_off = int64_t(g) * TILE;
+  const int64_t blk_stride = int64_t(Hkv) * TILE;
+
+  // each tile's (K, V) scales, one pair per lane like the block ids; a tile
+  // takes its pair with readlane when it is consumed
+  const uint32_t sc_lane = unsigned(blk_lane) < unsigned(prm.num_blocks)
+                               ? reinterpret_cast<const uint32_t*>(prm.scales)[int64_t(blk_lane) * Hkv + g]
+                               : 0u;
+  // 1152 * sum_d q[h][d] for this lane's head h = ln % G
+  float qs = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qs += float(qa[c][e]);
+  qs += xor_shfl(qs, 16);
+  qs += xor_shfl(qs, 32);
+  const float kbias = I8_BIAS * qs;
+
+  float4_t ob[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) ob[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m = -INFINITY, l = 0.0f, vb = 0.0f;
+  float vexp_scale = 1.0f, vexp_unscale = 1.0f;
+
+  struct Pair {
+    uint4 k[2][KL];
+    uint4 v[2][VL];
+    int blk[2];
+  };
+  // Tiles 2 pi and 2 pi + 1 (the second past n_my when n_my is odd: a
+  // padding tile, loaded from block 0 and fully masked). it <= 63 always.
+  auto load_pair = [&](int pi, Pair& t) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int blk = __builtin_amdgcn_readlane(blk_lane, 2 * pi + sub);
+      t.blk[sub] = blk;
+      const int safe = unsigned(blk) < unsigned(prm.num_blocks) ? blk : 0;
+      const char* kb = Kc + safe * blk_stride + head_off;
+      const char* vb_ = Vc + safe * blk_stride + head_off;
+#pragma unroll
+      for (int i = 0; i < KL; ++i) t.k[sub][i] = load_nt(kb + ln * D + (4 * i + lj) * 16);
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int q = lane + 64 * i;
+        t.v[sub][i] = load_nt(vb_ + (q / VPR) * D + (q % VPR) * 16);
+      }
+    }
+  };
+
+  // source address of this lane for the transpose read of dims 16 nb..: the
+  // 16 lanes of group lj cover tokens 4 lj..4 lj + 3 of both tiles, two
+  // 8-byte halves of the 16 dims each
+  const int tr_ofs = ((ln >> 3) * BT + 4 * lj + ((ln >> 1) & 3)) * VR + 8 * (ln & 1);
+  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+  auto compute_pair = [&](int pi, Pair& t) {
+    // stage both V tiles (rows of D codes, padded)
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int q = lane + 64 * i;
+        *reinterpret_cast<uint4*>(vst + (sub * BT + q / VPR) * VR + (q % VPR) * 16) = t.v[sub][i];
+      }
+    float4_t acc[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      acc[sub] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint4& w = t.k[sub][c >> 1];
+        uint32_t a0, a1, a2, a3;
+        i8x4_to_f16x4_biased((c & 1) ? w.z : w.x, a0, a1);
+        i8x4_to_f16x4_biased((c & 1) ? w.w : w.y, a2, a3);
+        const half8_t kb = __builtin_bit_cast(half8_t, make_uint4(a0, a1, a2, a3));
+        acc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb, qa[c], acc[sub], 0, 0, 0);
+      }
+    }
+    float s[8], vsc[2];
+    bool ok[8];
+    float smax = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int it = 2 * pi + sub;
+      const uint32_t sc = __builtin_amdgcn_readlane(sc_lane, it);
+      const float ks = prm.scale_log2 * lo_half(sc);
+      const float kbs = kbias * ks;
+      vsc[sub] = hi_half(sc) * vexp_scale;
+      const int j = first + WAVES * it;
+      const bool tile_ok = it < n_my && unsigned(t.blk[sub]) < unsigned(prm.num_blocks);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * sub + e;
+        ok[k] = tile_ok && j * BT + 4 * lj + e < ctx;
+        s[k] = ok[k] ? __builtin_fmaf(acc[sub][e], ks, -kbs) : -INFINITY;
+        smax = fmaxf(smax, s[k]);
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(smax > m + LAZY_MAX)) {  // wave-uniform, rare after the first step
+      float mx = smax;
+      mx = fmaxf(mx, xor_shfl(mx, 16));
+      mx = fmaxf(mx, xor_shfl(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.0f : exp2_fast(m - mn);
+      m = mn;
+      l *= alpha;
+      vb *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) ob[i] *= alpha;
+    }
+    half8_t pt;
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      const float p0 = ok[k] ? exp2_fast(s[k] - m) : 0.0f;
+      const float p1 = ok[k + 1] ? exp2_fast(s[k + 1] - m) : 0.0f;
+      l += p0 + p1;
+      const half2_t ph = {(_Float16)(p0 * vsc[k >> 2]), (_Float16)(p1 * vsc[k >> 2])};
+      vb = __builtin_amdgcn_fdot2(ph, ones, vb, false);
+      pt[k] = ph.x;
+      pt[k + 1] = ph.y;
+    }
+    // the staged V rows of the whole wave are visible to the transpose reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb) {
+      typedef int int2_t __attribute__((ext_vector_type(2)));
+      const int2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) int2_t*)(vst + tr_ofs + 16 * nb));
+      uint32_t a0, a1, b0, b1;
+      i8x4_to_f16x4_biased(uint32_t(r.x), a0, a1);  // first tile, tokens 4j..4j+3
+      i8x4_to_f16x4_biased(uint32_t(r.y), b0, b1);  // second tile
+      const half8_t va = __builtin_bit_cast(half8_t, make_uint4(a0, a1, b0, b1));
+      ob[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt, ob[nb], 0, 0, 0);
+    }
+    // the next step's stores stay behind these reads
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  auto take_vexp = [&]() {
+    float vmax = fabsf(hi_half(sc_lane));
+#pragma unroll
+    for (int mk = 1; mk < 64; mk <<= 1) vmax = fmaxf(vmax, xor_shfl(vmax, mk));
+    const int ve = vmax > 128.0f ? int(ceilf(__builtin_log2f(vmax))) - 7 : 0;
+    vexp_scale = __builtin_ldexpf(1.0f, -ve);
+    vexp_unscale = __builtin_ldexpf(1.0f, ve);
+  };
+
+  // Double-buffered over pairs: the next pair's loads are issued before the
+  // current pair is used.
+  const int npairs = (n_my + 1) / 2;
+  if (npairs > 0) {
+    Pair pa, pb;
+    int pi = 0;
+    load_pair(0, pa);
+    take_vexp();
+    for (; pi + 2 < npairs; pi += 2) {
+      load_pair(pi + 1, pb);
+      compute_pair(pi, pa);
+      load_pair(pi + 2, pa);
+      compute_pair(pi + 1, pb);
+    }
+    if (pi + 1 < npairs) {
+      load_pair(pi + 1, pb);
+      compute_pair(pi, pa);
+      compute_pair(pi + 1, pb);
+    } else {
+      compute_pair(pi, pa);
+    }
+  }
+
+  // row totals over the four token groups; rows n and n + G (...) hold the
+  // same head, rows below G are written
+  l += xor_shfl(l, 16);
+  l += xor_shfl(l, 32);
+  vb += xor_shfl(vb, 16);
+  vb += xor_shfl(vb, 32);
+  if (ln < G) {
+    const float bias = I8_BIAS * vb;
+#pragma unroll
+    for (int nb = 0; nb < NDB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mo[ln * D + 16 * nb + 4 * lj + e] = (ob[nb][e] - bias) * vexp_unscale;
+    if (lj == 0) {
+      mml[2 * ln] = m;
+      mml[2 * ln + 1] = l;
+    }
+  }
+}
+
 // Two work-groups per CU are asked of the register allocator where they
 // fit without spills (G <= 4; fp16 at D = 64): the shared-prefix role would
 // otherwise push the fp16 kernels past 256 registers a lane. The other
@@ -878,16 +1123,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
 // After its last tile the work-group writes one (m, l, o[D]) partial per
 // query head for the merge kernel, or the final fp16 row when the sequence
 // has a single partition.
-// COMPACT: the split grid holds the (sequence, partition) pairs that have
-// blocks and nothing else (no plan). The plain grid holds max-context
+// GRID_COMPACT: the split grid holds the (sequence, partition) pairs that
+// have blocks and nothing else (no plan). The plain grid holds max-context
 // partitions for every sequence, and a work-group past its sequence's last
 // partition exits once its length has arrived; under a full HBM stream that
 // holds its slot for microseconds, and real work-groups queue behind such
 // exits. The compact grid is chosen by the host from its copy of the lengths
 // and is a separate instantiation, so the plain grid's code is untouched by
 // the scan (sharing one body cost the shared-prefix launch 8%).
-template <int D, int G, bool I8, bool COMPACT>
-__global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void paged_decode_kernel(DecodeParams prm) {
+// GRID_PLAN: the plain grid led by the shared-prefix planes; the multi-row
+// attention of that role needs more registers than the split role, so
+// launches without a plan use GRID_PLAIN, which leaves it out.
+enum { GRID_PLAIN = 0, GRID_COMPACT = 1, GRID_PLAN = 2 };
+
+template <bool I8, int D, int G>
+constexpr int decode_wgs_per_cu() {
+  return (I8 || G <= 4 || D == 64) ? 2 : 1;
+}
+
+template <int D, int G, bool I8, int GRID>
+__global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_decode_kernel(DecodeParams prm) {
+  constexpr bool COMPACT = GRID == GRID_COMPACT;
   using S = Shape<D, G, I8>;
   const int g = blockIdx.x;
   __shared__ float p_lds[WAVES][BT][G];
@@ -898,7 +1154,7 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     static_assert(sizeof(merge_o) >= (WAVES + 2) * sizeof(int), "compact scan scratch");
     compact_pair(prm, blockIdx.y + gridDim.y * blockIdx.z, reinterpret_cast<int*>(&merge_o[0][0][0]), bc, pc);
     if (bc < 0) return;  // uniform over the work-group
-  } else {
+  } else if constexpr (GRID == GRID_PLAN) {
     // With a shared-prefix plan the first prefix_z planes of the grid are
     // shared-prefix work-groups: dispatched first, they run beside the split
     // work-groups of the same launch.
@@ -909,7 +1165,7 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     }
   }
   const int b = COMPACT ? bc : int(blockIdx.y);
-  const int p = COMPACT ? pc : int(blockIdx.z) - prm.prefix_z;
+  const int p = COMPACT ? pc : int(blockIdx.z) - (GRID == GRID_PLAN ? prm.prefix_z : 0);
   const int Hkv = prm.Hkv, Hq = Hkv * G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -954,6 +1210,52 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
   const int n_my = first < je ? (je - first + WAVES - 1) / WAVES : 0;  // <= 64
   const int blk_lane = lane < n_my ? blk_raw : -1;
 
+  const char* Kc = static_cast<const char*>(prm.K);
+  const char* Vc = static_cast<const char*>(prm.V);
+  const int64_t head_off = int64_t(g) * S::TILE;
+  const int64_t blk_stride = int64_t(Hkv) * S::TILE;
+
+  // Fused append: the new token is the last of the context, at logical
+  // position ctx - 1, in this sequence's last partition. That work-group
+  // writes its k and v rows for head g into the slot the table gives (fp16:
+  // a bitwise copy; int8: quantised on write, its block's scale raised and
+  // earlier rows re-rounded when needed), then reads them back with the rest
+  // of the tile; no other work-group reads that block of this head in the
+  // launch (a slot written at a non-zero offset of a shared block was moved
+  // to a private block by copy-on-write).
+  if (prm.k_new && p == nparts - 1) {
+    const int t = ctx - 1;
+    const int blk = trow[t / BT];
+    if (unsigned(blk) < unsigned(prm.num_blocks)) {
+      if constexpr (I8) {
+        if (wave < 2) {  // wave 0 writes the K row, wave 1 the V row
+          const _Float16* src = reinterpret_cast<const _Float16*>(wave ? prm.v_new : prm.k_new) +
+                                (int64_t(b) * Hkv + g) * D;
+          int8_t* tile = reinterpret_cast<int8_t*>(const_cast<char*>(wave ? Vc : Kc) + blk * blk_stride + head_off);
+          _Float16* sp = const_cast<_Float16*>(prm.scales) + (int64_t(blk) * Hkv + g) * 2 + wave;
+          float x[D / 64];
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e) x[e] = float(src[lane + 64 * e]);
+          const float sn = quantise_row_i8<D>(tile, t % BT, x, float(*sp));
+          if (lane == 0) *sp = _Float16(sn);
+        }
+      } else {
+        constexpr int PIECES = D / 8;  // 16-byte pieces per fp16 row
+        if (tid < 2 * PIECES) {
+          const int c = tid % PIECES;
+          const uint4* src = (tid < PIECES ? prm.k_new : prm.v_new) + (int64_t(b) * Hkv + g) * PIECES + c;
+          char* dst = const_cast<char*>(tid < PIECES ? Kc : Vc) + blk * blk_stride + head_off + (t % BT) * (D * 2);
+          reinterpret_cast<uint4*>(dst)[c] = *src;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+  }
+
+  if constexpr (I8) {
+    wave_stream_i8<D, G>(prm, g, blk_lane, n_my, first, ctx, qa, &merge_o[wave][0][0], &merge_ml[wave][0][0]);
+  } else {
   // mh: running max per head (wave-uniform); lrow: this lane's share of the
   // softmax denominator per score row; o: V accumulators, D/16 dims x G heads
   float mh[G], o[G][S::CE], lrow[4];
@@ -966,63 +1268,10 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
 #pragma unroll
   for (int e = 0; e < 4; ++e) lrow[e] = 0.0f;
 
-
-  const char* Kc = static_cast<const char*>(prm.K);
-  const char* Vc = static_cast<const char*>(prm.V);
-  const int64_t head_off = int64_t(g) * S::TILE;
-  const int64_t blk_stride = int64_t(Hkv) * S::TILE;
-
-  // Fused append (fp16 pools): the new token is the last of the context, at
-  // logical position ctx - 1, in this sequence's last partition. That
-  // work-group stores its k and v rows for head g into the slot the table
-  // gives, then reads them back with the rest of the tile; no other
-  // work-group reads that slot in this launch (a slot written at a non-zero
-  // offset of a shared block was moved to a private block by copy-on-write).
-  if constexpr (!I8) {
-    if (prm.k_new && p == nparts - 1) {
-      constexpr int PIECES = D / 8;  // 16-byte pieces per fp16 row
-      const int t = ctx - 1;
-      const int blk = trow[t / BT];
-      if (tid < 2 * PIECES && unsigned(blk) < unsigned(prm.num_blocks)) {
-        const int c = tid % PIECES;
-        const uint4* src = (tid < PIECES ? prm.k_new : prm.v_new) + (int64_t(b) * Hkv + g) * PIECES + c;
-        char* dst = const_cast<char*>(tid < PIECES ? Kc : Vc) + blk * blk_stride + head_off + (t % BT) * (D * 2);
-        reinterpret_cast<uint4*>(dst)[c] = *src;
-        __builtin_amdgcn_s_waitcnt(0);
-      }
-      __syncthreads();
-    }
-  }
-
   struct Tile {
     uint4 k[S::KL];
     uint4 v[S::NI];
     int blk;
-    int it;  // int8: the tile's lane in sc_lane, which holds its (K, V) fp16 scales
-  };
-
-  // int8: the scales of this wave's tiles, one (K, V) pair per lane like the
-  // block ids, loaded once; each tile takes its pair with readlane when it is
-  // consumed, so the first tile's loads do not wait for them. The value
-  // probabilities enter v_dot2 in fp16, pre-scaled by the tile's V scale and
-  // 2^-vexp, with vexp chosen from the wave's largest V scale so that
-  // p * scale_V * 2^-vexp <= 2^8 * 2^7 (p <= 2^8 under the lazy max); vexp is
-  // taken after the first tile's loads are issued.
-  uint32_t sc_lane = 0;
-  float vexp_scale = 1.0f, vexp_unscale = 1.0f;
-  if constexpr (I8) {
-    const bool ok = unsigned(blk_lane) < unsigned(prm.num_blocks);
-    sc_lane = ok ? reinterpret_cast<const uint32_t*>(prm.scales)[int64_t(blk_lane) * Hkv + g] : 0u;
-  }
-  auto take_vexp = [&]() {
-    if constexpr (I8) {
-      float vmax = fabsf(hi_half(sc_lane));
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) vmax = fmaxf(vmax, xor_shfl(vmax, m));
-      const int ve = vmax > 128.0f ? int(ceilf(__builtin_log2f(vmax))) - 7 : 0;
-      vexp_scale = __builtin_ldexpf(1.0f, -ve);
-      vexp_unscale = __builtin_ldexpf(1.0f, ve);
-    }
   };
 
   // A bad id (outside the pool) still loads block 0, which exists; compute()
@@ -1030,7 +1279,6 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
   auto load = [&](int it, Tile& t) {
     const int blk = __builtin_amdgcn_readlane(blk_lane, it);
     t.blk = blk;
-    if constexpr (I8) t.it = it;
     const int safe = unsigned(blk) < unsigned(prm.num_blocks) ? blk : 0;
     const char* kb = Kc + safe * blk_stride + head_off;
     const char* vb = Vc + safe * blk_stride + head_off;
@@ -1052,60 +1300,13 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     }
   };
 
-  // int8: the K codes enter the MFMA as 1152 + x, so every score of head h
-  // carries 1152 * sum_d q[h][d]; qb[h] holds that term (wave-uniform).
-  float qb[G];
-  if constexpr (I8) {
-    float part = 0.0f;  // this lane's dims of head kn % G
-#pragma unroll
-    for (int c = 0; c < S::NCH; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part += float(qa[c][e]);
-    part += xor_shfl(part, 16);
-    part += xor_shfl(part, 32);
-#pragma unroll
-    for (int h = 0; h < G; ++h) qb[h] = I8_BIAS * read_lane(part, h);
-  }
-  // (fixed for the whole stream: taken once per lane)
-  float4_t kbias = {0.0f, 0.0f, 0.0f, 0.0f};
-  if constexpr (I8) {
-    if constexpr (G == 8) {
-      kbias = half_of8(qb, odd);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kbias[e] = qb[e % G];
-    }
-  }
-  // int8 values: pairs of rows (i, i + 1) are contracted with v_dot2 on fp16
-  // probabilities and biased codes; vb[h] collects the bias part to remove.
-  constexpr bool PAIRS = I8 && S::NI >= 2;
-  float vb[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) vb[h] = 0.0f;
-
   auto compute = [&](int j, Tile& t) {
     const bool blk_ok = unsigned(t.blk) < unsigned(prm.num_blocks);
-    float kscale = prm.scale_log2, vscale = 1.0f;
-    if constexpr (I8) {
-      const uint32_t sc = __builtin_amdgcn_readlane(sc_lane, t.it);
-      kscale *= lo_half(sc);
-      vscale = PAIRS ? hi_half(sc) * vexp_scale : hi_half(sc);
-    }
+    const float kscale = prm.scale_log2;
     float4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int c = 0; c < S::NCH; ++c) {
-      half8_t kb;
-      if constexpr (I8) {
-        const uint4& w = t.k[c >> 1];
-        uint32_t a0, a1, a2, a3;
-        i8x4_to_f16x4_biased((c & 1) ? w.z : w.x, a0, a1);
-        i8x4_to_f16x4_biased((c & 1) ? w.w : w.y, a2, a3);
-        kb = __builtin_bit_cast(half8_t, make_uint4(a0, a1, a2, a3));
-      } else {
-        kb = __builtin_bit_cast(half8_t, t.k[c]);
-      }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kb, acc, 0, 0, 0);
-    }
+    for (int c = 0; c < S::NCH; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], __builtin_bit_cast(half8_t, t.k[c]), acc, 0, 0, 0);
     // A score of a row past the context (stale or poisoned) only reaches its
     // own column, and is replaced by -inf here.
     const bool tvalid = blk_ok && (j * BT + kn) < ctx;
@@ -1114,9 +1315,7 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     float4_t mr = mrows();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float raw = acc[e];
-      if constexpr (I8) raw -= kbias[e];  // remove 1152 * sum(q) of the biased codes
-      s[e] = tvalid ? raw * kscale : -INFINITY;
+      s[e] = tvalid ? acc[e] * kscale : -INFINITY;
       need |= s[e] > mr[e] + LAZY_MAX;
     }
     if (__builtin_amdgcn_ballot_w64(need)) {  // wave-uniform, rare after the first tile
@@ -1135,7 +1334,6 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
         mh[h] = mn;
 #pragma unroll
         for (int e = 0; e < S::CE; ++e) o[h][e] *= alpha[h];
-        vb[h] *= alpha[h];
       }
       if constexpr (G == 8) {
         const float4_t a4 = half_of8(alpha, odd);
@@ -1172,7 +1370,7 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
 #pragma unroll
     for (int i = 0; i < S::NI; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) pv[i][h] = p_lds[wave][vt + S::RPI * i][h] * vscale;
+      for (int h = 0; h < G; ++h) pv[i][h] = p_lds[wave][vt + S::RPI * i][h];
     // rows past the context (stale or poisoned) must contribute exact zeros
     const bool tail = !blk_ok || (j + 1) * BT > ctx;
     if (tail) {
@@ -1180,62 +1378,17 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
       for (int i = 0; i < S::NI; ++i)
         if (!blk_ok || j * BT + vt + S::RPI * i >= ctx) t.v[i] = make_uint4(0, 0, 0, 0);
     }
-    if constexpr (PAIRS) {
-#pragma unroll
-      for (int i = 0; i + 1 < S::NI; i += 2) {
-        uint32_t P[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const half2_t ph = {(_Float16)pv[i][h], (_Float16)pv[i + 1][h]};
-          P[h] = __builtin_bit_cast(uint32_t, ph);
-          vb[h] = dot2(P[h], 0x64806480u, vb[h]);  // (1152, 1152)
-        }
-        const uint32_t a4[4] = {t.v[i].x, t.v[i].y, t.v[i].z, t.v[i].w};
-        const uint32_t b4[4] = {t.v[i + 1].x, t.v[i + 1].y, t.v[i + 1].z, t.v[i + 1].w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t alo, ahi, blo, bhi;
-          i8x4_to_f16x4_biased(a4[w], alo, ahi);
-          i8x4_to_f16x4_biased(b4[w], blo, bhi);
-          // (row i, row i + 1) pairs of one dim each
-          const uint32_t x0 = __builtin_amdgcn_perm(blo, alo, 0x05040100u);
-          const uint32_t x1 = __builtin_amdgcn_perm(blo, alo, 0x07060302u);
-          const uint32_t x2 = __builtin_amdgcn_perm(bhi, ahi, 0x05040100u);
-          const uint32_t x3 = __builtin_amdgcn_perm(bhi, ahi, 0x07060302u);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            o[h][4 * w + 0] = dot2(P[h], x0, o[h][4 * w + 0]);
-            o[h][4 * w + 1] = dot2(P[h], x1, o[h][4 * w + 1]);
-            o[h][4 * w + 2] = dot2(P[h], x2, o[h][4 * w + 2]);
-            o[h][4 * w + 3] = dot2(P[h], x3, o[h][4 * w + 3]);
-          }
-        }
-      }
-    } else {
 #pragma unroll
     for (int i = 0; i < S::NI; ++i) {
       const uint32_t w4[4] = {t.v[i].x, t.v[i].y, t.v[i].z, t.v[i].w};
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        if constexpr (I8) {
-          uint32_t lo, hi;
-          i8x4_to_f16x4(w4[w], lo, hi);
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            o[h][4 * w + 0] = fmaf(pv[i][h], lo_half(lo), o[h][4 * w + 0]);
-            o[h][4 * w + 1] = fmaf(pv[i][h], hi_half(lo), o[h][4 * w + 1]);
-            o[h][4 * w + 2] = fmaf(pv[i][h], lo_half(hi), o[h][4 * w + 2]);
-            o[h][4 * w + 3] = fmaf(pv[i][h], hi_half(hi), o[h][4 * w + 3]);
-          }
-        } else {
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            o[h][2 * w + 0] = fmaf(pv[i][h], lo_half(w4[w]), o[h][2 * w + 0]);
-            o[h][2 * w + 1] = fmaf(pv[i][h], hi_half(w4[w]), o[h][2 * w + 1]);
-          }
+        for (int h = 0; h < G; ++h) {
+          o[h][2 * w + 0] = fmaf(pv[i][h], lo_half(w4[w]), o[h][2 * w + 0]);
+          o[h][2 * w + 1] = fmaf(pv[i][h], hi_half(w4[w]), o[h][2 * w + 1]);
         }
       }
-    }
     }
     // the next tile rewrites p_lds: its writes stay behind these reads
     __builtin_amdgcn_wave_barrier();
@@ -1248,7 +1401,6 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     Tile ta, tb;
     int it = 0;
     load(0, ta);
-    take_vexp();
     for (; it + 2 < n_my; it += 2) {
       load(it + 1, tb);
       compute(first + WAVES * it, ta);
@@ -1264,12 +1416,6 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
     }
   }
 
-  if constexpr (PAIRS) {  // remove the bias part and the 2^-vexp pre-scale
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < S::CE; ++e) o[h][e] = (o[h][e] - vb[h]) * vexp_unscale;
-  }
   // wave totals: l over the 16 tokens of each score row, o over the V row groups
   float lh[G];
 #pragma unroll
@@ -1297,6 +1443,7 @@ __global__ __launch_bounds__(256, (G <= 4 || (D == 64 && !I8)) ? 2 : 1) void pag
       merge_ml[wave][h][1] = lh[h];
     }
   }
+  }  // fp16 stream
   __syncthreads();
 
   // merge the 4 waves (fixed order); write the final row or this partition's partial
@@ -1525,7 +1672,7 @@ int choose_part_blocks(int Hkv, int B, int max_context, int partition_tokens, in
 struct Residency {
   int slots, cus;
 };
-Residency resident_wgs(const void* fn) {
+Residency resident_wgs(const void* fn, size_t dyn_lds) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, Residency> known;
   int dev = 0;
@@ -1535,11 +1682,41 @@ Residency resident_wgs(const void* fn) {
   const auto it = known.find(key);
   if (it != known.end()) return it->second;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, dyn_lds) != hipSuccess || per_cu < 1)
+    per_cu = 1;
   if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
   (void)hipGetLastError();  // a failed query above must not be reported by the launch
   return known[key] = Residency{per_cu * cus, cus};
+}
+
+// Dynamic LDS (unused by the kernel) that holds an int8 decode launch to two
+// work-groups per CU where registers and static LDS would allow three: the
+// int8 stream is HBM-bound and runs faster with two longer-lived
+// work-groups per CU (measured on MI355X, int8 batch 16 x 8192 tokens, same
+// box: 45.1-45.4 us at two per CU against 47.0-47.2 at three, and 45.9-46.1
+// with the two-per-CU cut on CUs that could take a third). 0 where at most
+// two fit anyway. Per device and kernel.
+size_t two_per_cu_lds(const void* fn) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> known;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, fn);
+  const auto it = known.find(key);
+  if (it != known.end()) return it->second;
+  size_t extra = 0;
+  int per_cu = 0, lds_cu = 0;
+  hipFuncAttributes attr;
+  if (dev >= 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) == hipSuccess && per_cu > 2 &&
+      hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
+      hipFuncGetAttributes(&attr, fn) == hipSuccess) {
+    const size_t want = size_t(lds_cu) / 3 + 1024;  // a third work-group no longer fits
+    if (want > attr.sharedSizeBytes) extra = want - attr.sharedSizeBytes;
+  }
+  (void)hipGetLastError();  // a failed query above must not be reported by the launch
+  return known[key] = extra;
 }
 
 // Blocks per partition for one launch. Each partition is one work-group and
@@ -1615,26 +1792,28 @@ int max_parts_for(int max_context, int part_blocks) {
 
 typedef void (*decode_fn)(DecodeParams);
 
-template <int D, bool I8, bool COMPACT>
+template <int D, bool I8, int GRID>
 decode_fn pick_g(int G) {
   switch (G) {
-    case 1: return paged_decode_kernel<D, 1, I8, COMPACT>;
-    case 2: return paged_decode_kernel<D, 2, I8, COMPACT>;
-    case 4: return paged_decode_kernel<D, 4, I8, COMPACT>;
-    case 8: return paged_decode_kernel<D, 8, I8, COMPACT>;
+    case 1: return paged_decode_kernel<D, 1, I8, GRID>;
+    case 2: return paged_decode_kernel<D, 2, I8, GRID>;
+    case 4: return paged_decode_kernel<D, 4, I8, GRID>;
+    case 8: return paged_decode_kernel<D, 8, I8, GRID>;
     default: return nullptr;
   }
 }
 
-template <bool COMPACT>
+template <int GRID>
 decode_fn pick_dt(int D, int G, bool i8) {
-  if (D == 128) return i8 ? pick_g<128, true, COMPACT>(G) : pick_g<128, false, COMPACT>(G);
-  if (D == 64) return i8 ? pick_g<64, true, COMPACT>(G) : pick_g<64, false, COMPACT>(G);
+  if (D == 128) return i8 ? pick_g<128, true, GRID>(G) : pick_g<128, false, GRID>(G);
+  if (D == 64) return i8 ? pick_g<64, true, GRID>(G) : pick_g<64, false, GRID>(G);
   return nullptr;
 }
 
-decode_fn pick_kernel(int D, int G, bool i8, bool compact = false) {
-  return compact ? pick_dt<true>(D, G, i8) : pick_dt<false>(D, G, i8);
+decode_fn pick_kernel(int D, int G, bool i8, int grid) {
+  return grid == GRID_COMPACT ? pick_dt<GRID_COMPACT>(D, G, i8)
+         : grid == GRID_PLAN  ? pick_dt<GRID_PLAN>(D, G, i8)
+                              : pick_dt<GRID_PLAIN>(D, G, i8);
 }
 
 // Split-K workspace: m [B][Hq][P], l [B][Hq][P], o [B][Hq][P][D] (fp32); none
@@ -1790,12 +1969,10 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   if (st != PKV_OK) return st;
   if ((a->k_new_dev == nullptr) != (a->v_new_dev == nullptr))
     return pkv::fail(PKV_ERR_INVALID_ARG, "k_new and v_new must both be given or both be NULL");
-  if (a->k_new_dev && c.dtype != PKV_F16)
-    return pkv::fail(PKV_ERR_UNSUPPORTED, "the fused append writes fp16 pools only");
   if (a->k_new_dev && (!aligned16(a->k_new_dev) || !aligned16(a->v_new_dev)))
     return pkv::fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
   const int G = a->num_q_heads / c.num_kv_heads;
-  decode_fn fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8);
+  decode_fn fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, a->prefix_groups > 0 ? GRID_PLAN : GRID_PLAIN);
   if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", G);
   if (c.num_kv_heads > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
   if (a->ctx_lens_host) {
@@ -1871,7 +2048,9 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
       const int cap_blocks = int((cap + BT - 1) / BT);
       const int32_t* lens = a->ctx_lens_host;
       auto span = [&](int b) { return lens ? int((std::min<int64_t>(lens[b], cap) + BT - 1) / BT) : cap_blocks; };
-      pb = launch_part_blocks(c.num_kv_heads, a->num_seqs, span, resident_wgs(reinterpret_cast<const void*>(fn)),
+      pb = launch_part_blocks(c.num_kv_heads, a->num_seqs, span,
+                              resident_wgs(reinterpret_cast<const void*>(fn),
+                                           c.dtype == PKV_I8 ? two_per_cu_lds(reinterpret_cast<const void*>(fn)) : 0),
                               (cap_blocks + mp0 - 1) / mp0);
       gparts = std::min(mp0, (cap_blocks + pb - 1) / pb);
     } else if (a->ctx_lens_host && a->prefix_plan_host) {
@@ -1941,7 +2120,7 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   prm.max_context = a->max_context;
   prm.scale_log2 = a->scale * LOG2E;
   prm.num_seqs = a->num_seqs;
-  if (compact) fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, true);
+  if (compact) fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, GRID_COMPACT);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -1953,10 +2132,11 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   const int cy = int(std::min<int64_t>(pairs, 65535));
   const dim3 grid = compact ? dim3(c.num_kv_heads, cy, unsigned((pairs + cy - 1) / cy))
                             : dim3(c.num_kv_heads, a->num_seqs, pz + gparts);
+  const size_t dyn_lds = c.dtype == PKV_I8 ? two_per_cu_lds(reinterpret_cast<const void*>(fn)) : 0;
   if (ev[0] && ev[1])
-    hipExtLaunchKernelGGL(fn, grid, dim3(256), 0, s, ev[0], ev[1], 0, prm);
+    hipExtLaunchKernelGGL(fn, grid, dim3(256), dyn_lds, s, ev[0], ev[1], 0, prm);
   else
-    hipLaunchKernelGGL(fn, grid, dim3(256), 0, s, prm);
+    hipLaunchKernelGGL(fn, grid, dim3(256), dyn_lds, s, prm);
   st = hip_status(hipGetLastError(), "paged_decode launch");
   if (st != PKV_OK || (gparts <= 1 && !plan)) return st;
   MergeParams mg;

@@ -14,9 +14,11 @@ from workloads import replay_churn
 
 class LibRun:
     def __init__(self, w, device=None, layers=1, quantised=None, poison=False, fused_append=False):
-        """``quantised``: for an int8 workload, the oracle's quantised store
-        (``RefCache`` with K, V, scales), uploaded into the pool before each
-        decode; the pool has no int8 write path of its own yet.
+        """``quantised``: for an int8 workload written in bulk
+        (``i8_write="bulk"``), the oracle's block-quantised store (``RefCache``
+        with K, V, scales), uploaded into the pool before each decode;
+        workloads with ``i8_write="append"`` are quantised on write by the
+        library's own int8 append instead.
         ``fused_append``: an append step of one token per sequence followed by
         a decode of exactly those sequences writes the tokens inside the
         decode launch (k_new/v_new) instead of a separate append call."""
@@ -93,7 +95,8 @@ class LibRun:
                     all_slots.append(slots)
                     all_cow.append(cow)
                 slots, cow = np.concatenate(all_slots), np.concatenate(all_cow)
-                if self.fused_append and self.cache is not None and self.w.dtype == "f16" and decode:
+                if self.fused_append and self.cache is not None and decode and \
+                        (self.w.dtype == "f16" or self.w.i8_write == "append"):
                     self.cache.copy_blocks(cow)
                     self.pending = (list(names), slots, k, v)
                 else:

@@ -144,15 +144,16 @@ def c2_llama_b8(seed=2):
     return w
 
 
-def c3_mixed(seed=3, batch=16, churn_requests=200):
+def c3_mixed(seed=3, batch=16, churn_requests=200, dtype="f16"):
     """Continuous-batching mix: 16 sequences of U[128, 8192] tokens, pool
-    scrambled by 200 earlier requests of U[1, 8192] tokens."""
+    scrambled by 200 earlier requests of U[1, 8192] tokens. ``dtype="i8"``:
+    the same draws, stored block-quantised as int8."""
     rng = np.random.default_rng(seed)
     N = 16 * 513
     churn = Churn(lengths=rng.integers(1, 8193, churn_requests),
                   uniforms=rng.random(8 * churn_requests + 64))
     lens = rng.integers(128, 8193, batch).tolist()
-    w = Workload("c3_mixed", N, 32, 8, 128, "f16", np.arange(N, dtype=np.int32))
+    w = Workload("c3_mixed", N, 32, 8, 128, dtype, np.arange(N, dtype=np.int32))
     w.steps.append(("churn", churn))
     names = [f"s{i}" for i in range(batch)]
     for s in names:
@@ -290,6 +291,21 @@ def headline(seed=6, batch=16, ctx=8192, spare_blocks=0):
     order = rng.permutation(N).astype(np.int32)
     w = _decode_batch("headline_b16_ctx8k", rng, N, 32, 8, 128, [ctx] * batch, order)
     w.seed = seed
+    return w
+
+
+def uniform_decode(seed, batch, ctx, Hq=32, Hkv=8, D=128, dtype="f16", append=True, i8_write="bulk",
+                   lens=None):
+    """``batch`` sequences prefilled to ``ctx`` tokens each (or to ``lens``),
+    one appended token each unless ``append`` is False, then one decode step;
+    a pool of exactly the blocks needed, in seeded random order."""
+    rng = np.random.default_rng(seed)
+    lens = [ctx] * batch if lens is None else [int(n) for n in lens]
+    N = sum(-(-(n + 1) // 16) for n in lens) + 2
+    order = rng.permutation(N).astype(np.int32)
+    w = _decode_batch(f"uniform_{seed}", rng, N, Hq, Hkv, D, lens, order, dtype=dtype, append=append)
+    w.seed = seed
+    w.i8_write = i8_write
     return w
 
 
