@@ -326,13 +326,13 @@ def test_device_calls_validate_before_launch():
     assert status(lambda: pkv.pkv_upload(0, fake, 16, None)) == C.PKV_ERR_INVALID_ARG
     assert status(lambda: pkv.pkv_upload(fake, fake + 4, 16, None)) == C.PKV_ERR_INVALID_ARG
     pkv.pkv_upload(fake, fake, 0, None)  # no-op
-    # fused append: both rows or neither; fp16 pools only
+    # fused append: both rows or neither, 16-byte aligned (fp16 and int8 pools)
     assert status(lambda: pkv.pkv_paged_decode(args(k_new_dev=fake), None)) == C.PKV_ERR_INVALID_ARG
     assert status(lambda: pkv.pkv_paged_decode(args(k_new_dev=fake, v_new_dev=fake + 8), None)) == \
         C.PKV_ERR_INVALID_ARG
     i8dec = pkv.make_config(2, 16, 2, 64, "i8")
-    assert status(lambda: pkv.pkv_paged_decode(args(cfg=C.ctypes.pointer(i8dec), k_new_dev=fake, v_new_dev=fake),
-                                               None)) == C.PKV_ERR_UNSUPPORTED
+    assert status(lambda: pkv.pkv_paged_decode(args(cfg=C.ctypes.pointer(i8dec), k_new_dev=fake + 4,
+                                                    v_new_dev=fake), None)) == C.PKV_ERR_INVALID_ARG
     assert status(lambda: pkv.pkv_paged_decode(args(max_blocks=300, max_context=4800, workspace_bytes=10,
                                                     partition_tokens=64), None)) == C.PKV_ERR_INVALID_ARG
 
@@ -613,8 +613,9 @@ def test_kernels_use_no_scratch_memory():
         pytest.skip("library not built in this tree")
     rows = [l.rstrip("\n").split("\t") for l in open(B.RESOURCES) if not l.startswith("#")]
     names = [r[0] for r in rows]
-    # D in {64, 128} x G in {1, 2, 4, 8} x {f16, i8} x {plain, compact grid}
-    assert sum("paged_decode_kernel" in n for n in names) == 32
+    # D in {64, 128} x G in {1, 2, 4, 8} x {f16, i8} x {plain grid, compact grid, plain grid with a
+    # shared-prefix plan}
+    assert sum("paged_decode_kernel" in n for n in names) == 48
     assert sum("prefill_kernel" in n for n in names) == 16  # the same for the prefill
     for r in rows:
         assert r[3] == "0" and r[4] == "0" and r[5] == "0", r
