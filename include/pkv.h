@@ -418,6 +418,24 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * UNSUPPORTED: head_dim/group size not built. */
 int pkv_paged_decode(const pkv_decode_args* args, void* stream);
 
+/* pkv_paged_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments, kernels and results, but the split-K
+ * partials go to the library's own scratch, a file-scope device array of
+ * PKV_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held from the library's load
+ * until the process ends; workspace_dev and workspace_bytes are ignored. The
+ * call allocates no device memory (its first call on a device looks up the
+ * array's address there, once). INVALID_ARG, with a message naming the
+ * limit, when the decode needs more than that maximum
+ * (pkv_decode_workspace_bytes / pkv_prefix_decode_workspace_bytes give the
+ * need); every other check and status is pkv_paged_decode's. The scratch
+ * needs no initial contents and keeps the last call's partials: all calls on
+ * one GPU share it, so calls that may overlap on one GPU (different streams,
+ * threads or processes sharing the library) race and must be serialised by
+ * the caller, for instance by issuing them on one stream. */
+#define PKV_NOALLOC_SCRATCH_BYTES (16 << 20)
+int pkv_paged_decode_noalloc(const pkv_decode_args* args, void* stream);
+
 /* Workspace bytes pkv_paged_decode needs with a shared-prefix plan of
  * n_groups groups: the whole workspace, in place of
  * pkv_decode_workspace_bytes() (equal to it when n_groups == 0). Layout:

@@ -18,7 +18,7 @@ from ._capi import (  # noqa: F401  (re-exported C names)
     PKV_STEP_DECODE, PKV_STEP_PREFILL, pkv_seq_len, pkv_seq_block_table, pkv_block_refcount,
     pkv_num_free, pkv_free_list, pkv_build_block_tables, pkv_plan_ints, pkv_plan_shared_prefix,
     pkv_copy_blocks, pkv_append_kv, pkv_decode_workspace_bytes, pkv_prefix_decode_workspace_bytes, pkv_paged_decode,
-    pkv_paged_prefill, pkv_upload, pkv_probe_stream_read, pkv_strerror,
+    pkv_paged_decode_noalloc, pkv_paged_prefill, pkv_upload, pkv_probe_stream_read, pkv_strerror,
     pkv_last_error,
 )
 from .cache import PagedKVCache, paged_decode  # noqa: F401

@@ -33,6 +33,7 @@ PKV_I8 = 1
 BLOCK_TOKENS = 16
 PKV_MAX_SHARERS = 32
 PKV_PREFIX_GROUP_INTS = 34
+PKV_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _c_i32 = ctypes.c_int32
 _c_i64 = ctypes.c_int64
@@ -128,6 +129,7 @@ _SIGS = {
     "pkv_prefix_decode_workspace_bytes": (_c_i64, [ctypes.POINTER(pkv_config), _c_i32, _c_i32, _c_i32, _c_i32,
                                                    _c_i32, _c_i32]),
     "pkv_paged_decode": (ctypes.c_int, [ctypes.POINTER(pkv_decode_args), _vp]),
+    "pkv_paged_decode_noalloc": (ctypes.c_int, [ctypes.POINTER(pkv_decode_args), _vp]),
     "pkv_paged_prefill": (ctypes.c_int, [ctypes.POINTER(pkv_prefill_args), _vp]),
     "pkv_upload": (ctypes.c_int, [_vp, _vp, _c_i64, _vp]),
     "pkv_probe_stream_read": (ctypes.c_int, [_vp, _c_i64, _vp, _vp]),
@@ -454,6 +456,10 @@ def pkv_prefix_decode_workspace_bytes(cfg, num_seqs, num_q_heads, max_context, m
 
 def pkv_paged_decode(args, stream):
     _check(load().pkv_paged_decode(ctypes.byref(args), stream))
+
+
+def pkv_paged_decode_noalloc(args, stream):
+    _check(load().pkv_paged_decode_noalloc(ctypes.byref(args), stream))
 
 
 def pkv_paged_prefill(args, stream):

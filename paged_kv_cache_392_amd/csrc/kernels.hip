@@ -1948,7 +1948,39 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
   return ws_layout(*cfg, num_seqs, num_q_heads, max_context, 1, partition_tokens, 0).bytes;
 }
 
-int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch of pkv_paged_decode_noalloc: the split-K partials of a decode, in
+// a file-scope device array (one copy per GPU the library runs on, held
+// until the process ends). Its address on a device comes from
+// hipGetSymbolAddress, taken once per device with that device current; host
+// code never passes the array's name itself to a kernel or a copy.
+constexpr int64_t NOALLOC_SCRATCH_BYTES = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+int scratch_on_current_device(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> known;
+  int dev = 0;
+  int st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != PKV_OK) return st;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = known.find(dev);
+  if (it != known.end()) {
+    *out = it->second;
+    return PKV_OK;
+  }
+  void* ptr = nullptr;
+  st = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+  if (st != PKV_OK) return st;
+  known[dev] = ptr;
+  *out = ptr;
+  return PKV_OK;
+}
+
+int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int64_t ws_bytes, bool noalloc) {
   if (!a) return pkv::fail(PKV_ERR_INVALID_ARG, "args is NULL");
   int st = pkv::validate_config(a->cfg);
   if (st != PKV_OK) return st;
@@ -2011,9 +2043,14 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
       ws_layout(c, a->num_seqs, a->num_q_heads, a->max_context, a->max_blocks, a->partition_tokens, a->prefix_groups);
   const int mp0 = wl.grid_parts, mp = wl.max_parts;
   const int64_t need = wl.bytes;
-  if (need > 0 && (!a->workspace_dev || a->workspace_bytes < need))
+  if (noalloc && need > ws_bytes)
+    return pkv::fail(PKV_ERR_INVALID_ARG,
+                     "pkv_paged_decode_noalloc: this decode needs %lld bytes of split-K scratch, above its "
+                     "maximum of %lld (use pkv_paged_decode with a workspace)",
+                     (long long)need, (long long)ws_bytes);
+  if (need > 0 && (!ws_dev || ws_bytes < need))
     return pkv::fail(PKV_ERR_INVALID_ARG, "workspace too small: need %lld bytes", (long long)need);
-  if (need > 0 && !aligned16(a->workspace_dev))
+  if (need > 0 && !aligned16(ws_dev))
     return pkv::fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   // prefix partitions of this launch: the workspace's count, or fewer when
   // the plan's host copy shows shorter shared runs
@@ -2102,7 +2139,7 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   prm.tables = a->block_tables_dev;
   prm.ctx_lens = a->ctx_lens_dev;
   const int64_t rows = int64_t(a->num_seqs) * a->num_q_heads * mp;
-  float* ws = static_cast<float*>(a->workspace_dev);
+  float* ws = static_cast<float*>(ws_dev);
   const bool parts = need > 0;
   prm.part_m = parts ? ws : nullptr;
   prm.part_l = parts ? ws + rows : nullptr;
@@ -2161,6 +2198,23 @@ int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
   else
     hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(pp + gparts)), 0, s, mg);
   return hip_status(hipGetLastError(), "lse_reduce launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_decode(const pkv_decode_args* a, void* stream) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  return paged_decode_impl(a, stream, a->workspace_dev, a->workspace_bytes, false);
+}
+
+int pkv_paged_decode_noalloc(const pkv_decode_args* a, void* stream) {
+  if (!a) return pkv::fail(PKV_ERR_INVALID_ARG, "args is NULL");
+  void* ptr = nullptr;
+  const int st = scratch_on_current_device(&ptr);
+  if (st != PKV_OK) return st;
+  return paged_decode_impl(a, stream, ptr, NOALLOC_SCRATCH_BYTES, true);
 }
 
 int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
