@@ -70,7 +70,9 @@ def parse():
                     help="shape workload: comma-separated context lengths, one per sequence")
     ap.add_argument("--q-heads", type=int, default=32, help="shape workload")
     ap.add_argument("--kv-heads", type=int, default=8, help="shape workload")
-    ap.add_argument("--dtype", choices=["f16", "i8"], default="f16", help="shape workload")
+    ap.add_argument("--dtype", choices=["f16", "i8"], default="f16",
+                    help="headline: the element type of the 32 layer pools (i8: the same step on int8 K/V, "
+                         "each new token quantised on write inside the decode launch); shape workload")
     ap.add_argument("--seed", type=int, default=None,
                     help="shape workload: lengths and block order (default 7); c3: block order (default: "
                          "the config's seed)")
@@ -179,19 +181,28 @@ def main():
     N = w.num_blocks
     max_blocks = -(-(CTX + total_steps + 1) // 16)
 
-    cache = pkv.PagedKVCache(L, N, HKV, D, "f16", w.free_order, dev)
+    i8 = args.dtype == "i8"
+    cache = pkv.PagedKVCache(L, N, HKV, D, args.dtype, w.free_order, dev)
     lib = C.load()
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    print(f"[bench] pool {cache.nbytes / 2**30:.2f} GiB, {L} layers, {N} blocks", file=sys.stderr, flush=True)
+    print(f"[bench] pool {cache.nbytes / 2**30:.2f} GiB, {L} layers, {N} blocks, {args.dtype}", file=sys.stderr,
+          flush=True)
 
     # --- build the cache: layer 0 from the seeded workload through the
-    # library's append, layers 1.. with seeded device noise (timing only)
+    # library's append (int8: quantised on write), layers 1.. with seeded
+    # device noise (timing only; int8: random codes and scales)
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed)
     for layer in range(1, L):
-        cache.region(0, layer).normal_(generator=gen)
-        cache.region(1, layer).normal_(generator=gen)
+        for which in (0, 1):
+            r = cache.region(which, layer)
+            if i8:
+                r.copy_(torch.randint(-127, 128, r.shape, dtype=torch.int8, device=dev, generator=gen))
+            else:
+                r.normal_(generator=gen)
+    if i8:
+        cache.scales()[1:].uniform_(0.01, 0.03, generator=gen)
     seqs, first_k, first_v, first_q = [], None, None, None
     for step in w.steps:
         if step[0] == "create":
@@ -362,19 +373,26 @@ def main():
                                   for l in check_layers)
 
     split_ms = np.array([g[0].elapsed_time(g[1]) for g in ev])
-    merge_ms = np.array([g[2].elapsed_time(g[3]) for g in ev])
+    # a launch that needed no merge leaves its merge events at their set-up
+    # record, from before the timed loop
+    merged = all(t0.elapsed_time(g[2]) > 0 for g in ev)
+    merge_ms = np.array([g[2].elapsed_time(g[3]) for g in ev]) if merged else None
     timed_lens = step_lens[W + 1:]
+    append_us = time_append(torch, C, lib, cache, dev, sp, K, knew, vnew, seq_arr, max_blocks)
 
     # algorithmic bytes
-    kv_tok = 2 * HKV * D * 2  # K and V of one token, one layer, fp16
+    E = 1 if i8 else 2
+    kv_tok = 2 * HKV * D * E  # K and V of one token, one layer
     def decode_bytes(lens, with_out=True):
         """K/V rows read + q + table entries + lengths (+ out) of one decode."""
         lens = np.asarray(lens, np.int64)
         nb = len(lens)
         nblk = (lens + 15) // 16
         b = int(lens.sum()) * kv_tok + nb * HQ * D * 2 + int(nblk.sum()) * 4 + nb * 4
+        if i8:
+            b += int(nblk.sum()) * HKV * 4  # the tiles' (K, V) fp16 scales
         return b + (nb * HQ * D * 2 if with_out else 0)
-    append_bytes = 2 * (B * HKV * D * 2) * 2  # the new k and v rows, read and written
+    append_bytes = 2 * (B * HKV * D * 2) + 2 * (B * HKV * D * E)  # the new k and v rows read (fp16), written
     upload_bytes = B * max_blocks * 4 + B * 4  # tables and lengths
     step_bytes = [L * (decode_bytes(l) + append_bytes) + upload_bytes for l in timed_lens]
     split_bytes = np.array([decode_bytes(l, with_out=False) for l in timed_lens])
@@ -398,9 +416,9 @@ def main():
         probe = nbytes * reps / (p0.elapsed_time(p1) * 1e-3) / 1e9
 
     src_hash = kernel_source_hash()
-    traffic = measured_traffic(src_hash, float(np.mean(split_bytes)))
+    traffic = None if i8 else measured_traffic(src_hash, float(np.mean(split_bytes)))
     result = {
-        "metric": "paged decode HBM GB/s (% of peak) + decode tok/s, 32q/8kv d128 fp16",
+        "metric": "paged decode HBM GB/s (% of peak) + decode tok/s, 32q/8kv d128 " + ("int8" if i8 else "fp16"),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -410,11 +428,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": {
             "workload": "decode step, batch 16, context 8192 (+1 token per step), 32 q heads / 8 KV heads, "
-                        "head_dim 128, fp16 K/V in 16-token blocks, 32 layer pools",
+                        "head_dim 128, " + ("int8 K/V with one fp16 scale per (block, KV head), the new token "
+                                            "quantised on write" if i8 else "fp16 K/V") +
+                        " in 16-token blocks, 32 layer pools",
             "batch": B, "context": CTX, "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "layers": L,
             "block_tokens": 16, "pool_blocks_per_layer": N,
             "partition_tokens": args.partition_tokens or "auto",
@@ -424,7 +444,9 @@ def main():
         "split_kernel_us": round(float(np.mean(split_ms)) * 1e3, 2),
         "split_kernel_us_p10_p90": [round(float(np.percentile(split_ms, 10)) * 1e3, 2),
                                     round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
-        "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2),
+        "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2) if merged else None,
+        "decode_a5_a6": decode_metric(split_ms, merge_ms, split_bytes),
+        "append_kernel_us": append_us,
         "timed_launch_samples": int(len(split_ms)),
         "execution": ("per step: host slot reservation and table packing, table upload, layer 0 "
                       "launched directly (timing events), " +
@@ -436,7 +458,7 @@ def main():
         "split_kernel_pct_of_probe": None if not probe else round(100.0 * split_gbps / probe, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged_decode_kernel<128,4,f16> (split-K decode)",
+            "kernel": f"paged_decode_kernel<128,4,{args.dtype}> (split-K decode)",
             "achieved": round(split_gbps, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
@@ -447,10 +469,75 @@ def main():
         "cpu_baseline": None,
     }
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not i8:
         result["cpu_baseline"] = cpu_baseline(w, first_out, first_tables, first_lens, args.cpu_seconds,
                                               decode_bytes)
     print(json.dumps(result), flush=True)
+
+
+def decode_metric(split_ms, merge_ms, bytes_per_launch):
+    """The decode metric over the split-K kernel and the merge together (the
+    two launches of one paged decode): per-sample sums of the two kernels'
+    HIP-event times, median and p10/p90 in µs, and the algorithmic bytes over
+    the median as GB/s and as a fraction of the 8 TB/s peak. Samples whose
+    launch needed no merge count the split kernel alone (merge_ms None)."""
+    both = np.asarray(split_ms) + (0.0 if merge_ms is None else np.asarray(merge_ms))
+    med = float(np.median(both))
+    gbps = float(np.mean(bytes_per_launch)) / (med * 1e-3) / 1e9
+    return {"median_us": round(med * 1e3, 2), "p10_us": round(float(np.percentile(both, 10)) * 1e3, 2),
+            "p90_us": round(float(np.percentile(both, 90)) * 1e3, 2), "GBps": round(gbps, 1),
+            "frac": round(gbps / PEAK_HBM_GBPS, 4), "samples": int(len(both))}
+
+
+def time_append(torch, C, lib, cache, dev, sp, K, knew, vnew, seq_arr, max_blocks):
+    """The append step (a4) on its own: the batch's new token (k and v of
+    every KV head) written into every layer by one pkv_append_kv launch per
+    layer, at slots reserved past the timed steps' tokens. The L launches are
+    replayed from one HIP graph (as a two-call decode step would issue them),
+    K replays between two events: µs per launch is the replay time over K x L.
+    Also the median of per-launch event pairs around single eager launches
+    (host-bound: it includes the launch gap). (The decode step itself
+    appends inside the decode launch; this is the separate kernel's cost.)"""
+    nb = len(seq_arr)
+    L = cache.num_layers
+    slots = np.empty(nb, np.int32)
+    for b in range(nb):
+        s, _ = cache.reserve([int(seq_arr[b])], [1])
+        slots[b] = s[0]
+    sd = torch.from_numpy(slots).to(dev)
+
+    def launch(layer, stream_handle):
+        C._check(lib.pkv_append_kv(ctypes.byref(cache.cfg), cache.pool.data_ptr(), layer,
+                                   knew[0, layer].data_ptr(), vnew[0, layer].data_ptr(), sd.data_ptr(), nb,
+                                   stream_handle))
+
+    for layer in range(L):
+        launch(layer, sp)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream().cuda_stream
+        for layer in range(L):
+            launch(layer, cs)
+    torch.cuda.synchronize()
+    graph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    per_launch = e0.elapsed_time(e1) * 1e3 / (K * L)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        evs[i][0].record()
+        launch(0, sp)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    return {"graph_us_per_launch": round(per_launch, 2), "eager_event_median_us": round(float(np.median(t)), 2),
+            "tokens_per_launch": nb, "launches_per_replay": L}
 
 
 def decode_only_bench(args, torch, pkv, C, lens, hq, hkv, dtype, free_order, seed, metric, workload):
@@ -581,6 +668,7 @@ def decode_only_bench(args, torch, pkv, C, lens, hq, hkv, dtype, free_order, see
         "split_kernel_us_p10_p90": [round(float(np.percentile(split_ms, 10)) * 1e3, 2),
                                     round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
         "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2) if merged else None,
+        "decode_a5_a6": decode_metric(split_ms, merge_ms if merged else None, [kernel_bytes]),
         "graph_matches_eager_bitwise": same,
         "roofline": {"bound": "hbm", "kernel": f"paged_decode_kernel<128,{G},{dtype}> (split-K decode)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -748,12 +836,16 @@ def prefix_decode_bench(args, torch, pkv, C, workloads):
             t1.record()
             torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / K
-        split = float(np.mean([g[0].elapsed_time(g[1]) for g in ev])) * 1e3
-        merge = float(np.mean([g[2].elapsed_time(g[3]) for g in ev])) * 1e3
-        return ms, split, merge, out
+        split_ms = np.array([g[0].elapsed_time(g[1]) for g in ev])
+        merge_ms = np.array([g[2].elapsed_time(g[3]) for g in ev])
+        merged = all(t0.elapsed_time(g[2]) > 0 for g in ev)
+        return ms, split_ms, merge_ms if merged else None, out
 
-    ms0, split0, merge0, out0 = run(False)
-    ms1, split1, merge1, out1 = run(True)
+    ms0, split0_ms, merge0_ms, out0 = run(False)
+    ms1, split1_ms, merge1_ms, out1 = run(True)
+    split0, split1 = float(np.mean(split0_ms)) * 1e3, float(np.mean(split1_ms)) * 1e3
+    merge0 = None if merge0_ms is None else float(np.mean(merge0_ms)) * 1e3
+    merge1 = None if merge1_ms is None else float(np.mean(merge1_ms)) * 1e3
     diff = float((out0.float() - out1.float()).abs().max())
     kv_tok = 2 * HKV * D * 2
     groups = plan.groups()
@@ -772,9 +864,11 @@ def prefix_decode_bench(args, torch, pkv, C, workloads):
                    "partition_tokens": args.partition_tokens or "auto", "plan_groups": plan.n_groups,
                    "shared_blocks": [nb for nb, _ in groups]},
         "with_plan": {"ms_per_step": round(ms1, 4), "decode_kernel_us": round(split1, 2),
-                      "merge_kernel_us": round(merge1, 2)},
+                      "merge_kernel_us": None if merge1 is None else round(merge1, 2),
+                      "decode_a5_a6_unique_bytes": decode_metric(split1_ms, merge1_ms, [unique_bytes])},
         "without_plan": {"ms_per_step": round(ms0, 4), "decode_kernel_us": round(split0, 2),
-                         "merge_kernel_us": round(merge0, 2), "tok_s": round(nseq / (ms0 * 1e-3), 1)},
+                         "merge_kernel_us": None if merge0 is None else round(merge0, 2),
+                         "tok_s": round(nseq / (ms0 * 1e-3), 1)},
         "speedup": round(ms0 / ms1, 3),
         "max_abs_diff_plan_vs_no_plan": diff,
         "logical_kv_bytes": logical * kv_tok, "unique_kv_bytes": (logical - shared) * kv_tok,

@@ -466,7 +466,7 @@ typedef struct pkv_prefill_args {
   const int32_t* ctx_lens_dev;    /* int32 [B]: tokens cached, the chunk's own
                                      included (append the chunk's K/V first)      */
   const int32_t* ctx_lens_host;   /* optional host copy, validated if non-NULL    */
-  int32_t max_context;            /* >= every ctx_len; at most 16384              */
+  int32_t max_context;            /* >= every ctx_len                             */
   void* out_dev;                  /* fp16 [T][Hq][D]                              */
   float scale;                    /* softmax scale, normally 1/sqrt(D)            */
 } pkv_prefill_args;
@@ -482,10 +482,12 @@ typedef struct pkv_prefill_args {
  * (pkv_append_kv). fp16 or int8 pools (int8 tiles dequantised, code x
  * block scale rounded to fp16, as they are staged); head_dim 64 or 128. No
  * workspace.
+ * Any context length: a work-group keeps its block ids in a ring of 1024
+ * in LDS, refilled as it walks longer contexts.
  * INVALID_ARG: null pointers, q_start not starting at 0 or decreasing,
  * misalignment, a chunk longer than its context or a context out of range
- * (host copies). UNSUPPORTED: group size or head_dim not built, a context
- * above 16384 tokens. Sequences with qlen_b = 0 are skipped. */
+ * (host copies). UNSUPPORTED: group size or head_dim not built. Sequences
+ * with qlen_b = 0 are skipped. */
 int pkv_paged_prefill(const pkv_prefill_args* args, void* stream);
 
 /* Upload host metadata for the next step (block tables, lengths: the

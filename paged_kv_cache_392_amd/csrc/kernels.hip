@@ -465,8 +465,11 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 // every limit must be at least full_tokens, below which no row is masked),
 // and V rows of tokens at or past nvalid (slots never written) are staged
 // as zeros, so a masked weight of 0 never meets a stale NaN.
-// Tiles jb .. jb + nt - 1 of `trow` (nt <= MAXT, their block ids staged in
-// LDS), taken two at a time (a step of 32 tokens). STREAM: tiles are read
+// Tiles jb .. jb + nt - 1 of `trow`, taken two at a time (a step of 32
+// tokens). Their block ids sit in a ring of MAXT entries in LDS: the first
+// MAXT are staged up front, and when nt exceeds MAXT the ring is refilled
+// 256 ids at a time at a step barrier, each refill writing slots whose ids
+// have already been read. STREAM: tiles are read
 // once (non-temporal loads); otherwise other work-groups re-read them, and
 // ordinary loads keep them in L2. emit(r, o, m, l)
 // receives row r's unnormalised output, lane (n, j) holding dims
@@ -510,19 +513,30 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   __shared__ __align__(16) char vst[2][2][BT * VROW];
   __shared__ int blk_ids[MAXT];
   __shared__ uint32_t tile_sc[I8 ? MAXT : 1];  // int8: each tile's (K, V) fp16 scales
+  constexpr int REFILL = 256;  // ids per refill: one per thread
+  static_assert(MAXT > REFILL || MAXT <= 64, "a refilled ring must hold more than one refill");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lj = lane >> 4;
-  if constexpr (I8) {
-    for (int i = tid; i < nt; i += 256) {
-      const int blk = trow[jb + i];
-      blk_ids[i] = blk;
-      tile_sc[i] = unsigned(blk) < unsigned(num_blocks) ? scales[int64_t(blk) * Hkv + g] : 0u;
+  auto stage_id = [&](int i) {  // tile i's id (and int8 scales) into its ring slot
+    const int blk = trow[jb + i];
+    blk_ids[i % MAXT] = blk;
+    if constexpr (I8) tile_sc[i % MAXT] = unsigned(blk) < unsigned(num_blocks) ? scales[int64_t(blk) * Hkv + g] : 0u;
+  };
+  for (int i = tid; i < min(nt, MAXT); i += 256) stage_id(i);
+  // After the loads of step it + 1 + PFS are issued, every tile below
+  // T0 = 2 (it + 2 + PFS) has been read; when T0 is a multiple of REFILL, the
+  // slots of tiles T0 - REFILL .. T0 - 1 take tiles MAXT further on, first
+  // read (MAXT - REFILL) / 2 steps later, after the barrier that ends this
+  // step. Uniform over the work-group; never taken when nt <= MAXT.
+  auto refill = [&](int it) {
+    const int T0 = 2 * (it + 2 + PFS);
+    if (T0 % REFILL == 0 && T0 - REFILL + MAXT < nt) {
+      const int t = T0 - REFILL + MAXT + tid;
+      if (t < nt) stage_id(t);
     }
-  } else {
-    for (int i = tid; i < nt; i += 256) blk_ids[i] = trow[jb + i];
-  }
+  };
   const int nsteps = (nt + 1) / 2;
 
   // q^T as the B operand of the score MFMA, per row block of this wave
@@ -563,7 +577,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   auto gload = [&](int step, uint4 (&r)[2][NLD]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const int blk = blk_ids[min(2 * step + sub, nt - 1)];
+      const int blk = blk_ids[min(2 * step + sub, nt - 1) % MAXT];
       const int safe = unsigned(blk) < unsigned(num_blocks) ? blk : 0;
       const int64_t base = (int64_t(safe) * Hkv + g) * TILE;
 #pragma unroll
@@ -588,7 +602,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
           piece(q, lrow, lpc);
           const bool live = q < LOADERS || !MASK || (jb + 2 * step + sub) * BT + lrow < nvalid;
           char* dst = q < LOADERS ? kst[st][sub] + lrow * KROW : vst[st][sub] + lrow * VROW;
-          const uint32_t sc = tile_sc[min(2 * step + sub, nt - 1)];
+          const uint32_t sc = tile_sc[min(2 * step + sub, nt - 1) % MAXT];
           const uint32_t s1 = q < LOADERS ? (sc & 0xffffu) : (sc >> 16);  // K or V scale
           uint4 a, b;
           dequant16(r[sub][j], s1 | (s1 << 16), a, b);
@@ -732,6 +746,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
         if (it < to) step_rows(st, it, masked);
         lstore(st ^ 1, ring[(u + 1) % PFS], it + 1);
         gload(it + 1 + PFS, ring[(u + 1) % PFS]);
+        refill(it);
         __syncthreads();
       }
     }
@@ -800,8 +815,8 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
 // ---------------------------------------------------------------------------
 // paged prefill
 
-// Context a prefill work-group walks: at most 1024 tiles (16384 tokens), its
-// block ids staged in LDS.
+// Block ids a prefill work-group keeps in LDS at once (a ring: longer
+// contexts are refilled as the walk proceeds).
 constexpr int PREFILL_MAX_TILES = 1024;
 // Steps (pairs of tiles) a prefill work-group keeps in flight.
 constexpr int PREFILL_PFS = 2;
@@ -841,7 +856,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
   if (ql <= 0 || i0 >= ql || ql > n) return;
   const int cnt = min(QT, ql - i0), R = cnt * G;
   const int pos0 = n - ql + i0;  // logical position of the tile's first token
-  const int nt = min((pos0 + cnt - 1) / BT + 1, PREFILL_MAX_TILES);
+  const int nt = (pos0 + cnt - 1) / BT + 1;
   const int lj = (threadIdx.x & 63) >> 4;
   auto qrow = [&](int r) -> const _Float16* {
     return r < R ? prm.q + (int64_t(t0 + i0 + r / G) * Hq + g * G + r % G) * D : nullptr;
@@ -2243,8 +2258,6 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
                      c.num_kv_heads);
   if (a->max_blocks < 1 || a->max_context < 1)
     return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks and max_context must be >= 1");
-  if (std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context) > int64_t(PREFILL_MAX_TILES) * BT)
-    return pkv::fail(PKV_ERR_UNSUPPORTED, "prefill context above %d tokens", PREFILL_MAX_TILES * BT);
   const int G = a->num_q_heads / c.num_kv_heads;
   if (c.num_kv_heads > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
   if (a->ctx_lens_host) {

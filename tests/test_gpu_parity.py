@@ -790,6 +790,23 @@ def test_prefill_int8_matches_oracle(seed, cached, chunk, Hq, Hkv, D):
     lib.close()
 
 
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+def test_prefill_past_the_block_id_ring(dtype):
+    """Chunks after 33000 and 17000 cached tokens: the work-groups walk more
+    tiles than their 1024-entry ring of block ids holds, so the ring is
+    refilled as they go (beside a sequence that needs no refill)."""
+    if dtype == "f16":
+        w = workloads.prefill_chunks(69, [33000, 17000, 1100], [300, 129, 900], 8, 2, 128)
+    else:
+        w = workloads.prefill_chunks(70, [33000, 17000], [300, 129], 8, 2, 128, dtype="i8")
+    lib, o = run_pair(w)
+    check_host_records(lib, o)
+    err = prefill_err(lib, o)
+    announce(f"long-context prefill {dtype} max abs err {err:.3g}")
+    assert err <= (F16_TOL if dtype == "f16" else I8_TOL)
+    lib.close()
+
+
 def test_prefill_long_prompts_and_physical_order():
     """Two 2048-token prompts (32 q / 8 KV heads, d128) against the oracle,
     and the same result bit for bit under another physical block order."""
