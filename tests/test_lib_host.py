@@ -545,7 +545,6 @@ def test_prefill_validated_before_launch():
     assert call([0, 5, 8], layer=1) == C.PKV_ERR_INVALID_ARG
     assert call([0, 5, 8], Hq=6) == C.PKV_ERR_UNSUPPORTED  # 3 q heads per KV head
     assert call([0, 5, 8], Hq=5) == C.PKV_ERR_INVALID_ARG
-    assert call([0, 5, 8], max_context=20000, max_blocks=2000, host_lens=False) == C.PKV_ERR_UNSUPPORTED
     lens[0] = 0
     assert call([0, 0, 8]) == C.PKV_ERR_INVALID_ARG  # a context of 0 tokens
     lens[0] = 40
