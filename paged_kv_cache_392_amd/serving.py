@@ -29,8 +29,8 @@ from .cache import _dev_i32
 
 class ServingLoop:
     def __init__(self, cache, num_q_heads, max_running, prefill_budget, model, layer=0):
-        if cache.dtype != "f16":
-            raise ValueError("the serving loop writes fp16 pools")
+        """``cache`` may hold fp16 or int8 K/V: on int8 pools every token is
+        quantised as it is written (``pkv_append_kv``)."""
         self.cache = cache
         self.Hq = num_q_heads
         self.model = model
@@ -58,7 +58,8 @@ class ServingLoop:
     def step(self):
         """Plan and run one step. Returns ``(plan, outputs, finished)``:
         ``outputs[i]`` is the fp16 ``[count, Hq, D]`` attention output of
-        plan item i."""
+        plan item i; ``plan["attn"][kind]`` records the ``(seqs, tables,
+        context_lens)`` each attention call of the step read (host copies)."""
         plan = C.pkv_sched_step(self.sched, self.plan)
         items = plan["items"]
         dev = self.cache.device
@@ -72,6 +73,7 @@ class ServingLoop:
             qs.append(q)
             slots += islots
         outputs = [None] * len(items)
+        plan["attn"] = {}
         if items:
             kd = torch.from_numpy(np.ascontiguousarray(np.concatenate(ks))).to(dev)
             vd = torch.from_numpy(np.ascontiguousarray(np.concatenate(vs))).to(dev)
@@ -85,6 +87,7 @@ class ServingLoop:
                 tables, _ = C.pkv_build_block_tables(self.cache.handle, seqs,
                                                      max(len(C.pkv_seq_block_table(self.cache.handle, s))
                                                          for s in seqs))
+                plan["attn"][kind] = (seqs, tables.copy(), ctx.copy())
                 td = torch.from_numpy(tables).to(dev)
                 ld = torch.from_numpy(ctx).to(dev)
                 qd = torch.from_numpy(np.ascontiguousarray(np.concatenate([qs[i] for i in idx]))).to(dev)
