@@ -373,12 +373,15 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * given, else every sequence at max_context), and among those the finest
  * cut; 16 to 256 blocks per partition, never finer than the workspace's
  * cut. The partition size changes the result only by rounding. With
- * ctx_lens_host, no shared-prefix plan and at most 1024 sequences, a launch
- * whose grid of (sequence, partition) slots at max_context would hold slots
- * past some sequence's last partition launches only the pairs that hold
- * blocks (same partitions, bit for bit the same output); ctx_lens_host must
- * then equal the device lengths (a mismatch gives wrong output for the
- * sequences it misstates, never an access out of bounds).
+ * ctx_lens_host, automatic partitions, no shared-prefix plan and at most 1024
+ * sequences, a ragged batch (one whose grid of (sequence, partition) slots
+ * at max_context would hold slots past some sequence's last partition) is
+ * split stream-K: all sequences' blocks laid end to end are cut into equal
+ * runs, about one round of resident work-groups, a run possibly ending one
+ * sequence and starting the next, and each sequence's pieces are merged in
+ * order. ctx_lens_host must then equal the device lengths (a mismatch gives
+ * wrong output for the sequences it misstates, never an access out of
+ * bounds).
  * Accumulation is fp32 and
  * the output is rounded to fp16 (nearest even). The result depends only on
  * logical token order, not on physical block ids, and is bitwise

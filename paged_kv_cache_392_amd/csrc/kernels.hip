@@ -307,9 +307,9 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int max_contex
   return min(ctx, min(max_blocks * BT, max_context));
 }
 
-// Sequences a compact split grid can enumerate (each work-group scans the
+// Sequences a stream-K split can lay end to end (each work-group scans the
 // partition counts of all of them).
-constexpr int COMPACT_MAX_SEQS = 1024;
+constexpr int STREAM_MAX_SEQS = 1024;
 
 // Exclusive prefix sum of v over the 256 threads of a work-group (thread
 // order), and the work-group's total. part: WAVES ints of LDS. Every thread
@@ -334,45 +334,6 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* part, int& total) {
   __syncthreads();  // part is rewritten by the next call
   total = tot;
   return off + x - v;
-}
-
-// Compact split grid: the (sequence, partition) pair of work-group k, from
-// the partition counts of every sequence (the same rule as the plain grid's
-// early exit; a sequence with no tokens keeps one work-group, which writes
-// its zero output). b = -1 when k is past the last pair. lds: WAVES + 2 ints
-// of the caller's LDS, free until the barrier that ends this call.
-__device__ __forceinline__ void compact_pair(const DecodeParams& prm, int k, int* lds, int& b, int& p) {
-  int* part = lds;
-  int* pick = lds + WAVES;
-  const int tid = threadIdx.x;
-  constexpr int PER = COMPACT_MAX_SEQS / 256;
-  int n[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {  // all lengths in flight together
-    const int t = tid + 256 * i;
-    n[i] = 0;
-    if (t < prm.num_seqs) {
-      const int ctx = clamp_ctx(prm.ctx_lens[t], prm.max_blocks, prm.max_context);
-      n[i] = ctx > 0 ? ((ctx + BT - 1) / BT + prm.part_blocks - 1) / prm.part_blocks : 1;
-    }
-  }
-  if (tid == 0) pick[0] = -1;  // ordered before the writes below by the scan's barriers
-  int carry = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (256 * i >= prm.num_seqs) break;  // uniform
-    int tot;
-    const int ex = carry + wg_exclusive_scan(n[i], part, tot);
-    if (k >= ex && k < ex + n[i]) {  // exactly one thread, if any
-      pick[0] = tid + 256 * i;
-      pick[1] = k - ex;
-    }
-    carry += tot;
-  }
-  __syncthreads();
-  b = __builtin_amdgcn_readfirstlane(pick[0]);
-  p = __builtin_amdgcn_readfirstlane(pick[1]);
-  __syncthreads();  // every wave has its pair before lds is reused
 }
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
@@ -1116,71 +1077,41 @@ __device__ __forceinline__ void wave_stream_i8(const DecodeParams& prm, int g, i
   }
 }
 
-// Two work-groups per CU are asked of the register allocator where they
-// fit without spills (G <= 4; fp16 at D = 64): the shared-prefix role would
-// otherwise push the fp16 kernels past 256 registers a lane. The other
-// G = 8 kernels keep the full register file.
-//
-// One work-group (4 wave64s) per (KV head g, sequence b, partition p), in
-// that grid order (x, y, z). Work-groups go to the eight XCDs round-robin by
-// linear id, so the partition index, the dimension along which work runs out
-// first (short sequences, or a shared prefix attended elsewhere), varies
-// slowest: the busy work-groups of any one partition index are spread over
-// all XCDs instead of piling onto those whose id matches a low index.
-//
-// Scores on the matrix cores: per tile, S[r][n] = sum_k Q[r][k] K[n][k] with
-// v_mfma_f32_16x16x32_f16 over D/32 chunks. A-row r holds query head r % G of
-// the group (rows repeat when G < 16), B-column n is token n of the tile.
-// Lane (n = lane % 16, j = lane / 16) feeds token n's K dims of k-slot group
-// j and receives rows 4j..4j+3 of column n: the scores of heads
-// (4j + e) % G, e = 0..3, for its token, already fully reduced.
-//
-// After its last tile the work-group writes one (m, l, o[D]) partial per
-// query head for the merge kernel, or the final fp16 row when the sequence
-// has a single partition.
-// GRID_COMPACT: the split grid holds the (sequence, partition) pairs that
-// have blocks and nothing else (no plan). The plain grid holds max-context
-// partitions for every sequence, and a work-group past its sequence's last
-// partition exits once its length has arrived; under a full HBM stream that
-// holds its slot for microseconds, and real work-groups queue behind such
-// exits. The compact grid is chosen by the host from its copy of the lengths
-// and is a separate instantiation, so the plain grid's code is untouched by
-// the scan (sharing one body cost the shared-prefix launch 8%).
-// GRID_PLAN: the plain grid led by the shared-prefix planes; the multi-row
-// attention of that role needs more registers than the split role, so
-// launches without a plan use GRID_PLAIN, which leaves it out.
-enum { GRID_PLAIN = 0, GRID_COMPACT = 1, GRID_PLAN = 2 };
-
-template <bool I8, int D, int G>
-constexpr int decode_wgs_per_cu() {
-  return (I8 || G <= 4 || D == 64) ? 2 : 1;
+// The early loads of a segment starting at logical block jb of sequence b:
+// this wave's block ids (lane it: block jb + wave + 4 it; the table row is
+// max_blocks wide and padded, ids past the context are masked later) and q
+// of the lane's head kn % G as the score MFMA operand (group kj's dims).
+template <int D, int G, bool I8>
+__device__ __forceinline__ void segment_loads(const DecodeParams& prm, int g, int b, int jb, int& blk_raw,
+                                              half8_t (&qa)[D / 32]) {
+  using S = Shape<D, G, I8>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kn = lane & 15, kj = lane >> 4;
+  const int jl = jb + wave + WAVES * lane;
+  blk_raw = jl < prm.max_blocks ? prm.tables[int64_t(b) * prm.max_blocks + jl] : -1;
+  const _Float16* qh = prm.q + (int64_t(b) * prm.Hkv * G + g * G + kn % G) * D;
+#pragma unroll
+  for (int c = 0; c < S::NCH; ++c) qa[c] = *reinterpret_cast<const half8_t*>(qh + S::dim_base(c, kj));
 }
 
-template <int D, int G, bool I8, int GRID>
-__global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_decode_kernel(DecodeParams prm) {
-  constexpr bool COMPACT = GRID == GRID_COMPACT;
+// One segment of a decode work-group: logical blocks jb .. je - 1 of
+// sequence b (context ctx) for KV head g. Wave w takes blocks jb + w,
+// jb + w + 4, ...: its it-th id sits in lane it of blk_raw (loaded by
+// segment_loads, with qa, before the context length is known, so a
+// work-group waits one memory round trip before its first tile), and each
+// tile reads it with readlane, so the id never waits on the vector memory
+// queue. The 4 waves' results merge in LDS in fixed order; the work-group
+// writes the final fp16 rows (final_row) or one (m, l, o[D]) partial per
+// query head into slot `slot` of the head's partial row. append_here: the
+// segment holds the sequence's last block, where the fused append writes
+// the new token. Every thread of the work-group must call it.
+template <int D, int G, bool I8>
+__device__ __forceinline__ void decode_segment(const DecodeParams& prm, int g, int b, int ctx, int jb, int je,
+                                               bool append_here, bool final_row, int slot, int blk_raw,
+                                               const half8_t (&qa)[D / 32], float (&p_lds)[WAVES][BT][G],
+                                               float (&merge_o)[WAVES][G][D], float (&merge_ml)[WAVES][G][2]) {
   using S = Shape<D, G, I8>;
-  const int g = blockIdx.x;
-  __shared__ float p_lds[WAVES][BT][G];
-  __shared__ float merge_o[WAVES][G][D];
-  __shared__ float merge_ml[WAVES][G][2];
-  int bc = 0, pc = 0;
-  if constexpr (COMPACT) {
-    static_assert(sizeof(merge_o) >= (WAVES + 2) * sizeof(int), "compact scan scratch");
-    compact_pair(prm, blockIdx.y + gridDim.y * blockIdx.z, reinterpret_cast<int*>(&merge_o[0][0][0]), bc, pc);
-    if (bc < 0) return;  // uniform over the work-group
-  } else if constexpr (GRID == GRID_PLAN) {
-    // With a shared-prefix plan the first prefix_z planes of the grid are
-    // shared-prefix work-groups: dispatched first, they run beside the split
-    // work-groups of the same launch.
-    if (int(blockIdx.z) < prm.prefix_z) {
-      const int k = blockIdx.y + gridDim.y * blockIdx.z;
-      if (k < prm.prefix_pp * prm.num_groups) prefix_role<D, G, I8>(prm, g, k / prm.prefix_pp, k % prm.prefix_pp);
-      return;
-    }
-  }
-  const int b = COMPACT ? bc : int(blockIdx.y);
-  const int p = COMPACT ? pc : int(blockIdx.z) - (GRID == GRID_PLAN ? prm.prefix_z : 0);
   const int Hkv = prm.Hkv, Hq = Hkv * G;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -1188,40 +1119,8 @@ __global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_de
   const int vt = lane / S::LPR, vd = lane % S::LPR;  // V mapping: row group, dims
   const bool odd = (kj & 1) != 0;  // G == 8: this lane's score rows are heads 4..7
 
-  // The context length, this wave's block ids and q are loaded together, so
-  // a work-group waits one memory round trip, not two, before its first
-  // tile: the block ids of partition p need no length (the table row is
-  // max_blocks wide and padded; ids past the context are masked below).
-  // Wave w takes logical blocks jb + w, jb + w + 4, ...: its it-th id sits in
-  // lane it of a VGPR, and each tile reads it with readlane, so the id never
-  // waits on the vector memory queue.
   const int32_t* trow = prm.tables + int64_t(b) * prm.max_blocks;
-  // With a shared-prefix plan, a grouped sequence's leading shared blocks are
-  // attended by the shared-prefix work-groups: partitions start after them,
-  // and their partials follow the `pre` prefix partials in the partial row.
-  int sb, pre;
-  seq_prefix(prm.plan, b, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
-  const int jb = sb + p * prm.part_blocks;
   const int first = jb + wave;
-  const int jl = first + WAVES * lane;
-  const int blk_raw = jl < prm.max_blocks ? trow[jl] : -1;
-  half8_t qa[S::NCH];  // q as the MFMA A operand: head kn % G, group kj's dims
-  {
-    const _Float16* qh = prm.q + (int64_t(b) * Hq + g * G + kn % G) * D;
-#pragma unroll
-    for (int c = 0; c < S::NCH; ++c) qa[c] = *reinterpret_cast<const half8_t*>(qh + S::dim_base(c, kj));
-  }
-  const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
-
-  if (ctx <= 0) {  // rejected on the host when lengths are given; never NaN
-    if (p == 0)
-      for (int i = tid; i < G * D; i += 256) prm.out[(int64_t(b) * Hq + g * G) * D + i] = _Float16(0.0f);
-    return;
-  }
-  const int nblk = (ctx + BT - 1) / BT;
-  const int nparts = nblk > sb ? (nblk - sb + prm.part_blocks - 1) / prm.part_blocks : 0;
-  if (p >= nparts) return;
-  const int je = min(nblk, jb + prm.part_blocks);
   const int n_my = first < je ? (je - first + WAVES - 1) / WAVES : 0;  // <= 64
   const int blk_lane = lane < n_my ? blk_raw : -1;
 
@@ -1231,14 +1130,14 @@ __global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_de
   const int64_t blk_stride = int64_t(Hkv) * S::TILE;
 
   // Fused append: the new token is the last of the context, at logical
-  // position ctx - 1, in this sequence's last partition. That work-group
+  // position ctx - 1, in this sequence's last segment. That work-group
   // writes its k and v rows for head g into the slot the table gives (fp16:
   // a bitwise copy; int8: quantised on write, its block's scale raised and
   // earlier rows re-rounded when needed), then reads them back with the rest
   // of the tile; no other work-group reads that block of this head in the
   // launch (a slot written at a non-zero offset of a shared block was moved
   // to a private block by copy-on-write).
-  if (prm.k_new && p == nparts - 1) {
+  if (prm.k_new && append_here) {
     const int t = ctx - 1;
     const int blk = trow[t / BT];
     if (unsigned(blk) < unsigned(prm.num_blocks)) {
@@ -1476,10 +1375,10 @@ __global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_de
       O += merge_o[w][h][d] * wt;
     }
     const int64_t row = int64_t(b) * Hq + g * G + h;
-    if (nparts == 1 && pre == 0) {
+    if (final_row) {
       prm.out[row * D + d] = (_Float16)(L > 0.0f ? O / L : 0.0f);
     } else {
-      const int64_t pi = row * prm.max_parts + pre + p;
+      const int64_t pi = row * prm.max_parts + slot;
       prm.part_o[pi * D + d] = O;
       if (d == 0) {
         prm.part_m[pi] = M;
@@ -1487,6 +1386,156 @@ __global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_de
       }
     }
   }
+}
+
+// Stream-K split (ragged batches with host lengths, no plan). The blocks of
+// all sequences, laid end to end (sequence 0's, then 1's, ...), are cut into
+// runs of q = prm.part_blocks blocks, one per work-group of a KV head:
+// work-group k covers blocks [k q, (k + 1) q), which may end one sequence and
+// start the next. Each piece of a sequence it covers is a segment with its
+// own partial, in slot k - floor(C_b / q) of the sequence's partial rows
+// (C_b: the sequence's first block in the run); a sequence that one
+// work-group covers entirely gets its final rows from it. Every sequence's
+// first block C_b comes from a work-group-wide scan of all lengths. Sequences
+// without tokens are skipped (the host rejects them when it has the lengths).
+template <int D, int G, bool I8>
+__device__ __forceinline__ void stream_k_role(const DecodeParams& prm, int g, int k, float (&p_lds)[WAVES][BT][G],
+                                              float (&merge_o)[WAVES][G][D], float (&merge_ml)[WAVES][G][2]) {
+  __shared__ int seq_first[STREAM_MAX_SEQS + 1];
+  __shared__ int seq_ctx[STREAM_MAX_SEQS];
+  static_assert(sizeof(merge_o) >= WAVES * sizeof(int), "scan scratch");
+  int* part = reinterpret_cast<int*>(&merge_o[0][0][0]);
+  const int tid = threadIdx.x;
+  const int B = prm.num_seqs, q = prm.part_blocks;
+  constexpr int PER = STREAM_MAX_SEQS / 256;
+  int n[PER], c[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {  // all lengths in flight together
+    const int t = tid + 256 * i;
+    c[i] = t < B ? clamp_ctx(prm.ctx_lens[t], prm.max_blocks, prm.max_context) : 0;
+    n[i] = c[i] > 0 ? (c[i] + BT - 1) / BT : 0;
+  }
+  int carry = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (256 * i >= B) break;  // uniform
+    int tot;
+    const int ex = carry + wg_exclusive_scan(n[i], part, tot);
+    const int t = tid + 256 * i;
+    if (t < B) {
+      seq_first[t] = ex;
+      seq_ctx[t] = c[i];
+    }
+    carry += tot;
+  }
+  if (tid == 0) seq_first[B] = carry;
+  __syncthreads();
+  const int T = seq_first[B];
+  const int lo = k * q;
+  if (lo >= T) return;  // uniform
+  const int hi = min(lo + q, T);
+  int b = 0, r = B;  // the last sequence whose first block is at or before lo
+  while (r - b > 1) {
+    const int m = (b + r) / 2;
+    if (seq_first[m] <= lo) b = m;
+    else r = m;
+  }
+  for (;;) {
+    const int cb = seq_first[b], cn = seq_first[b + 1];
+    if (cn > cb) {
+      const int s0 = max(lo, cb) - cb, s1 = min(hi, cn) - cb;
+      const int first_wg = cb / q, count = (cn - 1) / q - first_wg + 1;
+      int blk_raw;
+      half8_t qa[D / 32];
+      segment_loads<D, G, I8>(prm, g, b, s0, blk_raw, qa);
+      decode_segment<D, G, I8>(prm, g, b, seq_ctx[b], s0, s1, s1 == cn - cb, count == 1, k - first_wg, blk_raw, qa,
+                               p_lds, merge_o, merge_ml);
+      __syncthreads();  // the next segment reuses the wave-merge buffers
+    }
+    if (cn >= hi || ++b >= B) break;
+  }
+}
+
+// Two work-groups per CU are asked of the register allocator where they
+// fit without spills (G <= 4; fp16 at D = 64): the shared-prefix role would
+// otherwise push the fp16 kernels past 256 registers a lane. The other
+// G = 8 kernels keep the full register file.
+//
+// One work-group (4 wave64s) per (KV head g, sequence b, partition p), in
+// that grid order (x, y, z). Work-groups go to the eight XCDs round-robin by
+// linear id, so the partition index, the dimension along which work runs out
+// first (short sequences, or a shared prefix attended elsewhere), varies
+// slowest: the busy work-groups of any one partition index are spread over
+// all XCDs instead of piling onto those whose id matches a low index.
+//
+// Scores on the matrix cores: per tile, S[r][n] = sum_k Q[r][k] K[n][k] with
+// v_mfma_f32_16x16x32_f16 over D/32 chunks. A-row r holds query head r % G of
+// the group (rows repeat when G < 16), B-column n is token n of the tile.
+// Lane (n = lane % 16, j = lane / 16) feeds token n's K dims of k-slot group
+// j and receives rows 4j..4j+3 of column n: the scores of heads
+// (4j + e) % G, e = 0..3, for its token, already fully reduced.
+//
+// After its last tile the work-group writes one (m, l, o[D]) partial per
+// query head for the merge kernel, or the final fp16 row when the sequence
+// has a single partition.
+// GRID_STREAM: the stream-K split above, chosen by the host from its copy
+// of the lengths for ragged batches. The plain grid holds max-context
+// partitions for every sequence, and a work-group past its sequence's last
+// partition exits once its length has arrived; under a full HBM stream that
+// holds its slot for microseconds, and real work-groups queue behind such
+// exits. GRID_PLAN: the plain grid led by the shared-prefix planes; the
+// multi-row attention of that role needs more registers than the split
+// role, so launches without a plan use GRID_PLAIN, which leaves it out.
+enum { GRID_PLAIN = 0, GRID_STREAM = 1, GRID_PLAN = 2 };
+
+template <bool I8, int D, int G>
+constexpr int decode_wgs_per_cu() {
+  return (I8 || G <= 4) ? 2 : 1;
+}
+
+template <int D, int G, bool I8, int GRID>
+__global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_decode_kernel(DecodeParams prm) {
+  const int g = blockIdx.x;
+  __shared__ float p_lds[WAVES][BT][G];
+  __shared__ float merge_o[WAVES][G][D];
+  __shared__ float merge_ml[WAVES][G][2];
+  if constexpr (GRID == GRID_STREAM) {
+    stream_k_role<D, G, I8>(prm, g, blockIdx.y + gridDim.y * blockIdx.z, p_lds, merge_o, merge_ml);
+    return;
+  } else if constexpr (GRID == GRID_PLAN) {
+    // With a shared-prefix plan the first prefix_z planes of the grid are
+    // shared-prefix work-groups: dispatched first, they run beside the split
+    // work-groups of the same launch.
+    if (int(blockIdx.z) < prm.prefix_z) {
+      const int k = blockIdx.y + gridDim.y * blockIdx.z;
+      if (k < prm.prefix_pp * prm.num_groups) prefix_role<D, G, I8>(prm, g, k / prm.prefix_pp, k % prm.prefix_pp);
+      return;
+    }
+  }
+  const int b = blockIdx.y;
+  const int p = int(blockIdx.z) - (GRID == GRID_PLAN ? prm.prefix_z : 0);
+  // With a shared-prefix plan, a grouped sequence's leading shared blocks are
+  // attended by the shared-prefix work-groups: partitions start after them,
+  // and their partials follow the `pre` prefix partials in the partial row.
+  int sb, pre;
+  seq_prefix(prm.plan, b, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
+  const int jb = sb + p * prm.part_blocks;
+  // the block ids and q are loaded with the context length: one round trip
+  int blk_raw;
+  half8_t qa[D / 32];
+  segment_loads<D, G, I8>(prm, g, b, jb, blk_raw, qa);
+  const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
+  if (ctx <= 0) {  // rejected on the host when lengths are given; never NaN
+    if (p == 0)
+      for (int i = threadIdx.x; i < G * D; i += 256)
+        prm.out[(int64_t(b) * prm.Hkv * G + g * G) * D + i] = _Float16(0.0f);
+    return;
+  }
+  const int nblk = (ctx + BT - 1) / BT;
+  const int nparts = nblk > sb ? (nblk - sb + prm.part_blocks - 1) / prm.part_blocks : 0;
+  if (p >= nparts) return;
+  decode_segment<D, G, I8>(prm, g, b, ctx, jb, min(nblk, jb + prm.part_blocks), p == nparts - 1,
+                           nparts == 1 && pre == 0, pre + p, blk_raw, qa, p_lds, merge_o, merge_ml);
 }
 
 struct MergeParams {
@@ -1499,7 +1548,28 @@ struct MergeParams {
   int D, max_blocks, max_context, part_blocks, max_parts;
   int num_groups, prefix_pp;
   int row_parts;  // partials any row of this launch can hold (<= max_parts)
+  int num_seqs;
+  int stream_q;   // stream-K split: blocks per work-group (0 = partitions of part_blocks per sequence)
 };
+
+// Stream-K split: sequence b's first block C_b in the run of all sequences'
+// blocks, summed over the work-group's threads (tid of nthreads, at most
+// 1024), every thread receiving it. red: 16 ints of LDS.
+__device__ __forceinline__ int run_first_block(const MergeParams& prm, int b, int tid, int nthreads, int* red) {
+  int sum = 0;
+  for (int t = tid; t < b; t += nthreads) {
+    const int c = clamp_ctx(prm.ctx_lens[t], prm.max_blocks, prm.max_context);
+    sum += c > 0 ? (c + BT - 1) / BT : 0;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m, 64);
+  const int wave = tid >> 6, waves = (nthreads + 63) >> 6;
+  if ((tid & 63) == 0) red[wave] = sum;
+  __syncthreads();
+  int total = 0;
+  for (int w = 0; w < waves; ++w) total += red[w];
+  return total;
+}
 
 // Merge the partials of one (sequence, query head) by log-sum-exp:
 // M = max_p m_p, out = sum_p o_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), in
@@ -1548,9 +1618,16 @@ __global__ __launch_bounds__(1024) void lse_reduce_kernel(MergeParams prm) {
   int sb, pre;
   seq_prefix(prm.plan, b, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
   const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
+  const int nblk = ctx > 0 ? (ctx + BT - 1) / BT : 0;
+  int nparts;
+  if (prm.stream_q > 0) {  // the stream-K work-groups that covered the sequence, in order
+    __shared__ int red[16];
+    const int cb = run_first_block(prm, b, d + D * w, D * W, red);
+    nparts = nblk > 0 ? (cb + nblk - 1) / prm.stream_q - cb / prm.stream_q + 1 : 0;
+  } else {
+    nparts = nblk > sb ? (nblk - sb + prm.part_blocks - 1) / prm.part_blocks : 0;
+  }
   if (ctx <= 0) return;  // uniform over the work-group
-  const int nblk = (ctx + BT - 1) / BT;
-  const int nparts = nblk > sb ? (nblk - sb + prm.part_blocks - 1) / prm.part_blocks : 0;
   if (pre == 0 && nparts <= 1) return;
   const int count = min(pre + nparts, prm.row_parts);
 
@@ -1826,7 +1903,7 @@ decode_fn pick_dt(int D, int G, bool i8) {
 }
 
 decode_fn pick_kernel(int D, int G, bool i8, int grid) {
-  return grid == GRID_COMPACT ? pick_dt<GRID_COMPACT>(D, G, i8)
+  return grid == GRID_STREAM ? pick_dt<GRID_STREAM>(D, G, i8)
          : grid == GRID_PLAN  ? pick_dt<GRID_PLAN>(D, G, i8)
                               : pick_dt<GRID_PLAIN>(D, G, i8);
 }
@@ -2116,26 +2193,47 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
     }
   }
 
-  // Compact split grid (no plan, host lengths given): the (sequence,
-  // partition) pairs that hold blocks, and nothing else, when the plain grid
-  // would launch work-groups past some sequence's last partition. Measured on
-  // MI355X, 16 sequences of 1024..8192 tokens cut into 512 full 64-block
-  // partitions: 66.3 us on the plain grid (512 of its 1024 work-groups
-  // empty), 46.5 us compact, 45.5 us for 16 x 4096 tokens (the same
-  // partitions, no empty work-group); the continuous-batching mix (16 x
-  // U[128, 8192]) 68.2 -> 53.0 us, int8 48.9 -> 37.7 us. Dispatching the
-  // plain grid's planes last-first instead is no cure (64.0 and 67.2 us).
-  // The scan costs the compact launch ~1 us at its start, so a ragged batch
-  // whose plain grid has few empty work-groups runs ~2% slower.
-  int64_t pairs = 0;
-  bool compact = false;
-  if (!plan && a->ctx_lens_host && a->num_seqs <= COMPACT_MAX_SEQS) {
+  // Stream-K split (no plan, host lengths given, automatic partitions): a
+  // ragged batch, whose plain grid would launch work-groups past some
+  // sequence's last partition, is laid end to end and cut into equal runs of
+  // q blocks per work-group, about one round of resident work-groups. The
+  // plain grid's cut leaves short remainder partitions beside full ones, and
+  // the longest work-groups set the launch time; equal runs leave none
+  // longer than q (the continuous-batching mix: 72 blocks at most, against
+  // 81 for the one-round partitions).
+  bool stream_k = false;
+  int64_t stream_wgs = 0;
+  int stream_rows = 0;
+  if (!plan && a->ctx_lens_host && a->num_seqs <= STREAM_MAX_SEQS && a->partition_tokens == 0 &&
+      !std::getenv("PKV_PARTITION_TOKENS")) {
     const int64_t cap = std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context);
+    int64_t pairs = 0, T = 0;
     for (int b = 0; b < a->num_seqs; ++b) {
       const int64_t ctx = std::min<int64_t>(a->ctx_lens_host[b], cap);
-      pairs += ctx > 0 ? ((ctx + BT - 1) / BT + pb - 1) / pb : 1;
+      const int64_t nb = (ctx + BT - 1) / BT;
+      pairs += (nb + pb - 1) / pb;
+      T += nb;
     }
-    compact = pairs < int64_t(a->num_seqs) * gparts;
+    if (pairs < int64_t(a->num_seqs) * gparts && T > 0) {
+      const Residency res = resident_wgs(reinterpret_cast<const void*>(fn),
+                                         c.dtype == PKV_I8 ? two_per_cu_lds(reinterpret_cast<const void*>(fn)) : 0);
+      const int64_t slots_h = std::max<int64_t>(1, res.slots / c.num_kv_heads);
+      int64_t q = (T + slots_h - 1) / slots_h;
+      q = std::min<int64_t>(std::max<int64_t>(q, MIN_PART_BLOCKS), MAX_PARTITION_TOKENS / BT);
+      int64_t cb = 0;
+      int rows_max = 0;
+      for (int b = 0; b < a->num_seqs; ++b) {
+        const int64_t nb = (std::min<int64_t>(a->ctx_lens_host[b], cap) + BT - 1) / BT;
+        if (nb > 0) rows_max = std::max<int>(rows_max, int((cb + nb - 1) / q - cb / q + 1));
+        cb += nb;
+      }
+      if (rows_max <= mp0 && (T + q - 1) / q <= int64_t(65535) * 65535) {
+        stream_k = true;
+        stream_wgs = (T + q - 1) / q;
+        stream_rows = rows_max;
+        pb = int(q);
+      }
+    }
   }
 
   const int64_t E = pkv::elem_bytes(c.dtype);
@@ -2172,7 +2270,7 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
   prm.max_context = a->max_context;
   prm.scale_log2 = a->scale * LOG2E;
   prm.num_seqs = a->num_seqs;
-  if (compact) fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, GRID_COMPACT);
+  if (stream_k) fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, GRID_STREAM);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -2181,16 +2279,16 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
 
   // The fused append (if any) writes into private tail blocks only, which no
   // shared-prefix work-group reads.
-  const int cy = int(std::min<int64_t>(pairs, 65535));
-  const dim3 grid = compact ? dim3(c.num_kv_heads, cy, unsigned((pairs + cy - 1) / cy))
-                            : dim3(c.num_kv_heads, a->num_seqs, pz + gparts);
+  const int cy = int(std::min<int64_t>(stream_wgs, 65535));
+  const dim3 grid = stream_k ? dim3(c.num_kv_heads, cy, unsigned((stream_wgs + cy - 1) / cy))
+                           : dim3(c.num_kv_heads, a->num_seqs, pz + gparts);
   const size_t dyn_lds = c.dtype == PKV_I8 ? two_per_cu_lds(reinterpret_cast<const void*>(fn)) : 0;
   if (ev[0] && ev[1])
     hipExtLaunchKernelGGL(fn, grid, dim3(256), dyn_lds, s, ev[0], ev[1], 0, prm);
   else
     hipLaunchKernelGGL(fn, grid, dim3(256), dyn_lds, s, prm);
   st = hip_status(hipGetLastError(), "paged_decode launch");
-  if (st != PKV_OK || (gparts <= 1 && !plan)) return st;
+  if (st != PKV_OK || (stream_k ? stream_rows <= 1 : gparts <= 1 && !plan)) return st;
   MergeParams mg;
   mg.part_m = prm.part_m;
   mg.part_l = prm.part_l;
@@ -2205,13 +2303,15 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
   mg.max_parts = mp;
   mg.num_groups = prm.num_groups;
   mg.prefix_pp = prm.prefix_pp;
-  mg.row_parts = std::min(mp, (plan ? pp : 0) + gparts);
+  mg.row_parts = stream_k ? stream_rows : std::min(mp, (plan ? pp : 0) + gparts);
+  mg.num_seqs = a->num_seqs;
+  mg.stream_q = stream_k ? pb : 0;
   const dim3 rgrid(a->num_q_heads, a->num_seqs);
+  const int ways = merge_ways(mg.row_parts);
   if (ev[2] && ev[3])
-    hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(pp + gparts)), 0, s, ev[2], ev[3], 0,
-                          mg);
+    hipExtLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, ways), 0, s, ev[2], ev[3], 0, mg);
   else
-    hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, merge_ways(pp + gparts)), 0, s, mg);
+    hipLaunchKernelGGL(lse_reduce_kernel, rgrid, dim3(c.head_dim, ways), 0, s, mg);
   return hip_status(hipGetLastError(), "lse_reduce launch");
 }
 

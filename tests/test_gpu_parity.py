@@ -356,16 +356,18 @@ def test_partition_cut_with_and_without_host_lengths(hq, hkv):
     lib.close()
 
 
-@pytest.mark.parametrize("seed,B,max_len,hq,hkv,ptoks", [
-    (2001, 12, 6000, 32, 8, (256, 1024)),   # ragged: short sequences leave plain-grid planes empty
-    (2002, 300, 200, 8, 2, (16, 64)),       # more sequences than one 256-thread scan covers
-    (2003, 1100, 40, 4, 1, (16,)),          # past the compact grid's sequence limit: plain grid
+@pytest.mark.parametrize("seed,B,max_len,hq,hkv", [
+    (2001, 12, 6000, 32, 8),   # ragged: short sequences beside long ones
+    (2002, 300, 200, 8, 2),    # more sequences than one 256-thread scan covers; runs span several sequences
+    (2003, 1100, 40, 4, 1),    # past the stream-K sequence limit: the plain grid
+    (2004, 40, 3000, 16, 2),   # G = 8
 ])
-def test_compact_grid_matches_plain_grid_bitwise(seed, B, max_len, hq, hkv, ptoks):
-    """With host lengths and ragged sequences the launch enumerates only the
-    (sequence, partition) pairs that hold blocks; the partitions are those
-    of the plain grid, so the outputs are bit for bit those of a launch
-    without host lengths at the same partition size and max_context."""
+def test_stream_k_split_matches_oracle_and_plain_grid(seed, B, max_len, hq, hkv):
+    """With host lengths, a ragged batch is laid end to end and cut into
+    equal runs of blocks (a work-group's run may end one sequence and start
+    the next; the merge combines each sequence's pieces in order). The
+    result matches the oracle, a launch without host lengths (the plain
+    grid) within tolerance, and itself bit for bit on a second launch."""
     w = workloads.tiny_random(seed, B=B, Hq=hq, Hkv=hkv, D=128, max_len=max_len)
     lib, o = run_pair(w)
     assert max_err(lib, o) <= F16_TOL
@@ -374,13 +376,11 @@ def test_compact_grid_matches_plain_grid_bitwise(seed, B, max_len, hq, hkv, ptok
     ld = torch.from_numpy(rec["lens"]).to(DEV)
     qd = torch.from_numpy(rec["q"]).to(DEV)
     width = rec["tables"].shape[1] * 16
-    for pt in ptoks:
-        announce(f"compact vs plain grid B={B} Hq={hq} Hkv={hkv} partition_tokens={pt}")
-        plain = lib.cache.paged_decode(qd, td, ld, max_context=width, partition_tokens=pt).cpu().numpy()
-        compact = lib.cache.paged_decode(qd, td, ld, context_lens_host=rec["lens"], max_context=width,
-                                         partition_tokens=pt).cpu().numpy()
-        assert np.array_equal(plain.view(np.uint16), compact.view(np.uint16)), pt
-        assert np.abs(compact.astype(np.float64) - want).max() <= F16_TOL, pt
+    announce(f"stream-K vs plain grid B={B} Hq={hq} Hkv={hkv}")
+    plain = lib.cache.paged_decode(qd, td, ld, max_context=width).cpu().numpy()
+    assert np.abs(plain.astype(np.float64) - want).max() <= F16_TOL
+    again = lib.cache.paged_decode(qd, td, ld, context_lens_host=rec["lens"]).cpu().numpy()
+    assert np.array_equal(again.view(np.uint16), rec["out"].view(np.uint16))
     lib.close()
 
 

@@ -612,7 +612,7 @@ def test_kernels_use_no_scratch_memory():
         pytest.skip("library not built in this tree")
     rows = [l.rstrip("\n").split("\t") for l in open(B.RESOURCES) if not l.startswith("#")]
     names = [r[0] for r in rows]
-    # D in {64, 128} x G in {1, 2, 4, 8} x {f16, i8} x {plain grid, compact grid, plain grid with a
+    # D in {64, 128} x G in {1, 2, 4, 8} x {f16, i8} x {plain grid, stream-K split, plain grid with a
     # shared-prefix plan}
     assert sum("paged_decode_kernel" in n for n in names) == 48
     assert sum("prefill_kernel" in n for n in names) == 16  # the same for the prefill
