@@ -103,8 +103,11 @@ def build(verbose=False):
         objs.append(obj)
     write_resources(kernels)
     # every kernel keeps its state in registers and LDS: scratch memory in a
-    # hot loop costs more than the occupancy it buys
-    bad = [k["name"] for k in kernels if k.get("scratch", 0) or k.get("vgpr_spill", 0) or k.get("sgpr_spill", 0)]
+    # hot loop costs more than the occupancy it buys. Scalar registers
+    # spilled into vector-register lanes (the shared-prefix plan kernels'
+    # launch state) touch no memory and are allowed; a scratch size of zero
+    # shows that every spill went there.
+    bad = [k["name"] for k in kernels if k.get("scratch", 0) or k.get("vgpr_spill", 0)]
     if not kernels:
         raise RuntimeError("no kernel-resource-usage remarks from hipcc")
     if bad:

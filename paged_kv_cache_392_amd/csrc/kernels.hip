@@ -291,6 +291,7 @@ struct DecodeParams {
   const int32_t* plan;  // shared-prefix plan (null = none): per sequence (shared blocks, group*64+member),
                         // then PKV_PREFIX_GROUP_INTS per group
   int prefix_z;         // grid z-planes of shared-prefix work-groups (0 = none)
+  int plan_stream;      // plan grid: the split role is stream-K, its work-groups after the prefix ones
   int prefix_pp;        // prefix partitions per group
   int num_groups;
   int max_blocks;
@@ -388,9 +389,12 @@ __device__ __forceinline__ float4_t half_of8(const float (&x)[8], bool upper) {
 // ---------------------------------------------------------------------------
 // shared-prefix attention
 
-// Query rows a shared-prefix work-group attends per KV head: group members x
-// (Hq / Hkv), at most 128 (eight 16-row MFMA blocks over four waves).
+// Query rows of a shared-prefix group per KV head: members x (Hq / Hkv), at
+// most 128, attended by PREFIX_SPLIT work-groups of up to 64 rows (one
+// 16-row MFMA block per wave).
 constexpr int PREFIX_ROWS = 128;
+constexpr int PREFIX_SPLIT = 2;
+constexpr int PREFIX_HALF_ROWS = PREFIX_ROWS / PREFIX_SPLIT;
 
 // A group's np shared blocks are cut into at most pp partitions of
 // ceil(np / pp) blocks; prefix_parts of them are non-empty.
@@ -454,7 +458,8 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 // group j pointing at V[4j + s/4][16 i + 4 (s % 4)], lane (n, j) receives
 // V[4j..4j+3][16 i + n]: the A operand, 4 tokens of one dim. Online
 // softmax per row in base 2 with the lazy running max of the split kernel.
-template <int D, int MAXT, bool MASK, bool STREAM, int PFS, bool I8, typename QRow, typename Limit, typename Emit>
+template <int D, int MAXT, bool MASK, bool STREAM, int PFS, bool I8, int RB, typename QRow, typename Limit,
+          typename Emit>
 __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, const uint32_t* scales, int Hkv, int g,
                                             int num_blocks, const int32_t* trow, int jb, int nt, int R, int nvalid,
                                             int full_tokens, float scale_log2, QRow qrow, Limit limit,
@@ -501,8 +506,9 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   const int nsteps = (nt + 1) / 2;
 
   // q^T as the B operand of the score MFMA, per row block of this wave
+  static_assert(RB == 1 || RB == 2, "one or two 16-row blocks per wave");
   const int rb0 = wave, rb1 = wave + 4;
-  const bool has0 = rb0 * 16 < R, has1 = rb1 * 16 < R;
+  const bool has0 = rb0 * 16 < R, has1 = RB == 2 && rb1 * 16 < R;
   auto load_q = [&](int rb, half8_t (&qb)[NCH]) {
     const _Float16* qp = qrow(rb * 16 + ln);
 #pragma unroll
@@ -510,7 +516,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   };
   half8_t q0[NCH], q1[NCH];
   load_q(rb0, q0);
-  load_q(rb1, q1);
+  if constexpr (RB == 2) load_q(rb1, q1);
   const int lim0 = MASK ? limit(rb0 * 16 + ln) : 0, lim1 = MASK ? limit(rb1 * 16 + ln) : 0;
 
   float4_t o0[NDB], o1[NDB];
@@ -654,12 +660,12 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
       for (int c = 0; c < NCH; ++c) {
         const half8_t ka = *reinterpret_cast<const half8_t*>(kst[st][sub] + ln * KROW + (32 * c + 8 * lj) * 2);
         acc0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q0[c], acc0[sub], 0, 0, 0);
-        acc1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q1[c], acc1[sub], 0, 0, 0);
+        if constexpr (RB == 2) acc1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q1[c], acc1[sub], 0, 0, 0);
       }
     }
     float a0[8], a1[8];
     prep(acc0, step, lim0, masked, o0, m0, l0, a0);
-    prep(acc1, step, lim1, masked, o1, m1, l1, a1);
+    if constexpr (RB == 2) prep(acc1, step, lim1, masked, o1, m1, l1, a1);
     const half8_t pt0 = probs(a0, m0, l0);
     // lane (n, j) addresses V[4j + n/4][16 i + 4 (n % 4)] of each tile
     const int vofs = (4 * lj + (ln >> 2)) * VROW + (ln & 3) * 8;
@@ -673,14 +679,18 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
       va[i] = __builtin_bit_cast(half8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       o0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[i], pt0, o0[i], 0, 0, 0);
     }
-    const half8_t pt1 = probs(a1, m1, l1);
+    if constexpr (RB == 2) {
+      const half8_t pt1 = probs(a1, m1, l1);
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) o1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[i], pt1, o1[i], 0, 0, 0);
+      for (int i = 0; i < NDB; ++i) o1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[i], pt1, o1[i], 0, 0, 0);
+    }
     // interleave: one MFMA, then a few VALU instructions, while they last
+    if constexpr (RB == 2) {
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      for (int i = 0; i < NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
     }
   };
 
@@ -722,20 +732,26 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   // the row sums over the four token groups
   l0 += xor_shfl(l0, 16);
   l0 += xor_shfl(l0, 32);
-  l1 += xor_shfl(l1, 16);
-  l1 += xor_shfl(l1, 32);
   if (has0 && rb0 * 16 + ln < R) emit(rb0 * 16 + ln, o0, m0, l0);
-  if (has1 && rb1 * 16 + ln < R) emit(rb1 * 16 + ln, o1, m1, l1);
+  if constexpr (RB == 2) {
+    l1 += xor_shfl(l1, 16);
+    l1 += xor_shfl(l1, 32);
+    if (has1 && rb1 * 16 + ln < R) emit(rb1 * 16 + ln, o1, m1, l1);
+  }
 }
 
 // The shared-prefix role of a decode work-group: KV head g, partition `part`
-// of group grp's shared blocks. The group's members share their leading
+// of group grp's shared blocks, query rows half * 64 .. half * 64 + 63 of the
+// group's (two work-groups share a partition's rows: each step's chain of
+// matrix and softmax work is half as long, and the second reads the tiles
+// the first brought into its XCD's L2, the two being PREFIX_SPLIT apart in
+// dispatch order, Hkv work-groups apart in linear id). The group's members share their leading
 // blocks ([p1] §三): each K/V tile of the run is read once here and attended
 // by all R = members x G query rows. Shared blocks are full, so nothing is
 // masked. Each row ends as one (m, l, o[D]) partial, written into slot
 // `part` of the member's own partial row, ahead of its split-K partials.
 template <int D, int G, bool I8>
-__device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int grp, int part) {
+__device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int grp, int part, int half) {
   constexpr int NDB = D / 16;
   const int lj = (threadIdx.x & 63) >> 4;
   const int B = prm.num_seqs, Hq = prm.Hkv * G;
@@ -743,21 +759,23 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
   const int np = min(gd[0], prm.max_blocks);
   const int members = min(gd[1], PKV_MAX_SHARERS);
   const int R = min(members * G, PREFIX_ROWS);
+  const int r0 = half * PREFIX_HALF_ROWS;  // this work-group's rows: r0 .. r0 + 63 of the group's
+  const int Rh = min(R - r0, PREFIX_HALF_ROWS);
   const int b0 = gd[2];
-  if (np <= 0 || R <= 0 || unsigned(b0) >= unsigned(B)) return;
+  if (np <= 0 || Rh <= 0 || unsigned(b0) >= unsigned(B)) return;
   const int pbp = prefix_blocks_per_part(np, prm.prefix_pp);  // <= 64: the host sizes prefix_pp
   const int jb = part * pbp, je = min(np, jb + pbp);
   if (jb >= je) return;
-  auto member_of = [&](int r) { return r < R ? gd[2 + r / G] : -1; };
+  auto member_of = [&](int r) { return r < Rh ? gd[2 + (r0 + r) / G] : -1; };
   auto qrow = [&](int r) -> const _Float16* {
     const int bb = member_of(r);
-    return unsigned(bb) < unsigned(B) ? prm.q + (int64_t(bb) * Hq + g * G + r % G) * D : nullptr;
+    return unsigned(bb) < unsigned(B) ? prm.q + (int64_t(bb) * Hq + g * G + (r0 + r) % G) * D : nullptr;
   };
   auto no_limit = [](int) { return 0; };
   auto emit = [&](int r, const float4_t (&o)[NDB], float m, float l) {
     const int bb = member_of(r);
     if (unsigned(bb) >= unsigned(B)) return;
-    const int64_t pi = (int64_t(bb) * Hq + g * G + r % G) * prm.max_parts + part;
+    const int64_t pi = (int64_t(bb) * Hq + g * G + (r0 + r) % G) * prm.max_parts + part;
 #pragma unroll
     for (int i = 0; i < NDB; ++i)
 #pragma unroll
@@ -767,9 +785,9 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
       prm.part_l[pi] = l;
     }
   };
-  attend_rows<D, 64, false, true, 2, I8>(static_cast<const char*>(prm.K), static_cast<const char*>(prm.V),
+  attend_rows<D, 64, false, false, 2, I8, 1>(static_cast<const char*>(prm.K), static_cast<const char*>(prm.V),
                                          reinterpret_cast<const uint32_t*>(prm.scales), prm.Hkv, g, prm.num_blocks,
-                                         prm.tables + int64_t(b0) * prm.max_blocks, jb, je - jb, R, 0, 0,
+                                         prm.tables + int64_t(b0) * prm.max_blocks, jb, je - jb, Rh, 0, 0,
                                          prm.scale_log2, qrow, no_limit, emit);
 }
 
@@ -833,7 +851,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
       *reinterpret_cast<half4_t*>(dst + 16 * i) = h;
     }
   };
-  attend_rows<D, PREFILL_MAX_TILES, true, false, PREFILL_PFS, I8>(prm.K, prm.V, prm.scales, prm.Hkv, g,
+  attend_rows<D, PREFILL_MAX_TILES, true, false, PREFILL_PFS, I8, 2>(prm.K, prm.V, prm.scales, prm.Hkv, g,
                                                                   prm.num_blocks,
                                                                   prm.tables + int64_t(b) * prm.max_blocks, 0, nt,
                                                                   R, n, pos0 + 1, prm.scale_log2, qrow, limit, emit);
@@ -1398,7 +1416,9 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& prm, int g, i
 // work-group covers entirely gets its final rows from it. Every sequence's
 // first block C_b comes from a work-group-wide scan of all lengths. Sequences
 // without tokens are skipped (the host rejects them when it has the lengths).
-template <int D, int G, bool I8>
+// With a shared-prefix plan a grouped sequence's span starts after its
+// shared blocks, and its partials follow the group's prefix partials.
+template <int D, int G, bool I8, bool PLAN>
 __device__ __forceinline__ void stream_k_role(const DecodeParams& prm, int g, int k, float (&p_lds)[WAVES][BT][G],
                                               float (&merge_o)[WAVES][G][D], float (&merge_ml)[WAVES][G][2]) {
   __shared__ int seq_first[STREAM_MAX_SEQS + 1];
@@ -1413,7 +1433,9 @@ __device__ __forceinline__ void stream_k_role(const DecodeParams& prm, int g, in
   for (int i = 0; i < PER; ++i) {  // all lengths in flight together
     const int t = tid + 256 * i;
     c[i] = t < B ? clamp_ctx(prm.ctx_lens[t], prm.max_blocks, prm.max_context) : 0;
-    n[i] = c[i] > 0 ? (c[i] + BT - 1) / BT : 0;
+    int sb = 0, pre;
+    if (PLAN && t < B) seq_prefix(prm.plan, t, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
+    n[i] = c[i] > 0 ? max((c[i] + BT - 1) / BT - sb, 0) : 0;  // the span after the shared blocks
   }
   int carry = 0;
 #pragma unroll
@@ -1443,13 +1465,15 @@ __device__ __forceinline__ void stream_k_role(const DecodeParams& prm, int g, in
   for (;;) {
     const int cb = seq_first[b], cn = seq_first[b + 1];
     if (cn > cb) {
+      int sb = 0, pre = 0;  // a grouped sequence's span starts after its shared blocks; its prefix partials first
+      if constexpr (PLAN) seq_prefix(prm.plan, b, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
       const int s0 = max(lo, cb) - cb, s1 = min(hi, cn) - cb;
       const int first_wg = cb / q, count = (cn - 1) / q - first_wg + 1;
       int blk_raw;
       half8_t qa[D / 32];
-      segment_loads<D, G, I8>(prm, g, b, s0, blk_raw, qa);
-      decode_segment<D, G, I8>(prm, g, b, seq_ctx[b], s0, s1, s1 == cn - cb, count == 1, k - first_wg, blk_raw, qa,
-                               p_lds, merge_o, merge_ml);
+      segment_loads<D, G, I8>(prm, g, b, sb + s0, blk_raw, qa);
+      decode_segment<D, G, I8>(prm, g, b, seq_ctx[b], sb + s0, sb + s1, s1 == cn - cb, count == 1 && pre == 0,
+                               pre + k - first_wg, blk_raw, qa, p_lds, merge_o, merge_ml);
       __syncthreads();  // the next segment reuses the wave-merge buffers
     }
     if (cn >= hi || ++b >= B) break;
@@ -1500,15 +1524,23 @@ __global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_de
   __shared__ float merge_o[WAVES][G][D];
   __shared__ float merge_ml[WAVES][G][2];
   if constexpr (GRID == GRID_STREAM) {
-    stream_k_role<D, G, I8>(prm, g, blockIdx.y + gridDim.y * blockIdx.z, p_lds, merge_o, merge_ml);
+    stream_k_role<D, G, I8, false>(prm, g, blockIdx.y + gridDim.y * blockIdx.z, p_lds, merge_o, merge_ml);
     return;
   } else if constexpr (GRID == GRID_PLAN) {
-    // With a shared-prefix plan the first prefix_z planes of the grid are
-    // shared-prefix work-groups: dispatched first, they run beside the split
-    // work-groups of the same launch.
-    if (int(blockIdx.z) < prm.prefix_z) {
-      const int k = blockIdx.y + gridDim.y * blockIdx.z;
-      if (k < prm.prefix_pp * prm.num_groups) prefix_role<D, G, I8>(prm, g, k / prm.prefix_pp, k % prm.prefix_pp);
+    // With a shared-prefix plan the grid leads with the shared-prefix
+    // work-groups: dispatched first, they run beside the split work-groups of
+    // the same launch, which follow them (stream-K, when the host has both
+    // the lengths and the plan) or fill the planes after the first prefix_z.
+    const int k = blockIdx.y + gridDim.y * blockIdx.z;
+    const int units = prm.prefix_pp * prm.num_groups * PREFIX_SPLIT;
+    if (prm.plan_stream ? k < units : int(blockIdx.z) < prm.prefix_z) {
+      const int unit = k / PREFIX_SPLIT;
+      if (unit < prm.prefix_pp * prm.num_groups)
+        prefix_role<D, G, I8>(prm, g, unit / prm.prefix_pp, unit % prm.prefix_pp, k % PREFIX_SPLIT);
+      return;
+    }
+    if (prm.plan_stream) {
+      stream_k_role<D, G, I8, true>(prm, g, k - units, p_lds, merge_o, merge_ml);
       return;
     }
   }
@@ -1552,15 +1584,19 @@ struct MergeParams {
   int stream_q;   // stream-K split: blocks per work-group (0 = partitions of part_blocks per sequence)
 };
 
-// Stream-K split: sequence b's first block C_b in the run of all sequences'
-// blocks, summed over the work-group's threads (tid of nthreads, at most
-// 1024), every thread receiving it. red: 16 ints of LDS.
+// Stream-K split: the blocks sequence b's span (its blocks after any shared
+// ones) has and where it starts in the run of all spans, summed over the
+// work-group's threads (tid of nthreads, at most 1024), every thread
+// receiving it. red: 16 ints of LDS.
+__device__ __forceinline__ int span_blocks(const MergeParams& prm, int t) {
+  const int c = clamp_ctx(prm.ctx_lens[t], prm.max_blocks, prm.max_context);
+  int sb, pre;
+  seq_prefix(prm.plan, t, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
+  return c > 0 ? max((c + BT - 1) / BT - sb, 0) : 0;
+}
 __device__ __forceinline__ int run_first_block(const MergeParams& prm, int b, int tid, int nthreads, int* red) {
   int sum = 0;
-  for (int t = tid; t < b; t += nthreads) {
-    const int c = clamp_ctx(prm.ctx_lens[t], prm.max_blocks, prm.max_context);
-    sum += c > 0 ? (c + BT - 1) / BT : 0;
-  }
+  for (int t = tid; t < b; t += nthreads) sum += span_blocks(prm, t);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m, 64);
   const int wave = tid >> 6, waves = (nthreads + 63) >> 6;
@@ -1620,10 +1656,11 @@ __global__ __launch_bounds__(1024) void lse_reduce_kernel(MergeParams prm) {
   const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
   const int nblk = ctx > 0 ? (ctx + BT - 1) / BT : 0;
   int nparts;
-  if (prm.stream_q > 0) {  // the stream-K work-groups that covered the sequence, in order
+  if (prm.stream_q > 0) {  // the stream-K work-groups that covered the sequence's span, in order
     __shared__ int red[16];
     const int cb = run_first_block(prm, b, d + D * w, D * W, red);
-    nparts = nblk > 0 ? (cb + nblk - 1) / prm.stream_q - cb / prm.stream_q + 1 : 0;
+    const int span = ctx > 0 ? max(nblk - sb, 0) : 0;
+    nparts = span > 0 ? (cb + span - 1) / prm.stream_q - cb / prm.stream_q + 1 : 0;
   } else {
     nparts = nblk > sb ? (nblk - sb + prm.part_blocks - 1) / prm.part_blocks : 0;
   }
@@ -1954,7 +1991,7 @@ WsLayout ws_layout(const pkv_config& c, int B, int Hq, int max_context, int max_
   w.part_blocks = choose_part_blocks(c.num_kv_heads, B, max_context, partition_tokens, 2048);
   w.grid_parts = max_parts_for(max_context, w.part_blocks);
   w.prefix_pp = n_groups > 0 ? prefix_partitions(c.num_kv_heads, n_groups, max_blocks) : 0;
-  w.prefix_z = n_groups > 0 ? int((int64_t(w.prefix_pp) * n_groups + B - 1) / B) : 0;
+  w.prefix_z = n_groups > 0 ? int((int64_t(w.prefix_pp) * n_groups * PREFIX_SPLIT + B - 1) / B) : 0;
   w.max_parts = w.grid_parts + w.prefix_pp;
   w.bytes = n_groups > 0 ? int64_t(B) * Hq * w.max_parts * (c.head_dim + 2) * int64_t(sizeof(float))
                          : workspace_bytes_for(c, B, Hq, w.max_parts);
@@ -2154,7 +2191,7 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
                                                            int64_t(gi) * PKV_PREFIX_GROUP_INTS],
                                          a->max_blocks));
     pp = std::min(pp, std::max(1, (max_np + PREFIX_PART_BLOCKS - 1) / PREFIX_PART_BLOCKS));
-    pz = int((int64_t(pp) * a->prefix_groups + a->num_seqs - 1) / a->num_seqs);
+    pz = int((int64_t(pp) * a->prefix_groups * PREFIX_SPLIT + a->num_seqs - 1) / a->num_seqs);
   }
   if (int64_t(pz) + mp0 > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many partitions for one launch");
 
@@ -2193,41 +2230,56 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
     }
   }
 
-  // Stream-K split (no plan, host lengths given, automatic partitions): a
-  // ragged batch, whose plain grid would launch work-groups past some
-  // sequence's last partition, is laid end to end and cut into equal runs of
-  // q blocks per work-group, about one round of resident work-groups. The
-  // plain grid's cut leaves short remainder partitions beside full ones, and
-  // the longest work-groups set the launch time; equal runs leave none
-  // longer than q (the continuous-batching mix: 72 blocks at most, against
-  // 81 for the one-round partitions).
+  // Stream-K split (host lengths given, automatic partitions): the spans the
+  // split role covers (every block without a plan; a grouped sequence's
+  // blocks after its shared ones with one) laid end to end and cut into
+  // equal runs of q blocks per work-group, about one round of resident
+  // work-groups beside the shared-prefix ones. Without a plan it is taken
+  // for ragged batches, whose plain grid would launch work-groups past some
+  // sequence's last partition: the plain grid's cut leaves short remainder
+  // partitions beside full ones, and the longest work-groups set the launch
+  // time; equal runs leave none longer than q (the continuous-batching mix:
+  // 72 blocks at most, against 81 for the one-round partitions; 53.0 ->
+  // 51.4 us). With a plan (and its host copy) it always is: the plain
+  // grid's split planes queue behind work-groups with nothing to do.
+  const int units = plan ? pp * a->prefix_groups * PREFIX_SPLIT : 0;  // prefix work-groups per KV head
   bool stream_k = false;
   int64_t stream_wgs = 0;
   int stream_rows = 0;
-  if (!plan && a->ctx_lens_host && a->num_seqs <= STREAM_MAX_SEQS && a->partition_tokens == 0 &&
-      !std::getenv("PKV_PARTITION_TOKENS")) {
+  if (a->ctx_lens_host && (!plan || a->prefix_plan_host) && a->num_seqs <= STREAM_MAX_SEQS &&
+      a->partition_tokens == 0 && !std::getenv("PKV_PARTITION_TOKENS")) {
     const int64_t cap = std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context);
+    auto shared = [&](int b) {
+      return plan ? std::min(std::max(a->prefix_plan_host[2 * b], 0), a->max_blocks) : 0;
+    };
+    auto pre_parts = [&](int b) {  // the prefix partials leading sequence b's row
+      if (!plan) return 0;
+      const int sb = shared(b), gm = a->prefix_plan_host[2 * b + 1];
+      if (gm < 0 || (gm >> 6) >= a->prefix_groups || sb <= 0) return 0;
+      const int pbp = (sb + pp - 1) / pp;
+      return (sb + pbp - 1) / pbp;
+    };
     int64_t pairs = 0, T = 0;
     for (int b = 0; b < a->num_seqs; ++b) {
-      const int64_t ctx = std::min<int64_t>(a->ctx_lens_host[b], cap);
-      const int64_t nb = (ctx + BT - 1) / BT;
+      const int64_t nb = std::max<int64_t>((std::min<int64_t>(a->ctx_lens_host[b], cap) + BT - 1) / BT - shared(b), 0);
       pairs += (nb + pb - 1) / pb;
       T += nb;
     }
-    if (pairs < int64_t(a->num_seqs) * gparts && T > 0) {
+    if ((plan || pairs < int64_t(a->num_seqs) * gparts) && T > 0) {
       const Residency res = resident_wgs(reinterpret_cast<const void*>(fn),
                                          c.dtype == PKV_I8 ? two_per_cu_lds(reinterpret_cast<const void*>(fn)) : 0);
-      const int64_t slots_h = std::max<int64_t>(1, res.slots / c.num_kv_heads);
+      const int64_t slots_h = std::max<int64_t>(1, res.slots / c.num_kv_heads - units);
       int64_t q = (T + slots_h - 1) / slots_h;
       q = std::min<int64_t>(std::max<int64_t>(q, MIN_PART_BLOCKS), MAX_PARTITION_TOKENS / BT);
       int64_t cb = 0;
       int rows_max = 0;
       for (int b = 0; b < a->num_seqs; ++b) {
-        const int64_t nb = (std::min<int64_t>(a->ctx_lens_host[b], cap) + BT - 1) / BT;
-        if (nb > 0) rows_max = std::max<int>(rows_max, int((cb + nb - 1) / q - cb / q + 1));
+        const int64_t nb =
+            std::max<int64_t>((std::min<int64_t>(a->ctx_lens_host[b], cap) + BT - 1) / BT - shared(b), 0);
+        if (nb > 0) rows_max = std::max<int>(rows_max, pre_parts(b) + int((cb + nb - 1) / q - cb / q + 1));
         cb += nb;
       }
-      if (rows_max <= mp0 && (T + q - 1) / q <= int64_t(65535) * 65535) {
+      if (rows_max <= mp && (T + q - 1) / q + units <= int64_t(65535) * 65535) {
         stream_k = true;
         stream_wgs = (T + q - 1) / q;
         stream_rows = rows_max;
@@ -2270,7 +2322,8 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
   prm.max_context = a->max_context;
   prm.scale_log2 = a->scale * LOG2E;
   prm.num_seqs = a->num_seqs;
-  if (stream_k) fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, GRID_STREAM);
+  prm.plan_stream = plan && stream_k ? 1 : 0;
+  if (stream_k && !plan) fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, GRID_STREAM);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -2279,16 +2332,17 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
 
   // The fused append (if any) writes into private tail blocks only, which no
   // shared-prefix work-group reads.
-  const int cy = int(std::min<int64_t>(stream_wgs, 65535));
-  const dim3 grid = stream_k ? dim3(c.num_kv_heads, cy, unsigned((stream_wgs + cy - 1) / cy))
-                           : dim3(c.num_kv_heads, a->num_seqs, pz + gparts);
+  const int64_t lin = stream_wgs + units;  // stream-K: prefix work-groups first, then the runs
+  const int cy = int(std::min<int64_t>(lin, 65535));
+  const dim3 grid = stream_k ? dim3(c.num_kv_heads, cy, unsigned((lin + cy - 1) / cy))
+                             : dim3(c.num_kv_heads, a->num_seqs, pz + gparts);
   const size_t dyn_lds = c.dtype == PKV_I8 ? two_per_cu_lds(reinterpret_cast<const void*>(fn)) : 0;
   if (ev[0] && ev[1])
     hipExtLaunchKernelGGL(fn, grid, dim3(256), dyn_lds, s, ev[0], ev[1], 0, prm);
   else
     hipLaunchKernelGGL(fn, grid, dim3(256), dyn_lds, s, prm);
   st = hip_status(hipGetLastError(), "paged_decode launch");
-  if (st != PKV_OK || (stream_k ? stream_rows <= 1 : gparts <= 1 && !plan)) return st;
+  if (st != PKV_OK || (stream_k ? stream_rows <= 1 && !plan : gparts <= 1 && !plan)) return st;
   MergeParams mg;
   mg.part_m = prm.part_m;
   mg.part_l = prm.part_l;
