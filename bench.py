@@ -124,10 +124,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(src_hash, bytes_per_launch):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "paged_decode_b16_ctx8k_traffic.json")
+def measured_traffic(name, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    ``profiles/<name>_traffic.json``, if it was taken on the current kernel
+    source; else None."""
+    if name is None:
+        return None
+    path = os.path.join(ROOT, "profiles", name + "_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -416,7 +419,7 @@ def main():
         probe = nbytes * reps / (p0.elapsed_time(p1) * 1e-3) / 1e9
 
     src_hash = kernel_source_hash()
-    traffic = None if i8 else measured_traffic(src_hash, float(np.mean(split_bytes)))
+    traffic = None if i8 or args.partition_tokens else measured_traffic("paged_decode_b16_ctx8k", src_hash)
     result = {
         "metric": "paged decode HBM GB/s (% of peak) + decode tok/s, 32q/8kv d128 " + ("int8" if i8 else "fp16"),
         "value": round(value, 1),
@@ -540,7 +543,8 @@ def time_append(torch, C, lib, cache, dev, sp, K, knew, vnew, seq_arr, max_block
             "tokens_per_launch": nb, "launches_per_replay": L}
 
 
-def decode_only_bench(args, torch, pkv, C, lens, hq, hkv, dtype, free_order, seed, metric, workload):
+def decode_only_bench(args, torch, pkv, C, lens, hq, hkv, dtype, free_order, seed, metric, workload,
+                      traffic_name=None):
     """Decode-only step (no append) over `args.layers` layer pools: one
     paged decode per layer for sequences of the given context lengths, q
     heads, KV heads and element type (d128). K/V (codes and scales for int8)
@@ -672,7 +676,8 @@ def decode_only_bench(args, torch, pkv, C, lens, hq, hkv, dtype, free_order, see
         "graph_matches_eager_bitwise": same,
         "roofline": {"bound": "hbm", "kernel": f"paged_decode_kernel<128,{G},{dtype}> (split-K decode)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(traffic_name, kernel_source_hash()),
                      "bytes_per_launch": int(kernel_bytes)},
         "cpu_baseline": None,
     }), flush=True)
@@ -687,7 +692,8 @@ def int8_decode_bench(args, torch, pkv, C, workloads):
     decode_only_bench(args, torch, pkv, C, [8192] * B, HQ, HKV, "i8", w.free_order, w.seed,
                       "paged decode HBM GB/s (% of peak), int8 K/V, 32q/8kv d128",
                       "int8 decode-only step, batch 16, context 8192, 32 q heads / 8 KV heads, head_dim 128, "
-                      "int8 K/V with one fp16 scale per (block, KV head), 32 layer pools")
+                      "int8 K/V with one fp16 scale per (block, KV head), 32 layer pools",
+                      traffic_name=None if args.partition_tokens else "paged_decode_int8_b16_ctx8k")
 
 
 def c3_decode_bench(args, torch, pkv, C, workloads):
@@ -703,7 +709,9 @@ def c3_decode_bench(args, torch, pkv, C, workloads):
     decode_only_bench(args, torch, pkv, C, lens, HQ, HKV, "f16", order, seed,
                       "paged decode HBM GB/s (% of peak), fp16, continuous-batching mix",
                       "decode-only step, 16 sequences at U[128, 8192] + 1 tokens (seeded), 32 q heads / "
-                      "8 KV heads, head_dim 128, fp16, scrambled block order, 32 layer pools")
+                      "8 KV heads, head_dim 128, fp16, scrambled block order, 32 layer pools",
+                      traffic_name=None if args.partition_tokens or args.seed is not None
+                      else "paged_decode_c3_mix_b16")
 
 
 def shape_decode_bench(args, torch, pkv, C, workloads):
