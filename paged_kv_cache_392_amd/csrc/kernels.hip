@@ -483,6 +483,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   static_assert(MAXT > REFILL || MAXT <= 64, "a refilled ring must hold more than one refill");
 
   const int tid = threadIdx.x, lane = tid & 63;
+  __builtin_assume(tid < 256);  // work-groups of 256 threads
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lj = lane >> 4;
   auto stage_id = [&](int i) {  // tile i's id (and int8 scales) into its ring slot
@@ -505,14 +506,24 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   };
   const int nsteps = (nt + 1) / 2;
 
-  // q^T as the B operand of the score MFMA, per row block of this wave
+  // q^T as the B operand of the score MFMA, per row block of this wave. A
+  // negative scale's sign moves into q (exact), so the scores below are
+  // always multiplied by sl2 = |scale_log2|: a raw score a then exceeds the
+  // threshold thr = (m + LAZY_MAX) / sl2 exactly when its scaled value beats
+  // the running max m by more than LAZY_MAX.
   static_assert(RB == 1 || RB == 2, "one or two 16-row blocks per wave");
   const int rb0 = wave, rb1 = wave + 4;
   const bool has0 = rb0 * 16 < R, has1 = RB == 2 && rb1 * 16 < R;
+  const uint32_t qsign = scale_log2 < 0.0f ? 0x80008000u : 0u;
+  const float sl2 = fabsf(scale_log2), inv_sl2 = 1.0f / sl2;
   auto load_q = [&](int rb, half8_t (&qb)[NCH]) {
     const _Float16* qp = qrow(rb * 16 + ln);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) qb[c] = qp ? *reinterpret_cast<const half8_t*>(qp + 32 * c + 8 * lj) : half8_t{};
+    for (int c = 0; c < NCH; ++c) {
+      u32x4 w = qp ? *reinterpret_cast<const u32x4*>(qp + 32 * c + 8 * lj) : u32x4{0u, 0u, 0u, 0u};
+      w ^= qsign;
+      qb[c] = __builtin_bit_cast(half8_t, w);
+    }
   };
   half8_t q0[NCH], q1[NCH];
   load_q(rb0, q0);
@@ -525,7 +536,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
     o0[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
     o1[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.0f, l1 = 0.0f;
+  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.0f, l1 = 0.0f, thr0 = -INFINITY, thr1 = -INFINITY;
 
   // Tile staging: a tile is 2 x LOADERS 16-byte pieces (K, then V), each
   // piece along a row; thread t moves pieces t + 256 j (int8 at D = 64: only
@@ -564,10 +575,14 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
       for (int j = 0; j < NLD; ++j) {
         const int q = tid + 256 * j;
         int lrow, lpc;
+        // V rows at or past nvalid of this tile: `room` of its rows are
+        // valid, all of them unless it holds the end of the written tokens
+        // (a uniform test, so whole tiles skip the per-row one)
+        const int room = nvalid - (jb + 2 * step + sub) * BT;
         if constexpr (I8) {
           if (q >= 2 * LOADERS) continue;
           piece(q, lrow, lpc);
-          const bool live = q < LOADERS || !MASK || (jb + 2 * step + sub) * BT + lrow < nvalid;
+          const bool live = q < LOADERS || !MASK || room >= BT || lrow < room;
           char* dst = q < LOADERS ? kst[st][sub] + lrow * KROW : vst[st][sub] + lrow * VROW;
           const uint32_t sc = tile_sc[min(2 * step + sub, nt - 1) % MAXT];
           const uint32_t s1 = q < LOADERS ? (sc & 0xffffu) : (sc >> 16);  // K or V scale
@@ -580,9 +595,9 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
           if (q < LOADERS) {
             *reinterpret_cast<uint4*>(kst[st][sub] + lrow * KROW + lpc * 16) = r[sub][j];
           } else {
-            const bool live = !MASK || (jb + 2 * step + sub) * BT + lrow < nvalid;
-            *reinterpret_cast<uint4*>(vst[st][sub] + lrow * VROW + lpc * 16) =
-                live ? r[sub][j] : make_uint4(0u, 0u, 0u, 0u);
+            uint4* dst = reinterpret_cast<uint4*>(vst[st][sub] + lrow * VROW + lpc * 16);
+            *dst = r[sub][j];
+            if (MASK && room < BT && lrow >= room) *dst = make_uint4(0u, 0u, 0u, 0u);  // same lane: in order
           }
         }
       }
@@ -593,12 +608,13 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   // short because the VALU, not the matrix cores, sets this loop's pace, and
   // split in two so the exponentials of one row block can issue beside the
   // other's value MFMAs. prep: masking only in the `masked` variant (the
-  // diagonal and the odd tail, chosen per step) and the lazy-max test on the
-  // raw scores' maximum (raising m and rescaling when needed). probs: one
-  // FMA into each exponential, row sums of the fp16 probabilities by v_dot2
-  // against ones; returns P in the value MFMA's k-slot order.
+  // diagonal and the odd tail, chosen per step) and the lazy-max test, one
+  // compare per raw score against the row's threshold (raising m, thr and
+  // rescaling when any lane's score passes it). probs: one FMA into each
+  // exponential, row sums of the fp16 probabilities by v_dot2 against ones;
+  // returns P in the value MFMA's k-slot order.
   auto prep = [&](const float4_t (&acc)[2], int step, int lim, auto masked, float4_t (&o)[NDB], float& m,
-                  float& l, float (&a)[8]) {
+                  float& l, float& thr, float (&a)[8]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -614,14 +630,19 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
         }
       }
     }
-    const float amax = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
-    if (__builtin_amdgcn_ballot_w64(amax * scale_log2 > m + LAZY_MAX)) {  // wave-uniform, rare after the first step
-      float mx = amax * scale_log2;
+    bool up = false;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) up |= a[k] > thr;
+    if (__builtin_amdgcn_ballot_w64(up)) {  // wave-uniform, rare after the first step
+      const float amax =
+          fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+      float mx = amax * sl2;
       mx = fmaxf(mx, xor_shfl(mx, 16));
       mx = fmaxf(mx, xor_shfl(mx, 32));
       const float mn = fmaxf(m, mx);
       const float alpha = (m == -INFINITY) ? 0.0f : exp2_fast(m - mn);
       m = mn;
+      thr = (m + LAZY_MAX) * inv_sl2;
       l *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) o[i] *= alpha;
@@ -631,17 +652,15 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   // rounded values, so weights and normaliser agree
   auto probs = [&](const float (&a)[8], float m, float& l) {
     const float nm = -m;
-    half8_t pt;
+    half2_t pp[4];
     const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int k = 0; k < 8; k += 2) {
-      const half2_t pp = {(_Float16)exp2_fast(__builtin_fmaf(a[k], scale_log2, nm)),
-                          (_Float16)exp2_fast(__builtin_fmaf(a[k + 1], scale_log2, nm))};
-      pt[k] = pp.x;
-      pt[k + 1] = pp.y;
-      l = __builtin_amdgcn_fdot2(pp, ones, l, false);
+    for (int k = 0; k < 4; ++k) {
+      pp[k] = half2_t{(_Float16)exp2_fast(__builtin_fmaf(a[2 * k], sl2, nm)),
+                      (_Float16)exp2_fast(__builtin_fmaf(a[2 * k + 1], sl2, nm))};
+      l = __builtin_amdgcn_fdot2(pp[k], ones, l, false);
     }
-    return pt;
+    return __builtin_bit_cast(half8_t, pp);
   };
 
   // One step for both row blocks of the wave: every K and V fragment is
@@ -664,8 +683,8 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
       }
     }
     float a0[8], a1[8];
-    prep(acc0, step, lim0, masked, o0, m0, l0, a0);
-    if constexpr (RB == 2) prep(acc1, step, lim1, masked, o1, m1, l1, a1);
+    prep(acc0, step, lim0, masked, o0, m0, l0, thr0, a0);
+    if constexpr (RB == 2) prep(acc1, step, lim1, masked, o1, m1, l1, thr1, a1);
     const half8_t pt0 = probs(a0, m0, l0);
     // lane (n, j) addresses V[4j + n/4][16 i + 4 (n % 4)] of each tile
     const int vofs = (4 * lj + (ln >> 2)) * VROW + (ln & 3) * 8;
@@ -809,52 +828,63 @@ struct PrefillParams {
   const int32_t* ctx_lens;  // [B]: cached tokens, the chunk's own included
   _Float16* out;            // [T][Hq][D]
   const uint32_t* scales;   // int8: this layer's (K, V) fp16 scales [N][Hkv]; else null
-  int Hkv, max_blocks, num_blocks, max_context, qtiles;
+  int Hkv, max_blocks, num_blocks, max_context;
   float scale_log2;
 };
 
 // Causal attention of a chunk of new tokens over the paged cache ([p1] §二
 // and [p2] §1.3: the prompt's tokens are processed together; [p1] §四: tiled
-// with an online softmax, same result). One work-group per (KV head g, query
-// tile, sequence b): a query tile is 128 / G consecutive tokens of the chunk,
-// and its rows are (token, query head of the group), so every K/V tile read
-// is attended by 128 query rows on the matrix cores. Token i of sequence b's
-// chunk sits at logical position ctx - qlen + i and sees tokens 0..itself;
-// the work-group walks tiles 0 .. that of its last token, masking per row.
-// Query tiles are dispatched latest first (they walk the most tiles).
+// with an online softmax, same result). A query tile is 128 / G consecutive
+// tokens of a sequence's chunk, and its rows are (token, query head of the
+// group), so every K/V tile read is attended by 128 query rows on the
+// matrix cores. Token i of sequence b's chunk sits at logical position
+// ctx - qlen + i and sees tokens 0..itself; a query tile walks K/V tiles 0 ..
+// that of its last token, masking per row. Causal tiles differ in length
+// (the last walks the whole context, the first its prefix only), so each
+// work-group (KV head g, pair y, sequence b) takes two of them, the
+// sequence's tile Q - 1 - y and then tile y (Q tiles in all; the middle one
+// alone when Q is odd): every pair walks about the same number of steps, and
+// one round of work-groups holds no long tile that would run on after the
+// others have drained.
 template <int D, int G, bool I8>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
   constexpr int NDB = D / 16;
-  constexpr int QT = PREFIX_ROWS / G;  // query tokens per work-group
-  const int g = blockIdx.x, b = blockIdx.z;
-  const int qt = prm.qtiles - 1 - int(blockIdx.y);
+  constexpr int QT = PREFIX_ROWS / G;  // query tokens per tile
+  const int g = blockIdx.x, y = blockIdx.y, b = blockIdx.z;
   const int Hq = prm.Hkv * G;
   const int t0 = prm.q_start[b], ql = prm.q_start[b + 1] - t0;
   const int n = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
-  const int i0 = qt * QT;
-  if (ql <= 0 || i0 >= ql || ql > n) return;
-  const int cnt = min(QT, ql - i0), R = cnt * G;
-  const int pos0 = n - ql + i0;  // logical position of the tile's first token
-  const int nt = (pos0 + cnt - 1) / BT + 1;
+  if (ql <= 0 || ql > n) return;
+  const int Q = (ql + QT - 1) / QT;
+  if (2 * y >= Q) return;
   const int lj = (threadIdx.x & 63) >> 4;
-  auto qrow = [&](int r) -> const _Float16* {
-    return r < R ? prm.q + (int64_t(t0 + i0 + r / G) * Hq + g * G + r % G) * D : nullptr;
-  };
-  auto limit = [&](int r) { return r < R ? pos0 + r / G + 1 : INT_MAX; };
-  auto emit = [&](int r, const float4_t (&o)[NDB], float, float l) {
-    _Float16* dst = prm.out + (int64_t(t0 + i0 + r / G) * Hq + g * G + r % G) * D + 4 * lj;
+  const int passes = 2 * y + 1 < Q ? 2 : 1;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int i0 = (pass == 0 ? Q - 1 - y : y) * QT;
+    const int cnt = min(QT, ql - i0), R = cnt * G;
+    const int pos0 = n - ql + i0;  // logical position of the tile's first token
+    const int nt = (pos0 + cnt - 1) / BT + 1;
+    auto qrow = [&](int r) -> const _Float16* {
+      return r < R ? prm.q + (int64_t(t0 + i0 + r / G) * Hq + g * G + r % G) * D : nullptr;
+    };
+    auto limit = [&](int r) { return r < R ? pos0 + r / G + 1 : INT_MAX; };
+    auto emit = [&](int r, const float4_t (&o)[NDB], float, float l) {
+      _Float16* dst = prm.out + (int64_t(t0 + i0 + r / G) * Hq + g * G + r % G) * D + 4 * lj;
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-    for (int i = 0; i < NDB; ++i) {
-      half4_t h;
+      for (int i = 0; i < NDB; ++i) {
+        half4_t h;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = (_Float16)(l > 0.0f ? o[i][e] / l : 0.0f);
-      *reinterpret_cast<half4_t*>(dst + 16 * i) = h;
-    }
-  };
-  attend_rows<D, PREFILL_MAX_TILES, true, false, PREFILL_PFS, I8, 2>(prm.K, prm.V, prm.scales, prm.Hkv, g,
-                                                                  prm.num_blocks,
-                                                                  prm.tables + int64_t(b) * prm.max_blocks, 0, nt,
-                                                                  R, n, pos0 + 1, prm.scale_log2, qrow, limit, emit);
+        for (int e = 0; e < 4; ++e) h[e] = (_Float16)(o[i][e] * inv);
+        *reinterpret_cast<half4_t*>(dst + 16 * i) = h;
+      }
+    };
+    if (pass) __syncthreads();  // the first walk's LDS reads are done
+    attend_rows<D, PREFILL_MAX_TILES, true, false, PREFILL_PFS, I8, 2>(prm.K, prm.V, prm.scales, prm.Hkv, g,
+                                                                    prm.num_blocks,
+                                                                    prm.tables + int64_t(b) * prm.max_blocks, 0, nt,
+                                                                    R, n, pos0 + 1, prm.scale_log2, qrow, limit, emit);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2441,7 +2471,8 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", G);
   const int QT = PREFIX_ROWS / G;
   const int qtiles = (max_ql + QT - 1) / QT;
-  if (qtiles > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "chunk too long");
+  const int pairs = (qtiles + 1) / 2;  // each work-group takes a long and a short query tile
+  if (pairs > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "chunk too long");
 
   const int64_t layer_bytes = pkv::layer_elems(c) * pkv::elem_bytes(c.dtype);
   const char* base = static_cast<const char*>(a->pool_dev);
@@ -2460,9 +2491,8 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   prm.max_blocks = a->max_blocks;
   prm.num_blocks = c.num_blocks;
   prm.max_context = a->max_context;
-  prm.qtiles = qtiles;
   prm.scale_log2 = a->scale * LOG2E;
-  hipLaunchKernelGGL(fn, dim3(c.num_kv_heads, qtiles, a->num_seqs), dim3(256), 0, static_cast<hipStream_t>(stream),
+  hipLaunchKernelGGL(fn, dim3(c.num_kv_heads, pairs, a->num_seqs), dim3(256), 0, static_cast<hipStream_t>(stream),
                      prm);
   return hip_status(hipGetLastError(), "paged_prefill launch");
 }

@@ -807,6 +807,29 @@ def test_prefill_past_the_block_id_ring(dtype):
     lib.close()
 
 
+@pytest.mark.parametrize("scale", [-0.0883883, 0.5, -0.5])
+def test_softmax_scale_sign_and_size(scale):
+    """Softmax scales other than 1/sqrt(D), negative ones included: the
+    matrix-core paths (prefill and shared-prefix work-groups) move a negative
+    scale's sign into q, and the lazy running max must still hold every
+    probability within range. Prefill chunks, then a decode step with a
+    shared-prefix plan, against the oracle at the same scale."""
+    w = workloads.prefill_chunks(75, [0, 200], [300, 129], 32, 8, 128)
+    w.softmax_scale = scale
+    lib, o = run_pair(w)
+    err = prefill_err(lib, o)
+    announce(f"prefill scale {scale} max abs err {err:.3g}")
+    assert err <= F16_TOL
+    lib.close()
+    w = workloads.prefix_forest(76, groups=((700, 6),), singles=1, Hq=32, Hkv=8, D=128, suffix=(0, 600))
+    w.softmax_scale = scale
+    lib, o = run_pair(w, prefix_plan={"max_members": 32})
+    err = max_err(lib, o)
+    announce(f"plan decode scale {scale} max abs err {err:.3g}")
+    assert err <= F16_TOL
+    lib.close()
+
+
 def test_prefill_long_prompts_and_physical_order():
     """Two 2048-token prompts (32 q / 8 KV heads, d128) against the oracle,
     and the same result bit for bit under another physical block order."""

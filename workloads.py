@@ -85,10 +85,12 @@ class Workload:
     # int8 workloads: "bulk" = the fp16 K/V are quantised block by block on
     # the host before decode; "append" = every token is quantised on write
     i8_write: str = "bulk"
+    # softmax scale; None: 1 / sqrt(head_dim)
+    softmax_scale: float = None
 
     @property
     def scale(self):
-        return 1.0 / math.sqrt(self.head_dim)
+        return 1.0 / math.sqrt(self.head_dim) if self.softmax_scale is None else self.softmax_scale
 
     @property
     def group(self):
