@@ -337,10 +337,17 @@ def main():
                 launch(layer, 0, None, cap, stream_handle=cs)
         torch.cuda.synchronize()
 
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K + 1)]
+
     def graph_step(i, events=None):
         lh = prepare(i)
         launch(0, i, lh, int(lh.max()), events)
+        j = i - (W + 1)  # timed step index (the untimed step's events are overwritten)
+        if 0 <= j < K:
+            gev[j][0].record()
         graph.replay()
+        if 0 <= j < K:
+            gev[j][1].record()
 
     step_fn = eager_step if graph is None else graph_step
     step_fn(W)  # one untimed step in the timed mode (first graph replay)
@@ -449,6 +456,11 @@ def main():
                                     round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
         "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2) if merged else None,
         "decode_a5_a6": decode_metric(split_ms, merge_ms, split_bytes),
+        # graph layers: the decode with its fused append and the merge, sized
+        # for the table width (no host lengths)
+        "decode_a4_a5_a6_graph": None if graph is None else graph_layer_metric(
+            np.array([a.elapsed_time(b) for a, b in gev[:K]]) / (L - 1),
+            split_bytes + append_bytes, L - 1),
         "append_kernel_us": append_us,
         "timed_launch_samples": int(len(split_ms)),
         "execution": ("per step: host slot reservation and table packing, table upload, layer 0 "
@@ -490,6 +502,19 @@ def decode_metric(split_ms, merge_ms, bytes_per_launch):
     return {"median_us": round(med * 1e3, 2), "p10_us": round(float(np.percentile(both, 10)) * 1e3, 2),
             "p90_us": round(float(np.percentile(both, 90)) * 1e3, 2), "GBps": round(gbps, 1),
             "frac": round(gbps / PEAK_HBM_GBPS, 4), "samples": int(len(both))}
+
+
+def graph_layer_metric(layer_ms, bytes_per_layer, layers):
+    """The same launches as they run back to back in a step: per timed step,
+    one HIP-event pair around the replay of the graph of `layers` layers
+    (each layer's launches and nothing else), divided by `layers`; median
+    and p10/p90 in µs, and the algorithmic bytes of one layer over the
+    median as GB/s and as a fraction of the 8 TB/s peak."""
+    med = float(np.median(layer_ms))
+    gbps = float(np.mean(bytes_per_layer)) / (med * 1e-3) / 1e9
+    return {"median_us": round(med * 1e3, 2), "p10_us": round(float(np.percentile(layer_ms, 10)) * 1e3, 2),
+            "p90_us": round(float(np.percentile(layer_ms, 90)) * 1e3, 2), "GBps": round(gbps, 1),
+            "frac": round(gbps / PEAK_HBM_GBPS, 4), "layers_per_replay": layers, "samples": int(len(layer_ms))}
 
 
 def time_append(torch, C, lib, cache, dev, sp, K, knew, vnew, seq_arr, max_blocks):
@@ -632,14 +657,18 @@ def decode_only_bench(args, torch, pkv, C, lens, hq, hkv, dtype, free_order, see
     graph.replay()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     with no_collections():
         t0.record()
         for i in range(K):
             launch(0, keep[i])
+            gev[i][0].record()
             graph.replay()
+            gev[i][1].record()
         t1.record()
         torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / K
+    layer_ms = np.array([a.elapsed_time(b) for a, b in gev]) / (L - 1)
     check = [1, L // 2, L - 1] if L > 2 else list(range(1, L))
     got = {l: out[l].clone() for l in check}
     for l in check:
@@ -673,6 +702,7 @@ def decode_only_bench(args, torch, pkv, C, lens, hq, hkv, dtype, free_order, see
                                     round(float(np.percentile(split_ms, 90)) * 1e3, 2)],
         "merge_kernel_us": round(float(np.mean(merge_ms)) * 1e3, 2) if merged else None,
         "decode_a5_a6": decode_metric(split_ms, merge_ms if merged else None, [kernel_bytes]),
+        "decode_a5_a6_graph": graph_layer_metric(layer_ms, [kernel_bytes], L - 1),
         "graph_matches_eager_bitwise": same,
         "roofline": {"bound": "hbm", "kernel": f"paged_decode_kernel<128,{G},{dtype}> (split-K decode)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
