@@ -421,6 +421,23 @@ __device__ __forceinline__ void seq_prefix(const int32_t* plan, int b, int max_b
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's bytes land at lds + 16 l (lds
+// wave-uniform; checked on gfx950 with an in-bounds one-wave probe). Written
+// as asm so that the compiler, which cannot tell which LDS bytes such a load
+// writes, does not wait for every one in flight before each LDS read; the
+// caller orders them itself: vmcnt waits (loads complete in order) before
+// the barrier that hands the bytes to other waves, and before any reuse of
+// the LDS. It has no register outputs; its address is read at issue.
+__device__ __forceinline__ void lds_load16(const char* src, const char* lds) {
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)lds));
+  __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                       :
+                       : "s"(m0), "v"(src)
+                       : "memory", "m0");
+}
+
 // Attention of up to 128 query rows over consecutive tiles of one block
 // table, by a work-group of 4 waves on the matrix cores: the shared-prefix
 // work-groups of the decode and the paged prefill both run it. Rows come in
@@ -450,8 +467,9 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 //       8j..8j+7 of lane (n, j) are tokens 4j..4j+3 of the first tile and
 //       then of the second: exactly the scores the lane holds, so P goes from
 //       one MFMA to the next without moving between lanes.
-// K and V tiles are both staged in LDS row-major (rows padded by 16 bytes,
-// 16-byte stores). The V^T operand comes from the LDS transpose read
+// K and V tiles are both staged in LDS row-major: padded rows written from
+// a register ring of loads, or (the DMA mode below) unpadded, swizzled rows
+// loaded straight into LDS. The V^T operand comes from the LDS transpose read
 // ds_read_b64_tr_b16: within each 16-lane group, lane s addresses 4
 // halves and lane i receives element i % 4 of lanes i/4, 4 + i/4, 8 + i/4
 // and 12 + i/4 (checked on gfx950 with a one-wave probe). With lane s of
@@ -475,8 +493,18 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   constexpr int TILE = BT * D * E;      // pool bytes per (block, KV head) tile
   // PFS: steps (tile pairs) in flight per thread
   static_assert(PFS % 2 == 0, "LDS stages alternate with the ring slot");
-  __shared__ __align__(16) char kst[2][2][BT * KROW];
-  __shared__ __align__(16) char vst[2][2][BT * VROW];
+  // DMA (fp16 d128, two row blocks per wave: the paged prefill): tiles go
+  // from HBM straight into LDS (global_load_lds, 16 bytes per lane), three
+  // stages of a step's two K and two V tiles,
+  // unpadded, each row's 16-byte pieces XOR-swizzled by the row index so
+  // that 16 lanes reading one piece of 16 rows (K) or 4 rows (the V
+  // transpose read) hit distinct banks. Otherwise tiles are loaded into a
+  // register ring and stored to two padded LDS stages.
+  constexpr bool DMA = !I8 && D == 128 && RB == 2;
+  constexpr int TB = BT * D * 2;  // bytes per staged fp16 tile
+  __shared__ __align__(16) char dma_st[DMA ? 3 : 1][DMA ? 4 * TB : 16];
+  __shared__ __align__(16) char kst[DMA ? 1 : 2][2][DMA ? 16 : BT * KROW];
+  __shared__ __align__(16) char vst[DMA ? 1 : 2][2][DMA ? 16 : BT * VROW];
   __shared__ int blk_ids[MAXT];
   __shared__ uint32_t tile_sc[I8 ? MAXT : 1];  // int8: each tile's (K, V) fp16 scales
   constexpr int REFILL = 256;  // ids per refill: one per thread
@@ -498,7 +526,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   // read (MAXT - REFILL) / 2 steps later, after the barrier that ends this
   // step. Uniform over the work-group; never taken when nt <= MAXT.
   auto refill = [&](int it) {
-    const int T0 = 2 * (it + 2 + PFS);
+    const int T0 = 2 * (it + (DMA ? 3 : 2 + PFS));  // DMA: the loads of step it + 2 are issued
     if (T0 % REFILL == 0 && T0 - REFILL + MAXT < nt) {
       const int t = T0 - REFILL + MAXT + tid;
       if (t < nt) stage_id(t);
@@ -604,6 +632,54 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
     }
   };
 
+  // DMA staging: lane l of wave w moves row 4 w + l / 16 of a tile, its
+  // 16 bytes landing at LDS slot l % 16 of that row; it loads the tile's
+  // piece (l % 16) ^ row, so slot s of row r holds piece s ^ r.
+  const int drow = 4 * wave + (lane >> 4);
+  const int dofs = drow * (D * 2) + (((lane & 15) ^ drow) << 4);
+  auto dma_tile = [&](int st, int k) { return dma_st[st] + k * TB; };  // k: K0, K1, V0, V1
+  auto dma_step = [&](int st, int step) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int blk = blk_ids[min(2 * step + sub, nt - 1) % MAXT];
+      const int safe = unsigned(blk) < unsigned(num_blocks) ? blk : 0;
+      const int64_t base = (int64_t(safe) * Hkv + g) * TILE + dofs;
+      lds_load16(Kc + base, dma_tile(st, sub) + 1024 * wave);
+      lds_load16(Vc + base, dma_tile(st, 2 + sub) + 1024 * wave);
+    }
+  };
+  // after this wave's loads of `step` have landed: V rows at or past nvalid
+  // in the tile that holds the end of the written tokens become zeros
+  // (each lane rewrites the 16 bytes its own load wrote)
+  auto dma_zero_tail = [&](int st, int step) {
+    if constexpr (MASK) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int room = nvalid - (jb + 2 * step + sub) * BT;
+        if (room < BT && drow >= room)
+          *reinterpret_cast<uint4*>(dma_tile(st, 2 + sub) + 1024 * wave + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  // wait until at most n of this wave's vector-memory loads are in flight
+  // (loads complete in order); vmcnt(n), expcnt and lgkmcnt not waited on
+  auto wait_loads = [](auto n) {
+    static_assert(decltype(n)::value >= 0 && decltype(n)::value < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | decltype(n)::value);
+  };
+  // The step barrier of the DMA loop: this wave's LDS accesses done
+  // (lgkmcnt(0)) and all but the newest step's four tile loads landed
+  // (vmcnt(4)), then s_barrier. A __syncthreads() would also wait for the
+  // newest loads (its work-group fence covers the LDS they write), which
+  // would leave no load in flight across the barrier. The empty asm keeps
+  // the compiler from moving memory accesses across it.
+  auto dma_barrier = []() {
+    __builtin_amdgcn_s_waitcnt(0x0074);
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+  };
+
   // Online softmax of one row block's scores of a step (two tiles), kept
   // short because the VALU, not the matrix cores, sets this loop's pace, and
   // split in two so the exponentials of one row block can issue beside the
@@ -677,7 +753,9 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
       acc1[sub] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const half8_t ka = *reinterpret_cast<const half8_t*>(kst[st][sub] + ln * KROW + (32 * c + 8 * lj) * 2);
+        const char* kp = DMA ? dma_tile(st, sub) + ln * (D * 2) + (((4 * c + lj) ^ ln) << 4)
+                             : kst[DMA ? 0 : st][sub] + ln * KROW + (32 * c + 8 * lj) * 2;
+        const half8_t ka = *reinterpret_cast<const half8_t*>(kp);
         acc0[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q0[c], acc0[sub], 0, 0, 0);
         if constexpr (RB == 2) acc1[sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, q1[c], acc1[sub], 0, 0, 0);
       }
@@ -686,15 +764,35 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
     prep(acc0, step, lim0, masked, o0, m0, l0, thr0, a0);
     if constexpr (RB == 2) prep(acc1, step, lim1, masked, o1, m1, l1, thr1, a1);
     const half8_t pt0 = probs(a0, m0, l0);
+    if constexpr (DMA) {
+      // lane (n, j) addresses V[4j + n/4][16 i + 4 (n % 4)] of each tile:
+      // piece 2 i + (n % 4) / 2 of row 4j + n/4, half (n % 2) of it; both
+      // row blocks' probabilities first, so each V fragment is used by the
+      // two MFMAs right after its read (no registers hold all of them)
+      const half8_t pt1 = RB == 2 ? probs(a1, m1, l1) : pt0;
+      const int vr = 4 * lj + (ln >> 2);
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) {
+        const int vofs = vr * (D * 2) + (((2 * i + ((ln >> 1) & 1)) ^ vr) << 4) + 8 * (ln & 1);
+        const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(dma_tile(st, 2) + vofs));
+        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(dma_tile(st, 3) + vofs));
+        const half8_t va = __builtin_bit_cast(half8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt0, o0[i], 0, 0, 0);
+        if constexpr (RB == 2) o1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt1, o1[i], 0, 0, 0);
+      }
+      return;
+    }
     // lane (n, j) addresses V[4j + n/4][16 i + 4 (n % 4)] of each tile
     const int vofs = (4 * lj + (ln >> 2)) * VROW + (ln & 3) * 8;
     half8_t va[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) {
       const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) short4_t*)(vst[st][0] + vofs + 32 * i));
+          (__attribute__((address_space(3))) short4_t*)(vst[DMA ? 0 : st][0] + vofs + 32 * i));
       const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) short4_t*)(vst[st][1] + vofs + 32 * i));
+          (__attribute__((address_space(3))) short4_t*)(vst[DMA ? 0 : st][1] + vofs + 32 * i));
       va[i] = __builtin_bit_cast(half8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       o0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[i], pt0, o0[i], 0, 0, 0);
     }
@@ -713,7 +811,43 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
     }
   };
 
+  // steps with both tiles real and every token visible to every row
+  int nfree = nt / 2;
+  if (MASK) nfree = min(nfree, max(0, (full_tokens / BT - jb) / 2));
+
   __syncthreads();  // block ids
+  if constexpr (DMA) {
+    // Step s sits in LDS stage s % 3. Iteration it: the math of step it
+    // (stage it % 3), the loads of step it + 2 into stage (it + 2) % 3 --
+    // last read in iteration it - 1, which a barrier ended -- and, once this
+    // wave's loads of step it + 1 have landed (only step it + 2's four may
+    // still be in flight), the barrier that hands stage (it + 1) % 3 to all
+    // waves. A loop runs rounds of three steps (unrolled, so every stage is
+    // a constant); past its last step only the math is skipped.
+    dma_step(0, 0);
+    dma_step(1, 1);
+    wait_loads(std::integral_constant<int, 4>{});
+    dma_zero_tail(0, 0);
+    dma_barrier();
+    auto run3 = [&](int from, int to, auto masked) {
+      for (int it0 = from; it0 < to; it0 += 3) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          const int it = it0 + u;
+          if (it < to) step_rows(u, it, masked);
+          dma_step((u + 2) % 3, it + 2);
+          refill(it);
+          wait_loads(std::integral_constant<int, 4>{});
+          dma_zero_tail((u + 1) % 3, it + 1);
+          dma_barrier();
+        }
+      }
+    };
+    nfree -= nfree % 3;
+    run3(0, nfree, std::false_type{});
+    run3(nfree, nsteps, std::true_type{});
+    wait_loads(std::integral_constant<int, 0>{});  // the last loads (past the end) land before the LDS is reused
+  } else {
 #pragma unroll
   for (int u = 0; u < PFS; ++u) gload(u, ring[u]);
   lstore(0, ring[0], 0);
@@ -741,12 +875,10 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
       }
     }
   };
-  // steps with both tiles real and every token visible to every row
-  int nfree = nt / 2;
-  if (MASK) nfree = min(nfree, max(0, (full_tokens / BT - jb) / 2));
   nfree -= nfree % PFS;
   run(0, nfree, std::false_type{});
   run(nfree, nsteps, std::true_type{});
+  }
 
   // the row sums over the four token groups
   l0 += xor_shfl(l0, 16);
