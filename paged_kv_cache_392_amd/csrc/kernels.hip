@@ -2125,10 +2125,13 @@ int64_t workspace_bytes_for(const pkv_config& c, int B, int Hq, int max_parts) {
 constexpr int PREFIX_TARGET_WGS = 128;
 // With the plan's host copy the launch knows each group's shared blocks and
 // cuts the longest run into partitions of about this many blocks (at most
-// as many as the workspace holds): 32 sequences over a 2048-token prefix
-// 25.8 -> 23.7-24.5 us at 16-22 blocks, one 4096-token prefix 26.9 -> 25.7
-// at 32, two 3000-token prefixes best at 32.
-constexpr int PREFIX_PART_BLOCKS = 28;
+// as many as the workspace holds). Measured on MI355X with the rows split
+// over two work-groups and the stream-K split side, 32 sequences over a
+// 2048-token prefix (128 shared blocks): 4 partitions of 32 blocks 22.1 us
+// per launch, 5 of 26 22.7, 7 of 19 24.4, 10 of 13 27.4, 2 of 64 30.1, one
+// of 128 46.6; one 4096-token prefix and two 3000-token prefixes were best
+// at 32 blocks as well.
+constexpr int PREFIX_PART_BLOCKS = 32;
 int prefix_partitions(int Hkv, int n_groups, int max_blocks) {
   const int64_t lo = (int64_t(max_blocks) + 63) / 64;  // <= 64 blocks: the block ids staged in LDS
   const int64_t hi = std::max<int64_t>(lo, (max_blocks + 15) / 16);
