@@ -565,6 +565,12 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
     o1[i] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
   }
   float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.0f, l1 = 0.0f, thr0 = -INFINITY, thr1 = -INFINITY;
+  // DMA mode: the row sums on the matrix cores, P^T against an all-ones
+  // operand (every element of ls is the row's sum); otherwise v_dot2 sums
+  // per lane, reduced over the four token groups at the end
+  float4_t ls0 = {0.0f, 0.0f, 0.0f, 0.0f}, ls1 = {0.0f, 0.0f, 0.0f, 0.0f};
+  const half8_t ones8 = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                         (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 
   // Tile staging: a tile is 2 x LOADERS 16-byte pieces (K, then V), each
   // piece along a row; thread t moves pieces t + 256 j (int8 at D = 64: only
@@ -690,7 +696,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   // exponential, row sums of the fp16 probabilities by v_dot2 against ones;
   // returns P in the value MFMA's k-slot order.
   auto prep = [&](const float4_t (&acc)[2], int step, int lim, auto masked, float4_t (&o)[NDB], float& m,
-                  float& l, float& thr, float (&a)[8]) {
+                  float& l, float& thr, float4_t& ls, float (&a)[8]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -719,7 +725,10 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
       const float alpha = (m == -INFINITY) ? 0.0f : exp2_fast(m - mn);
       m = mn;
       thr = (m + LAZY_MAX) * inv_sl2;
-      l *= alpha;
+      if constexpr (DMA)
+        ls *= alpha;
+      else
+        l *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) o[i] *= alpha;
     }
@@ -734,7 +743,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
     for (int k = 0; k < 4; ++k) {
       pp[k] = half2_t{(_Float16)exp2_fast(__builtin_fmaf(a[2 * k], sl2, nm)),
                       (_Float16)exp2_fast(__builtin_fmaf(a[2 * k + 1], sl2, nm))};
-      l = __builtin_amdgcn_fdot2(pp[k], ones, l, false);
+      if constexpr (!DMA) l = __builtin_amdgcn_fdot2(pp[k], ones, l, false);
     }
     return __builtin_bit_cast(half8_t, pp);
   };
@@ -761,8 +770,8 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
       }
     }
     float a0[8], a1[8];
-    prep(acc0, step, lim0, masked, o0, m0, l0, thr0, a0);
-    if constexpr (RB == 2) prep(acc1, step, lim1, masked, o1, m1, l1, thr1, a1);
+    prep(acc0, step, lim0, masked, o0, m0, l0, thr0, ls0, a0);
+    if constexpr (RB == 2) prep(acc1, step, lim1, masked, o1, m1, l1, thr1, ls1, a1);
     const half8_t pt0 = probs(a0, m0, l0);
     if constexpr (DMA) {
       // lane (n, j) addresses V[4j + n/4][16 i + 4 (n % 4)] of each tile:
@@ -782,6 +791,8 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
         o0[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt0, o0[i], 0, 0, 0);
         if constexpr (RB == 2) o1[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pt1, o1[i], 0, 0, 0);
       }
+      ls0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, pt0, ls0, 0, 0, 0);
+      if constexpr (RB == 2) ls1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, pt1, ls1, 0, 0, 0);
       return;
     }
     // lane (n, j) addresses V[4j + n/4][16 i + 4 (n % 4)] of each tile
@@ -881,14 +892,20 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   }
 
   // the row sums over the four token groups
-  l0 += xor_shfl(l0, 16);
-  l0 += xor_shfl(l0, 32);
-  if (has0 && rb0 * 16 + ln < R) emit(rb0 * 16 + ln, o0, m0, l0);
-  if constexpr (RB == 2) {
-    l1 += xor_shfl(l1, 16);
-    l1 += xor_shfl(l1, 32);
-    if (has1 && rb1 * 16 + ln < R) emit(rb1 * 16 + ln, o1, m1, l1);
+  if constexpr (DMA) {
+    l0 = ls0[0];
+    l1 = ls1[0];
+  } else {
+    l0 += xor_shfl(l0, 16);
+    l0 += xor_shfl(l0, 32);
+    if constexpr (RB == 2) {
+      l1 += xor_shfl(l1, 16);
+      l1 += xor_shfl(l1, 32);
+    }
   }
+  if (has0 && rb0 * 16 + ln < R) emit(rb0 * 16 + ln, o0, m0, l0);
+  if constexpr (RB == 2)
+    if (has1 && rb1 * 16 + ln < R) emit(rb1 * 16 + ln, o1, m1, l1);
 }
 
 // The shared-prefix role of a decode work-group: KV head g, partition `part`
