@@ -807,6 +807,27 @@ def test_prefill_past_the_block_id_ring(dtype):
     lib.close()
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_prefill_random_chunks(case):
+    """Seeded random prefill batches on fp16 d128 pools (the kernel's
+    direct-to-LDS path): 1-4 sequences, each a chunk of 1-700 tokens after
+    0-2500 cached ones, group sizes 1, 2, 4 and 8, so walks end in partial
+    tiles, odd tile counts and pairs of query tiles of every length."""
+    rng = np.random.default_rng(900 + case)
+    n = int(rng.integers(1, 5))
+    cached = [int(x) for x in rng.integers(0, 2501, n)]
+    chunk = [int(x) for x in rng.integers(1, 701, n)]
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    w = workloads.prefill_chunks(950 + case, cached, chunk, G * Hkv, Hkv, 128)
+    lib, o = run_pair(w)
+    check_host_records(lib, o)
+    err = prefill_err(lib, o)
+    announce(f"random prefill {n} seqs cached={cached} chunk={chunk} G={G} Hkv={Hkv}: max abs err {err:.3g}")
+    assert err <= F16_TOL
+    lib.close()
+
+
 @pytest.mark.parametrize("scale", [-0.0883883, 0.5, -0.5])
 def test_softmax_scale_sign_and_size(scale):
     """Softmax scales other than 1/sqrt(D), negative ones included: the
