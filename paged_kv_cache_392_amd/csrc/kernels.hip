@@ -586,10 +586,24 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
     lrow = pc / PIECES;
     lpc = pc % PIECES;
   };
+  // Block id of tile t (past the last tile: the last tile's) for the loads.
+  // The ids of 64 consecutive tiles (wb .. wb + 63) sit one per lane in idw
+  // and are taken with readlane, so the loads of a step wait for no LDS read
+  // of their ids; idw is refreshed from the ring every 32 steps (tiles only
+  // grow, and those read are staged long before).
+  int wb = -64, idw = -1;
+  auto tile_block = [&](int t) {
+    t = min(t, nt - 1);
+    if (t >= wb + 64) {  // wave-uniform
+      wb = t & ~63;
+      idw = blk_ids[(wb + lane) % MAXT];
+    }
+    return __builtin_amdgcn_readlane(idw, t - wb);
+  };
   auto gload = [&](int step, uint4 (&r)[2][NLD]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const int blk = blk_ids[min(2 * step + sub, nt - 1) % MAXT];
+      const int blk = tile_block(2 * step + sub);
       const int safe = unsigned(blk) < unsigned(num_blocks) ? blk : 0;
       const int64_t base = (int64_t(safe) * Hkv + g) * TILE;
 #pragma unroll
@@ -647,7 +661,7 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   auto dma_step = [&](int st, int step) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const int blk = blk_ids[min(2 * step + sub, nt - 1) % MAXT];
+      const int blk = tile_block(2 * step + sub);
       const int safe = unsigned(blk) < unsigned(num_blocks) ? blk : 0;
       const int64_t base = (int64_t(safe) * Hkv + g) * TILE + dofs;
       lds_load16(Kc + base, dma_tile(st, sub) + 1024 * wave);
