@@ -302,6 +302,7 @@ struct DecodeParams {
   int max_context;
   float scale_log2;  // softmax scale * log2(e)
   int num_seqs;
+  int stream_pad;    // stream-K split: blocks of start-up cost charged ahead of each sequence's span
 };
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int max_context) {
@@ -311,6 +312,14 @@ __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int max_contex
 // Sequences a stream-K split can lay end to end (each work-group scans the
 // partition counts of all of them).
 constexpr int STREAM_MAX_SEQS = 1024;
+// Start-up charge of a sequence's piece in a stream-K run, in blocks (int8
+// blocks carry half the bytes, so twice as many). Measured on MI355X, split
+// kernel us at a charge of 0 / 4 / 8 / 12 fp16 blocks (0 / 8 / 16 / 24
+// int8): the continuous-batching mix 51.7 / 51.1 / 50.8 / 51.0, ragged int8
+// 16 x U[128, 8192] (seed 7) 35.6 / 33.5 / 32.1 / 32.1; the shared-prefix
+// launch 22.1 at every charge.
+constexpr int STREAM_PAD_F16 = 8;
+constexpr int STREAM_PAD_I8 = 16;
 
 // Exclusive prefix sum of v over the 256 threads of a work-group (thread
 // order), and the work-group's total. part: WAVES ints of LDS. Every thread
@@ -1600,14 +1609,16 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& prm, int g, i
 }
 
 // Stream-K split (ragged batches with host lengths, no plan). The blocks of
-// all sequences, laid end to end (sequence 0's, then 1's, ...), are cut into
-// runs of q = prm.part_blocks blocks, one per work-group of a KV head:
-// work-group k covers blocks [k q, (k + 1) q), which may end one sequence and
-// start the next. Each piece of a sequence it covers is a segment with its
-// own partial, in slot k - floor(C_b / q) of the sequence's partial rows
-// (C_b: the sequence's first block in the run); a sequence that one
-// work-group covers entirely gets its final rows from it. Every sequence's
-// first block C_b comes from a work-group-wide scan of all lengths. Sequences
+// all sequences, laid end to end (sequence 0's, then 1's, ...), each span
+// led by prm.stream_pad blocks that stand for the start-up of a piece and
+// hold no work, are cut into runs of q = prm.part_blocks blocks, one per
+// work-group of a KV head: work-group k covers [k q, (k + 1) q), which may
+// end one sequence and start the next (and then holds fewer real blocks).
+// Each piece of a sequence it covers is a segment with its own partial, in
+// slot k - floor(C_b / q) of the sequence's partial rows (C_b: the
+// sequence's first real block in the run); a sequence that one work-group
+// covers entirely gets its final rows from it. Every sequence's C_b comes
+// from a work-group-wide scan of all lengths. Sequences
 // without tokens are skipped (the host rejects them when it has the lengths).
 // With a shared-prefix plan a grouped sequence's span starts after its
 // shared blocks, and its partials follow the group's prefix partials.
@@ -1629,6 +1640,7 @@ __device__ __forceinline__ void stream_k_role(const DecodeParams& prm, int g, in
     int sb = 0, pre;
     if (PLAN && t < B) seq_prefix(prm.plan, t, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
     n[i] = c[i] > 0 ? max((c[i] + BT - 1) / BT - sb, 0) : 0;  // the span after the shared blocks
+    n[i] += n[i] > 0 ? prm.stream_pad : 0;                   // and its start-up charge ahead of it
   }
   int carry = 0;
 #pragma unroll
@@ -1656,8 +1668,9 @@ __device__ __forceinline__ void stream_k_role(const DecodeParams& prm, int g, in
     else r = m;
   }
   for (;;) {
-    const int cb = seq_first[b], cn = seq_first[b + 1];
-    if (cn > cb) {
+    // sequence b's real blocks: [cb, cn), after its start-up charge
+    const int cn = seq_first[b + 1], cb = min(seq_first[b] + prm.stream_pad, cn);
+    if (cn > cb && hi > cb) {
       int sb = 0, pre = 0;  // a grouped sequence's span starts after its shared blocks; its prefix partials first
       if constexpr (PLAN) seq_prefix(prm.plan, b, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
       const int s0 = max(lo, cb) - cb, s1 = min(hi, cn) - cb;
@@ -1775,6 +1788,7 @@ struct MergeParams {
   int row_parts;  // partials any row of this launch can hold (<= max_parts)
   int num_seqs;
   int stream_q;   // stream-K split: blocks per work-group (0 = partitions of part_blocks per sequence)
+  int stream_pad;  // stream-K split: start-up charge ahead of each span (as in DecodeParams)
 };
 
 // Stream-K split: the blocks sequence b's span (its blocks after any shared
@@ -1787,9 +1801,15 @@ __device__ __forceinline__ int span_blocks(const MergeParams& prm, int t) {
   seq_prefix(prm.plan, t, prm.max_blocks, prm.num_groups, prm.prefix_pp, sb, pre);
   return c > 0 ? max((c + BT - 1) / BT - sb, 0) : 0;
 }
+// the span's length in the run: its blocks and, when it has any, the
+// start-up charge laid ahead of them
+__device__ __forceinline__ int run_blocks(const MergeParams& prm, int t) {
+  const int n = span_blocks(prm, t);
+  return n > 0 ? n + prm.stream_pad : 0;
+}
 __device__ __forceinline__ int run_first_block(const MergeParams& prm, int b, int tid, int nthreads, int* red) {
   int sum = 0;
-  for (int t = tid; t < b; t += nthreads) sum += span_blocks(prm, t);
+  for (int t = tid; t < b; t += nthreads) sum += run_blocks(prm, t);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) sum += __shfl_xor(sum, m, 64);
   const int wave = tid >> 6, waves = (nthreads + 63) >> 6;
@@ -1851,7 +1871,7 @@ __global__ __launch_bounds__(1024) void lse_reduce_kernel(MergeParams prm) {
   int nparts;
   if (prm.stream_q > 0) {  // the stream-K work-groups that covered the sequence's span, in order
     __shared__ int red[16];
-    const int cb = run_first_block(prm, b, d + D * w, D * W, red);
+    const int cb = run_first_block(prm, b, d + D * w, D * W, red) + prm.stream_pad;  // first real block
     const int span = ctx > 0 ? max(nblk - sb, 0) : 0;
     nparts = span > 0 ? (cb + span - 1) / prm.stream_q - cb / prm.stream_q + 1 : 0;
   } else {
@@ -1972,6 +1992,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 // 16-sequence 8K batch on one KV head: 20.5 us at 80 tokens, 14.4 at 512).
 // The partitions of the longest sequence are then made equal.
 constexpr int MIN_PART_BLOCKS = 16;
+// Stream-K split: blocks of work charged for starting a sequence's piece.
+// A work-group that crosses into the next sequence pays that piece's
+// start-up (its block ids and q, the first tiles' latency, and the wave
+// merge and partial write of the piece before): charging it as blocks laid
+// ahead of every span gives such work-groups fewer real blocks.
+int stream_pad_blocks(int dtype) { return dtype == PKV_I8 ? STREAM_PAD_I8 : STREAM_PAD_F16; }
+
 int choose_part_blocks(int Hkv, int B, int max_context, int partition_tokens, int64_t want_wgs) {
   if (partition_tokens == 0) {
     if (const char* env = std::getenv("PKV_PARTITION_TOKENS")) partition_tokens = std::atoi(env);
@@ -2455,11 +2482,12 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
       const int pbp = (sb + pp - 1) / pp;
       return (sb + pbp - 1) / pbp;
     };
+    const int pad = stream_pad_blocks(c.dtype);
     int64_t pairs = 0, T = 0;
     for (int b = 0; b < a->num_seqs; ++b) {
       const int64_t nb = std::max<int64_t>((std::min<int64_t>(a->ctx_lens_host[b], cap) + BT - 1) / BT - shared(b), 0);
       pairs += (nb + pb - 1) / pb;
-      T += nb;
+      T += nb > 0 ? nb + pad : 0;
     }
     if ((plan || pairs < int64_t(a->num_seqs) * gparts) && T > 0) {
       const Residency res = resident_wgs(reinterpret_cast<const void*>(fn),
@@ -2467,13 +2495,15 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
       const int64_t slots_h = std::max<int64_t>(1, res.slots / c.num_kv_heads - units);
       int64_t q = (T + slots_h - 1) / slots_h;
       q = std::min<int64_t>(std::max<int64_t>(q, MIN_PART_BLOCKS), MAX_PARTITION_TOKENS / BT);
-      int64_t cb = 0;
+      int64_t cb = 0;  // where sequence b's charge starts in the run
       int rows_max = 0;
       for (int b = 0; b < a->num_seqs; ++b) {
         const int64_t nb =
             std::max<int64_t>((std::min<int64_t>(a->ctx_lens_host[b], cap) + BT - 1) / BT - shared(b), 0);
-        if (nb > 0) rows_max = std::max<int>(rows_max, pre_parts(b) + int((cb + nb - 1) / q - cb / q + 1));
-        cb += nb;
+        if (nb == 0) continue;
+        const int64_t first = cb + pad;  // its first real block
+        rows_max = std::max<int>(rows_max, pre_parts(b) + int((first + nb - 1) / q - first / q + 1));
+        cb = first + nb;
       }
       if (rows_max <= mp && (T + q - 1) / q + units <= int64_t(65535) * 65535) {
         stream_k = true;
@@ -2519,6 +2549,7 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
   prm.scale_log2 = a->scale * LOG2E;
   prm.num_seqs = a->num_seqs;
   prm.plan_stream = plan && stream_k ? 1 : 0;
+  prm.stream_pad = stream_k ? stream_pad_blocks(c.dtype) : 0;
   if (stream_k && !plan) fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, GRID_STREAM);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -2556,6 +2587,7 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
   mg.row_parts = stream_k ? stream_rows : std::min(mp, (plan ? pp : 0) + gparts);
   mg.num_seqs = a->num_seqs;
   mg.stream_q = stream_k ? pb : 0;
+  mg.stream_pad = prm.stream_pad;
   const dim3 rgrid(a->num_q_heads, a->num_seqs);
   const int ways = merge_ways(mg.row_parts);
   if (ev[2] && ev[3])
