@@ -384,6 +384,19 @@ def test_stream_k_split_matches_oracle_and_plain_grid(seed, B, max_len, hq, hkv)
     lib.close()
 
 
+@pytest.mark.parametrize("dtype,D", [("f16", 128), ("i8", 128), ("f16", 64)])
+def test_stream_k_runs_through_start_up_charges(dtype, D):
+    """Many short sequences (1..7 blocks) beside the start-up charge laid
+    ahead of each span (8 blocks, int8 16): runs begin and end inside
+    charges, so work-groups cover charges of sequences they hold no block
+    of, and most sequences are split over two work-groups or held whole by
+    one. Against the oracle, fp16 and int8."""
+    w = workloads.tiny_random(2005, B=200, Hq=8, Hkv=2, D=D, max_len=100, dtype=dtype)
+    lib, o = run_pair(w)
+    assert max_err(lib, o) <= (F16_TOL if dtype == "f16" else I8_TOL)
+    lib.close()
+
+
 def test_run_to_run_bitwise_determinism():
     w = workloads.tiny_random(1002, B=4, Hq=32, Hkv=8, D=128, max_len=3000)
     announce("determinism")
