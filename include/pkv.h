@@ -376,12 +376,14 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * ctx_lens_host, automatic partitions, no shared-prefix plan and at most 1024
  * sequences, a ragged batch (one whose grid of (sequence, partition) slots
  * at max_context would hold slots past some sequence's last partition) is
- * split stream-K: all sequences' blocks laid end to end are cut into equal
- * runs, about one round of resident work-groups, a run possibly ending one
- * sequence and starting the next, and each sequence's pieces are merged in
- * order. ctx_lens_host must then equal the device lengths (a mismatch gives
- * wrong output for the sequences it misstates, never an access out of
- * bounds).
+ * split stream-K: all sequences' blocks laid end to end, each sequence's
+ * led by a few blocks' worth of start-up charge that hold no work, are cut
+ * into equal runs, about one round of resident work-groups, a run possibly
+ * ending one sequence and starting the next (and then holding fewer real
+ * blocks), and each sequence's pieces are merged in order. ctx_lens_host
+ * must then equal the device lengths (a mismatch gives wrong output for the
+ * sequences it misstates and possibly for those after them, never an
+ * access out of bounds).
  * Accumulation is fp32 and
  * the output is rounded to fp16 (nearest even). The result depends only on
  * logical token order, not on physical block ids, and is bitwise
@@ -393,9 +395,9 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * contents after the call unspecified). Calls sharing one workspace must be
  * ordered on one stream.
  *
- * With a shared-prefix plan (prefix_plan_dev, prefix_groups > 0; fp16
- * pools), extra work-groups of the same launch attend every group's members
- * to the group's shared blocks, reading each K/V tile once for up to 128
+ * With a shared-prefix plan (prefix_plan_dev, prefix_groups > 0), extra
+ * work-groups of the same launch attend every group's members to the
+ * group's shared blocks, reading each K/V tile once for up to 128
  * query rows on the matrix cores; the split work-groups cover each grouped
  * sequence from its first unshared block, and the merge combines prefix and
  * suffix partials in logical order. The workspace must hold
@@ -407,7 +409,7 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * out-of-bounds access). With both host copies (lengths and plan) and
  * automatic partitions, split-K partitions are sized for the longest
  * unshared stretch instead of max_context. With the plan's host copy the
- * launch also cuts shared runs into prefix partitions of about 28 blocks
+ * launch also cuts shared runs into prefix partitions of about 32 blocks
  * (never more partitions than the workspace holds); without it, into as
  * many as the workspace holds. The output is the same up to rounding.
  *
