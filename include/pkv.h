@@ -420,7 +420,9 @@ int64_t pkv_decode_workspace_bytes(const pkv_config* cfg, int32_t num_seqs, int3
  * INVALID_ARG: null pointers, ctx_len == 0 or > 16*max_blocks or >
  * max_context (host copy), workspace too small or misaligned,
  * partition_tokens not a multiple of 16, only one of k_new/v_new given.
- * UNSUPPORTED: head_dim/group size not built. */
+ * UNSUPPORTED: head_dim not 64 or 128, or more than 8 query heads per KV
+ * head (groups of 3, 5, 6 or 7 run on the kernels built for 4 and 8, their
+ * extra heads never written). */
 int pkv_paged_decode(const pkv_decode_args* args, void* stream);
 
 /* pkv_paged_decode for callers that cannot allocate device memory (code
@@ -491,8 +493,9 @@ typedef struct pkv_prefill_args {
  * in LDS, refilled as it walks longer contexts.
  * INVALID_ARG: null pointers, q_start not starting at 0 or decreasing,
  * misalignment, a chunk longer than its context or a context out of range
- * (host copies). UNSUPPORTED: group size or head_dim not built. Sequences
- * with qlen_b = 0 are skipped. */
+ * (host copies). UNSUPPORTED: more than 8 query heads per KV head, or
+ * head_dim not 64 or 128 (a query tile holds floor(128 / G) tokens).
+ * Sequences with qlen_b = 0 are skipped. */
 int pkv_paged_prefill(const pkv_prefill_args* args, void* stream);
 
 /* Upload host metadata for the next step (block tables, lengths: the

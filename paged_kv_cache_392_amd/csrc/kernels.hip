@@ -303,6 +303,7 @@ struct DecodeParams {
   float scale_log2;  // softmax scale * log2(e)
   int num_seqs;
   int stream_pad;    // stream-K split: blocks of start-up cost charged ahead of each sequence's span
+  int group;         // query heads per KV head: the kernel's G, or fewer (its last heads are then padding)
 };
 
 __device__ __forceinline__ int clamp_ctx(int ctx, int max_blocks, int max_context) {
@@ -945,11 +946,11 @@ template <int D, int G, bool I8>
 __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int grp, int part, int half) {
   constexpr int NDB = D / 16;
   const int lj = (threadIdx.x & 63) >> 4;
-  const int B = prm.num_seqs, Hq = prm.Hkv * G;
+  const int B = prm.num_seqs, gr = prm.group, Hq = prm.Hkv * gr;  // rows: (member, head of the group)
   const int32_t* gd = prm.plan + 2 * int64_t(B) + int64_t(grp) * PKV_PREFIX_GROUP_INTS;
   const int np = min(gd[0], prm.max_blocks);
   const int members = min(gd[1], PKV_MAX_SHARERS);
-  const int R = min(members * G, PREFIX_ROWS);
+  const int R = min(members * gr, PREFIX_ROWS);
   const int r0 = half * PREFIX_HALF_ROWS;  // this work-group's rows: r0 .. r0 + 63 of the group's
   const int Rh = min(R - r0, PREFIX_HALF_ROWS);
   const int b0 = gd[2];
@@ -957,16 +958,16 @@ __device__ __forceinline__ void prefix_role(const DecodeParams& prm, int g, int 
   const int pbp = prefix_blocks_per_part(np, prm.prefix_pp);  // <= 64: the host sizes prefix_pp
   const int jb = part * pbp, je = min(np, jb + pbp);
   if (jb >= je) return;
-  auto member_of = [&](int r) { return r < Rh ? gd[2 + (r0 + r) / G] : -1; };
+  auto member_of = [&](int r) { return r < Rh ? gd[2 + (r0 + r) / gr] : -1; };
   auto qrow = [&](int r) -> const _Float16* {
     const int bb = member_of(r);
-    return unsigned(bb) < unsigned(B) ? prm.q + (int64_t(bb) * Hq + g * G + (r0 + r) % G) * D : nullptr;
+    return unsigned(bb) < unsigned(B) ? prm.q + (int64_t(bb) * Hq + g * gr + (r0 + r) % gr) * D : nullptr;
   };
   auto no_limit = [](int) { return 0; };
   auto emit = [&](int r, const float4_t (&o)[NDB], float m, float l) {
     const int bb = member_of(r);
     if (unsigned(bb) >= unsigned(B)) return;
-    const int64_t pi = (int64_t(bb) * Hq + g * G + (r0 + r) % G) * prm.max_parts + part;
+    const int64_t pi = (int64_t(bb) * Hq + g * gr + (r0 + r) % gr) * prm.max_parts + part;
 #pragma unroll
     for (int i = 0; i < NDB; ++i)
 #pragma unroll
@@ -1002,6 +1003,7 @@ struct PrefillParams {
   const uint32_t* scales;   // int8: this layer's (K, V) fp16 scales [N][Hkv]; else null
   int Hkv, max_blocks, num_blocks, max_context;
   float scale_log2;
+  int group;  // query heads per KV head (the kernel's G when it has one)
 };
 
 // Causal attention of a chunk of new tokens over the paged cache ([p1] §二
@@ -1021,9 +1023,10 @@ struct PrefillParams {
 template <int D, int G, bool I8>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
   constexpr int NDB = D / 16;
-  constexpr int QT = PREFIX_ROWS / G;  // query tokens per tile
+  const int gr = G > 0 ? G : prm.group;  // G = 0: any group size, taken at run time
+  const int QT = PREFIX_ROWS / gr;       // query tokens per tile
   const int g = blockIdx.x, y = blockIdx.y, b = blockIdx.z;
-  const int Hq = prm.Hkv * G;
+  const int Hq = prm.Hkv * gr;
   const int t0 = prm.q_start[b], ql = prm.q_start[b + 1] - t0;
   const int n = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
   if (ql <= 0 || ql > n) return;
@@ -1033,15 +1036,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams prm) {
   const int passes = 2 * y + 1 < Q ? 2 : 1;
   for (int pass = 0; pass < passes; ++pass) {
     const int i0 = (pass == 0 ? Q - 1 - y : y) * QT;
-    const int cnt = min(QT, ql - i0), R = cnt * G;
+    const int cnt = min(QT, ql - i0), R = cnt * gr;
     const int pos0 = n - ql + i0;  // logical position of the tile's first token
     const int nt = (pos0 + cnt - 1) / BT + 1;
     auto qrow = [&](int r) -> const _Float16* {
-      return r < R ? prm.q + (int64_t(t0 + i0 + r / G) * Hq + g * G + r % G) * D : nullptr;
+      return r < R ? prm.q + (int64_t(t0 + i0 + r / gr) * Hq + g * gr + r % gr) * D : nullptr;
     };
-    auto limit = [&](int r) { return r < R ? pos0 + r / G + 1 : INT_MAX; };
+    auto limit = [&](int r) { return r < R ? pos0 + r / gr + 1 : INT_MAX; };
     auto emit = [&](int r, const float4_t (&o)[NDB], float, float l) {
-      _Float16* dst = prm.out + (int64_t(t0 + i0 + r / G) * Hq + g * G + r % G) * D + 4 * lj;
+      _Float16* dst = prm.out + (int64_t(t0 + i0 + r / gr) * Hq + g * gr + r % gr) * D + 4 * lj;
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) {
@@ -1310,9 +1313,13 @@ __device__ __forceinline__ void segment_loads(const DecodeParams& prm, int g, in
   const int kn = lane & 15, kj = lane >> 4;
   const int jl = jb + wave + WAVES * lane;
   blk_raw = jl < prm.max_blocks ? prm.tables[int64_t(b) * prm.max_blocks + jl] : -1;
-  const _Float16* qh = prm.q + (int64_t(b) * prm.Hkv * G + g * G + kn % G) * D;
+  const int gr = prm.group, h = kn % G;  // heads gr .. G - 1 of the kernel's group are padding (zero q)
+  const _Float16* qh = prm.q + (int64_t(b) * prm.Hkv * gr + g * gr + min(h, gr - 1)) * D;
 #pragma unroll
-  for (int c = 0; c < S::NCH; ++c) qa[c] = *reinterpret_cast<const half8_t*>(qh + S::dim_base(c, kj));
+  for (int c = 0; c < S::NCH; ++c) {
+    const u32x4 w = h < gr ? *reinterpret_cast<const u32x4*>(qh + S::dim_base(c, kj)) : u32x4{0u, 0u, 0u, 0u};
+    qa[c] = __builtin_bit_cast(half8_t, w);
+  }
 }
 
 // One segment of a decode work-group: logical blocks jb .. je - 1 of
@@ -1332,7 +1339,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& prm, int g, i
                                                const half8_t (&qa)[D / 32], float (&p_lds)[WAVES][BT][G],
                                                float (&merge_o)[WAVES][G][D], float (&merge_ml)[WAVES][G][2]) {
   using S = Shape<D, G, I8>;
-  const int Hkv = prm.Hkv, Hq = Hkv * G;
+  const int Hkv = prm.Hkv, gr = prm.group, Hq = Hkv * gr;  // heads gr .. G - 1 are padding
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int kn = lane & 15, kj = lane >> 4;  // score mapping: token, k-slot group
@@ -1581,7 +1588,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& prm, int g, i
   __syncthreads();
 
   // merge the 4 waves (fixed order); write the final row or this partition's partial
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < gr * D; idx += 256) {
     const int h = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
@@ -1594,7 +1601,7 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& prm, int g, i
       L += merge_ml[w][h][1] * wt;
       O += merge_o[w][h][d] * wt;
     }
-    const int64_t row = int64_t(b) * Hq + g * G + h;
+    const int64_t row = int64_t(b) * Hq + g * gr + h;
     if (final_row) {
       prm.out[row * D + d] = (_Float16)(L > 0.0f ? O / L : 0.0f);
     } else {
@@ -1765,8 +1772,8 @@ __global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_de
   const int ctx = clamp_ctx(prm.ctx_lens[b], prm.max_blocks, prm.max_context);
   if (ctx <= 0) {  // rejected on the host when lengths are given; never NaN
     if (p == 0)
-      for (int i = threadIdx.x; i < G * D; i += 256)
-        prm.out[(int64_t(b) * prm.Hkv * G + g * G) * D + i] = _Float16(0.0f);
+      for (int i = threadIdx.x; i < prm.group * D; i += 256)
+        prm.out[(int64_t(b) * prm.Hkv * prm.group + g * prm.group) * D + i] = _Float16(0.0f);
     return;
   }
   const int nblk = (ctx + BT - 1) / BT;
@@ -2141,12 +2148,19 @@ int max_parts_for(int max_context, int part_blocks) {
 
 typedef void (*decode_fn)(DecodeParams);
 
+// A group of G query heads runs on the kernel built for the next size up
+// (3 on 4; 5, 6 and 7 on 8): its extra heads get zero q and are never
+// written, so they cost arithmetic and no bytes.
 template <int D, bool I8, int GRID>
 decode_fn pick_g(int G) {
   switch (G) {
     case 1: return paged_decode_kernel<D, 1, I8, GRID>;
     case 2: return paged_decode_kernel<D, 2, I8, GRID>;
+    case 3:
     case 4: return paged_decode_kernel<D, 4, I8, GRID>;
+    case 5:
+    case 6:
+    case 7:
     case 8: return paged_decode_kernel<D, 8, I8, GRID>;
     default: return nullptr;
   }
@@ -2357,7 +2371,7 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
     return pkv::fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
   const int G = a->num_q_heads / c.num_kv_heads;
   decode_fn fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, a->prefix_groups > 0 ? GRID_PLAN : GRID_PLAIN);
-  if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", G);
+  if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1 to 8)", G);
   if (c.num_kv_heads > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
   if (a->ctx_lens_host) {
     const int64_t cap = std::min<int64_t>(int64_t(a->max_blocks) * BT, a->max_context);
@@ -2550,6 +2564,7 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
   prm.num_seqs = a->num_seqs;
   prm.plan_stream = plan && stream_k ? 1 : 0;
   prm.stream_pad = stream_k ? stream_pad_blocks(c.dtype) : 0;
+  prm.group = G;
   if (stream_k && !plan) fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, GRID_STREAM);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -2655,18 +2670,23 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   typedef void (*fn_t)(PrefillParams);
   fn_t fn = nullptr;
   const bool i8 = c.dtype == PKV_I8;
+  // group sizes 1, 2, 4 and 8 have kernels of their own; 3, 5, 6 and 7 take
+  // theirs at run time (G = 0)
+  const bool own = G == 1 || G == 2 || G == 4 || G == 8, any = G >= 1 && G <= 8;
   if (c.head_dim == 128) {
     fn = G == 1 ? (i8 ? prefill_kernel<128, 1, true> : prefill_kernel<128, 1, false>)
        : G == 2 ? (i8 ? prefill_kernel<128, 2, true> : prefill_kernel<128, 2, false>)
        : G == 4 ? (i8 ? prefill_kernel<128, 4, true> : prefill_kernel<128, 4, false>)
-       : G == 8 ? (i8 ? prefill_kernel<128, 8, true> : prefill_kernel<128, 8, false>) : nullptr;
+       : G == 8 ? (i8 ? prefill_kernel<128, 8, true> : prefill_kernel<128, 8, false>)
+       : any && !own ? (i8 ? prefill_kernel<128, 0, true> : prefill_kernel<128, 0, false>) : nullptr;
   } else if (c.head_dim == 64) {
     fn = G == 1 ? (i8 ? prefill_kernel<64, 1, true> : prefill_kernel<64, 1, false>)
        : G == 2 ? (i8 ? prefill_kernel<64, 2, true> : prefill_kernel<64, 2, false>)
        : G == 4 ? (i8 ? prefill_kernel<64, 4, true> : prefill_kernel<64, 4, false>)
-       : G == 8 ? (i8 ? prefill_kernel<64, 8, true> : prefill_kernel<64, 8, false>) : nullptr;
+       : G == 8 ? (i8 ? prefill_kernel<64, 8, true> : prefill_kernel<64, 8, false>)
+       : any && !own ? (i8 ? prefill_kernel<64, 0, true> : prefill_kernel<64, 0, false>) : nullptr;
   }
-  if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1, 2, 4 or 8)", G);
+  if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1 to 8)", G);
   const int QT = PREFIX_ROWS / G;
   const int qtiles = (max_ql + QT - 1) / QT;
   const int pairs = (qtiles + 1) / 2;  // each work-group takes a long and a short query tile
@@ -2690,6 +2710,7 @@ int pkv_paged_prefill(const pkv_prefill_args* a, void* stream) {
   prm.num_blocks = c.num_blocks;
   prm.max_context = a->max_context;
   prm.scale_log2 = a->scale * LOG2E;
+  prm.group = G;
   hipLaunchKernelGGL(fn, dim3(c.num_kv_heads, pairs, a->num_seqs), dim3(256), 0, static_cast<hipStream_t>(stream),
                      prm);
   return hip_status(hipGetLastError(), "paged_prefill launch");

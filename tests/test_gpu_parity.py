@@ -397,6 +397,36 @@ def test_stream_k_runs_through_start_up_charges(dtype, D):
     lib.close()
 
 
+@pytest.mark.parametrize("seed,Hq,Hkv,D,dtype", [
+    (3101, 6, 2, 128, "f16"),   # 3 q heads per KV head, on the kernels built for 4
+    (3102, 5, 1, 64, "f16"),    # 5, on those built for 8
+    (3103, 12, 2, 128, "f16"),  # 6
+    (3104, 7, 1, 128, "f16"),   # 7
+    (3105, 6, 2, 64, "i8"),
+    (3106, 14, 2, 128, "i8"),
+])
+def test_group_sizes_between_the_built_ones(seed, Hq, Hkv, D, dtype):
+    """Group sizes 3, 5, 6 and 7 run on the decode kernels built for 4 and 8,
+    their extra heads zero-q padding that is never written: host records
+    exact, fp16 stored bytes exact, the stream-K launch (host lengths) and the
+    plain grid (no host lengths) against the oracle."""
+    w = workloads.tiny_random(seed, B=6, Hq=Hq, Hkv=Hkv, D=D, max_len=900, dtype=dtype)
+    lib, o = run_pair(w)
+    check_host_records(lib, o)
+    if dtype == "f16":
+        check_stored_bytes(lib, o)
+    tol = F16_TOL if dtype == "f16" else I8_TOL
+    assert max_err(lib, o) <= tol
+    rec, want = lib.decodes[0], o.decodes[0]["out"]
+    td = torch.from_numpy(rec["tables"]).to(DEV)
+    ld = torch.from_numpy(rec["lens"]).to(DEV)
+    qd = torch.from_numpy(rec["q"]).to(DEV)
+    announce(f"group size {Hq // Hkv} plain grid")
+    plain = lib.cache.paged_decode(qd, td, ld, max_context=rec["tables"].shape[1] * 16).cpu().numpy()
+    assert np.abs(plain.astype(np.float64) - want).max() <= tol
+    lib.close()
+
+
 def test_run_to_run_bitwise_determinism():
     w = workloads.tiny_random(1002, B=4, Hq=32, Hkv=8, D=128, max_len=3000)
     announce("determinism")
@@ -595,6 +625,8 @@ def test_upload_kernel_copies_pinned_host_bytes():
     (44, ((800, 32),), 0, 8, 8, 128, 32),  # 1 per KV head, 32 members
     (45, ((2100, 12), (48, 3)), 1, 8, 1, 64, 16),  # a single KV head, runs of 2 blocks
     (46, ((512, 40),), 2, 32, 8, 128, 32),  # 40 sharers: groups of 32 and 8
+    (47, ((900, 20), (200, 4)), 1, 10, 2, 128, 25),  # 5 q heads per KV head: 25 members are 125 rows
+    (48, ((333, 9),), 2, 6, 2, 64, 32),  # 3 per KV head, d64
 ])
 def test_shared_prefix_plan_matches_oracle(seed, groups, singles, Hq, Hkv, D, max_members):
     w = workloads.prefix_forest(seed, groups=groups, singles=singles, Hq=Hq, Hkv=Hkv, D=D, suffix=(0, 600))
@@ -612,6 +644,7 @@ def test_shared_prefix_plan_matches_oracle(seed, groups, singles, Hq, Hkv, D, ma
 @pytest.mark.parametrize("seed,groups,singles,Hq,Hkv,D", [
     (51, ((700, 6), (333, 3)), 2, 32, 8, 128),
     (52, ((517, 5),), 1, 4, 2, 64),
+    (53, ((700, 6),), 1, 14, 2, 128),  # 7 q heads per KV head
 ])
 def test_shared_prefix_plan_int8(seed, groups, singles, Hq, Hkv, D):
     """A shared-prefix plan on an int8 pool: the prefix work-groups dequantise
@@ -771,6 +804,9 @@ def prefill_err(lib, o):
     (64, [7, 0], [300, 129], 8, 8, 64),  # MHA, d64: 128 tokens per work-group
     (65, [0, 16, 3], [77, 64, 0], 4, 2, 64),  # a sequence with an empty chunk
     (66, [2000], [600], 8, 1, 128),  # MQA after a long cached run
+    (67, [0, 40], [300, 77], 6, 2, 128),  # 3 q heads per KV head: 42 tokens (126 rows) per tile
+    (68, [100], [257], 5, 1, 64),  # 5 per KV head, d64: 25 tokens (125 rows) per tile
+    (69, [0, 33], [129, 64], 14, 2, 128),  # 7 per KV head: 18 tokens (126 rows) per tile
 ])
 def test_prefill_matches_oracle(seed, cached, chunk, Hq, Hkv, D):
     w = workloads.prefill_chunks(seed, cached, chunk, Hq, Hkv, D)
@@ -787,6 +823,7 @@ def test_prefill_matches_oracle(seed, cached, chunk, Hq, Hkv, D):
     (71, [0, 40, 700], [300, 33, 129], 32, 8, 128),  # fresh and chunked, int8 pool
     (72, [5, 0], [100, 64], 8, 2, 64),  # d64: half the threads stage the tiles
     (73, [0], [257], 16, 2, 128),  # 8 q heads per KV head
+    (74, [0, 90], [200, 31], 12, 2, 128),  # 6 q heads per KV head
 ])
 def test_prefill_int8_matches_oracle(seed, cached, chunk, Hq, Hkv, D):
     """Paged prefill over an int8 pool (every token quantised on write): the
