@@ -313,7 +313,7 @@ typedef struct pkv_decode_args {
   int32_t layer;                  /* 0 <= layer < L                               */
   const void* q_dev;              /* fp16 [B][Hq][D]                              */
   int32_t num_seqs;               /* B >= 1                                       */
-  int32_t num_q_heads;            /* Hq, a multiple of Hkv; G = Hq/Hkv in {1,2,4,8} */
+  int32_t num_q_heads;            /* Hq, a multiple of Hkv; G = Hq/Hkv in 1..8     */
   const int32_t* block_tables_dev;/* int32 [B][max_blocks], -1 padded             */
   int32_t max_blocks;             /* row stride of the tables                     */
   const int32_t* ctx_lens_dev;    /* int32 [B], tokens attended (>= 1)            */
@@ -464,7 +464,7 @@ typedef struct pkv_prefill_args {
   const void* q_dev;              /* fp16 [T][Hq][D]: the chunks' queries,
                                      sequence after sequence                     */
   int32_t num_seqs;               /* B, in [1, 65535]                             */
-  int32_t num_q_heads;            /* Hq, a multiple of Hkv; Hq/Hkv in {1,2,4,8}   */
+  int32_t num_q_heads;            /* Hq, a multiple of Hkv; Hq/Hkv in 1..8        */
   const int32_t* q_start_dev;     /* int32 [B + 1]: sequence b's rows of q and out
                                      are q_start[b] .. q_start[b + 1] - 1         */
   const int32_t* q_start_host;    /* the same, on the host: required              */
