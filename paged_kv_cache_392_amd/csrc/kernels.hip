@@ -432,19 +432,24 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
 // 16 bytes per lane from global memory straight into LDS
-// (global_load_lds_dwordx4): lane l's bytes land at lds + 16 l (lds
-// wave-uniform; checked on gfx950 with an in-bounds one-wave probe). Written
-// as asm so that the compiler, which cannot tell which LDS bytes such a load
-// writes, does not wait for every one in flight before each LDS read; the
-// caller orders them itself: vmcnt waits (loads complete in order) before
-// the barrier that hands the bytes to other waves, and before any reuse of
-// the LDS. It has no register outputs; its address is read at issue.
-__device__ __forceinline__ void lds_load16(const char* src, const char* lds) {
+// (global_load_lds_dwordx4): lane l reads base + ofs (base wave-uniform, in
+// SGPRs, so the address costs no vector instruction; ofs the lane's 32-bit
+// offset) and its bytes land at lds + 16 l (lds wave-uniform; checked on
+// gfx950 with an in-bounds one-wave probe). Written as asm so that the
+// compiler, which cannot tell which LDS bytes such a load writes, does not
+// wait for every one in flight before each LDS read; the caller orders them
+// itself: vmcnt waits (loads complete in order) before the barrier that
+// hands the bytes to other waves, and before any reuse of the LDS. It has no
+// register outputs; its operands are read at issue. The s_nop gives the
+// five wait states a vector memory instruction needs after a VALU write of
+// an SGPR it reads (and the one after the M0 write), whatever the compiler
+// placed before the asm.
+__device__ __forceinline__ void lds_load16(const char* base, uint32_t ofs, const char* lds) {
   const uint32_t m0 = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)lds));
-  __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+  __asm__ __volatile__("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
                        :
-                       : "s"(m0), "v"(src)
+                       : "s"(m0), "v"(ofs), "s"(base)
                        : "memory", "m0");
 }
 
@@ -673,21 +678,25 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
     for (int sub = 0; sub < 2; ++sub) {
       const int blk = tile_block(2 * step + sub);
       const int safe = unsigned(blk) < unsigned(num_blocks) ? blk : 0;
-      const int64_t base = (int64_t(safe) * Hkv + g) * TILE + dofs;
-      lds_load16(Kc + base, dma_tile(st, sub) + 1024 * wave);
-      lds_load16(Vc + base, dma_tile(st, 2 + sub) + 1024 * wave);
+      const int64_t base = (int64_t(safe) * Hkv + g) * TILE;
+      lds_load16(Kc + base, dofs, dma_tile(st, sub) + 1024 * wave);
+      lds_load16(Vc + base, dofs, dma_tile(st, 2 + sub) + 1024 * wave);
     }
   };
   // after this wave's loads of `step` have landed: V rows at or past nvalid
   // in the tile that holds the end of the written tokens become zeros
-  // (each lane rewrites the 16 bytes its own load wrote)
+  // (each lane rewrites the 16 bytes its own load wrote). The step test is
+  // uniform (a scalar branch), so steps before the end cost no vector
+  // instruction.
   auto dma_zero_tail = [&](int st, int step) {
     if constexpr (MASK) {
+      if ((jb + 2 * step + 2) * BT > nvalid) {
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int room = nvalid - (jb + 2 * step + sub) * BT;
-        if (room < BT && drow >= room)
-          *reinterpret_cast<uint4*>(dma_tile(st, 2 + sub) + 1024 * wave + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        for (int sub = 0; sub < 2; ++sub) {
+          const int room = nvalid - (jb + 2 * step + sub) * BT;
+          if (drow >= room)
+            *reinterpret_cast<uint4*>(dma_tile(st, 2 + sub) + 1024 * wave + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
     }
   };
