@@ -584,8 +584,11 @@ __device__ __forceinline__ void attend_rows(const char* Kc, const char* Vc, cons
   // operand (every element of ls is the row's sum); otherwise v_dot2 sums
   // per lane, reduced over the four token groups at the end
   float4_t ls0 = {0.0f, 0.0f, 0.0f, 0.0f}, ls1 = {0.0f, 0.0f, 0.0f, 0.0f};
-  const half8_t ones8 = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
-                         (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+  half8_t ones8 = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                   (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+  // held in registers for the whole walk: the compiler would otherwise
+  // rebuild it every step (two vector moves)
+  if constexpr (DMA) __asm__("" : "+v"(ones8));
 
   // Tile staging: a tile is 2 x LOADERS 16-byte pieces (K, then V), each
   // piece along a row; thread t moves pieces t + 256 j (int8 at D = 64: only
