@@ -1560,7 +1560,15 @@ __device__ __forceinline__ void decode_segment(const DecodeParams& prm, int g, i
       load(it + 2, ta);
       compute(first + WAVES * (it + 1), tb);
     }
-    if (it + 1 < n_my) {
+    if constexpr (G == 8) {
+      // one copy of each half of the tail (a uniform branch around the
+      // second): the three-copy tail below would need more than 256 VGPRs
+      // at eight heads
+      const bool two = it + 1 < n_my;
+      if (two) load(it + 1, tb);
+      compute(first + WAVES * it, ta);
+      if (two) compute(first + WAVES * (it + 1), tb);
+    } else if (it + 1 < n_my) {
       load(it + 1, tb);
       compute(first + WAVES * it, ta);
       compute(first + WAVES * (it + 1), tb);
@@ -1737,13 +1745,20 @@ __device__ __forceinline__ void stream_k_role(const DecodeParams& prm, int g, in
 // role, so launches without a plan use GRID_PLAIN, which leaves it out.
 enum { GRID_PLAIN = 0, GRID_STREAM = 1, GRID_PLAN = 2 };
 
-template <bool I8, int D, int G>
+// Work-groups per CU the decode kernels are built for (two waves per SIMD
+// or one). fp16 at eight query heads per KV head holds twice the value
+// accumulators; with its stream's tail written once per half it fits 256
+// VGPRs (219 on the plain grid) and the plain grid runs at two per CU (16 x
+// 8193 tokens, 64 q / 8 KV heads: 88.3-88.5 us against 91.0-91.3 at one).
+// The stream-K and plan grids keep one (the host holds them there with
+// dynamic LDS, see cap_per_cu_lds).
+template <bool I8, int D, int G, int GRID>
 constexpr int decode_wgs_per_cu() {
-  return (I8 || G <= 4) ? 2 : 1;
+  return (I8 || G <= 4 || GRID == GRID_PLAIN) ? 2 : 1;
 }
 
 template <int D, int G, bool I8, int GRID>
-__global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G>())) void paged_decode_kernel(DecodeParams prm) {
+__global__ __launch_bounds__(256, (decode_wgs_per_cu<I8, D, G, GRID>())) void paged_decode_kernel(DecodeParams prm) {
   const int g = blockIdx.x;
   __shared__ float p_lds[WAVES][BT][G];
   __shared__ float merge_o[WAVES][G][D];
@@ -2058,14 +2073,19 @@ Residency resident_wgs(const void* fn, size_t dyn_lds) {
   return known[key] = Residency{per_cu * cus, cus};
 }
 
-// Dynamic LDS (unused by the kernel) that holds an int8 decode launch to two
-// work-groups per CU where registers and static LDS would allow three: the
-// int8 stream is HBM-bound and runs faster with two longer-lived
-// work-groups per CU (measured on MI355X, int8 batch 16 x 8192 tokens, same
-// box: 45.1-45.4 us at two per CU against 47.0-47.2 at three, and 45.9-46.1
-// with the two-per-CU cut on CUs that could take a third). 0 where at most
-// two fit anyway. Per device and kernel.
-size_t two_per_cu_lds(const void* fn) {
+// Dynamic LDS (unused by the kernel) that holds a decode launch to `cap`
+// work-groups per CU where registers and static LDS would allow more:
+//   * int8, cap 2: the int8 stream is HBM-bound and runs faster with two
+//     longer-lived work-groups per CU (measured on MI355X, int8 batch 16 x
+//     8192 tokens, same box: 45.1-45.4 us at two per CU against 47.0-47.2 at
+//     three, and 45.9-46.1 with the two-per-CU cut on CUs that could take a
+//     third);
+//   * fp16 at eight query heads per KV head on the stream-K and plan grids,
+//     cap 1 (their tails fit 256 VGPRs, but two per CU measured no faster:
+//     ragged 16 x U[128, 8193], 64 q / 8 KV heads, 57.1-57.4 us at two
+//     against 56.8-57.1 at one).
+// 0 where at most `cap` fit anyway. Per device and kernel.
+size_t cap_per_cu_lds(const void* fn, int cap) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, size_t> known;
   int dev = 0;
@@ -2077,14 +2097,21 @@ size_t two_per_cu_lds(const void* fn) {
   size_t extra = 0;
   int per_cu = 0, lds_cu = 0;
   hipFuncAttributes attr;
-  if (dev >= 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) == hipSuccess && per_cu > 2 &&
+  if (dev >= 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) == hipSuccess && per_cu > cap &&
       hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
       hipFuncGetAttributes(&attr, fn) == hipSuccess) {
-    const size_t want = size_t(lds_cu) / 3 + 1024;  // a third work-group no longer fits
+    const size_t want = size_t(lds_cu) / (cap + 1) + 1024;  // work-group cap + 1 no longer fits
     if (want > attr.sharedSizeBytes) extra = want - attr.sharedSizeBytes;
   }
   (void)hipGetLastError();  // a failed query above must not be reported by the launch
   return known[key] = extra;
+}
+
+// The dynamic LDS of a decode launch of kernel fn (built for kg query heads
+// per KV head, on `grid`).
+size_t decode_dyn_lds(const void* fn, bool i8, int kg, int grid) {
+  if (i8) return cap_per_cu_lds(fn, 2);
+  return kg == 8 && grid != GRID_PLAIN ? cap_per_cu_lds(fn, 1) : 0;
 }
 
 // Blocks per partition for one launch. Each partition is one work-group and
@@ -2382,6 +2409,7 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
   if (a->k_new_dev && (!aligned16(a->k_new_dev) || !aligned16(a->v_new_dev)))
     return pkv::fail(PKV_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
   const int G = a->num_q_heads / c.num_kv_heads;
+  const int kg = G <= 2 ? G : G <= 4 ? 4 : 8;  // the group size the kernel is built for
   decode_fn fn = pick_kernel(c.head_dim, G, c.dtype == PKV_I8, a->prefix_groups > 0 ? GRID_PLAN : GRID_PLAIN);
   if (!fn) return pkv::fail(PKV_ERR_UNSUPPORTED, "group size %d not built (1 to 8)", G);
   if (c.num_kv_heads > 65535) return pkv::fail(PKV_ERR_UNSUPPORTED, "too many KV heads");
@@ -2465,7 +2493,8 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
       auto span = [&](int b) { return lens ? int((std::min<int64_t>(lens[b], cap) + BT - 1) / BT) : cap_blocks; };
       pb = launch_part_blocks(c.num_kv_heads, a->num_seqs, span,
                               resident_wgs(reinterpret_cast<const void*>(fn),
-                                           c.dtype == PKV_I8 ? two_per_cu_lds(reinterpret_cast<const void*>(fn)) : 0),
+                                           decode_dyn_lds(reinterpret_cast<const void*>(fn), c.dtype == PKV_I8, kg,
+                                                          plan ? GRID_PLAN : GRID_PLAIN)),
                               (cap_blocks + mp0 - 1) / mp0);
       gparts = std::min(mp0, (cap_blocks + pb - 1) / pb);
     } else if (a->ctx_lens_host && a->prefix_plan_host) {
@@ -2516,8 +2545,10 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
       T += nb > 0 ? nb + pad : 0;
     }
     if ((plan || pairs < int64_t(a->num_seqs) * gparts) && T > 0) {
-      const Residency res = resident_wgs(reinterpret_cast<const void*>(fn),
-                                         c.dtype == PKV_I8 ? two_per_cu_lds(reinterpret_cast<const void*>(fn)) : 0);
+      // the residency of the kernel that will run the cut (the stream-K one without a plan)
+      const void* sk = plan ? reinterpret_cast<const void*>(fn)
+                            : reinterpret_cast<const void*>(pick_kernel(c.head_dim, G, c.dtype == PKV_I8, GRID_STREAM));
+      const Residency res = resident_wgs(sk, decode_dyn_lds(sk, c.dtype == PKV_I8, kg, plan ? GRID_PLAN : GRID_STREAM));
       const int64_t slots_h = std::max<int64_t>(1, res.slots / c.num_kv_heads - units);
       int64_t q = (T + slots_h - 1) / slots_h;
       q = std::min<int64_t>(std::max<int64_t>(q, MIN_PART_BLOCKS), MAX_PARTITION_TOKENS / BT);
@@ -2590,7 +2621,8 @@ int paged_decode_impl(const pkv_decode_args* a, void* stream, void* ws_dev, int6
   const int cy = int(std::min<int64_t>(lin, 65535));
   const dim3 grid = stream_k ? dim3(c.num_kv_heads, cy, unsigned((lin + cy - 1) / cy))
                              : dim3(c.num_kv_heads, a->num_seqs, pz + gparts);
-  const size_t dyn_lds = c.dtype == PKV_I8 ? two_per_cu_lds(reinterpret_cast<const void*>(fn)) : 0;
+  const size_t dyn_lds = decode_dyn_lds(reinterpret_cast<const void*>(fn), c.dtype == PKV_I8, kg,
+                                        plan ? GRID_PLAN : (stream_k ? GRID_STREAM : GRID_PLAIN));
   if (ev[0] && ev[1])
     hipExtLaunchKernelGGL(fn, grid, dim3(256), dyn_lds, s, ev[0], ev[1], 0, prm);
   else
