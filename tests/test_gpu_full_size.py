@@ -94,6 +94,18 @@ def test_continuous_batching_mix_stream_k(dtype):
     lib.close()
 
 
+def test_gqa8_ragged_stream_k():
+    """64 q / 8 KV heads (G = 8) over the continuous-batching mix's ragged
+    lengths, fp16: the stream-K split of the eight-head kernel, which the
+    launch holds at one work-group per CU; all 1024 rows."""
+    w = workloads.c3_mixed(seed=63, Hq=64)
+    announce("G=8 ragged 16 x U[128, 8192] + 1, fp16, stream-K split")
+    lib, o, err = compare_all_rows(w, F16_TOL)
+    announce(f"G=8 ragged max abs err {err:.3g}")
+    assert err <= F16_TOL
+    lib.close()
+
+
 def test_two_rounds_of_work_groups_32x8193():
     """32 sequences at 8192 + 1 tokens: more partitions than the device holds
     at once (two rounds of work-groups); all 1024 rows."""

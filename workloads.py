@@ -146,16 +146,17 @@ def c2_llama_b8(seed=2):
     return w
 
 
-def c3_mixed(seed=3, batch=16, churn_requests=200, dtype="f16"):
+def c3_mixed(seed=3, batch=16, churn_requests=200, dtype="f16", Hq=32):
     """Continuous-batching mix: 16 sequences of U[128, 8192] tokens, pool
     scrambled by 200 earlier requests of U[1, 8192] tokens. ``dtype="i8"``:
-    the same draws, stored block-quantised as int8."""
+    the same draws, stored block-quantised as int8. ``Hq`` query heads over
+    the 8 KV heads (32 by default)."""
     rng = np.random.default_rng(seed)
     N = 16 * 513
     churn = Churn(lengths=rng.integers(1, 8193, churn_requests),
                   uniforms=rng.random(8 * churn_requests + 64))
     lens = rng.integers(128, 8193, batch).tolist()
-    w = Workload("c3_mixed", N, 32, 8, 128, dtype, np.arange(N, dtype=np.int32))
+    w = Workload("c3_mixed", N, Hq, 8, 128, dtype, np.arange(N, dtype=np.int32))
     w.steps.append(("churn", churn))
     names = [f"s{i}" for i in range(batch)]
     for s in names:
@@ -163,7 +164,7 @@ def c3_mixed(seed=3, batch=16, churn_requests=200, dtype="f16"):
     for s, n in zip(names, lens):
         w.steps.append(("prefill", s, _normal(rng, (n, 8, 128)), _normal(rng, (n, 8, 128))))
     w.steps.append(("append", names, _normal(rng, (batch, 8, 128)), _normal(rng, (batch, 8, 128))))
-    w.steps.append(("decode", names, _normal(rng, (batch, 32, 128))))
+    w.steps.append(("decode", names, _normal(rng, (batch, Hq, 128))))
     w.seed = seed
     return w
 
