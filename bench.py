@@ -920,7 +920,8 @@ def prefix_decode_bench(args, torch, pkv, C, workloads):
 
 def prefill_bench(args, torch, pkv, C, workloads):
     """Prefill step: 4 fresh prompts of 2048 tokens, 32 q / 8 KV heads, d128,
-    fp16, over 32 layer pools. Per layer the prompts' K/V rows are appended
+    fp16 (or int8 pools with ``--dtype i8``: the append quantises on write),
+    over 32 layer pools. Per layer the prompts' K/V rows are appended
     into their blocks (one bulk append of 8192 tokens) and attended
     causally (one prefill launch). The blocks come from the library's
     allocator in a seeded random order; K, V and q are seeded device noise
@@ -932,7 +933,8 @@ def prefill_bench(args, torch, pkv, C, workloads):
     nblk = T // 16
     N = Bp * nblk
     order = np.random.default_rng(7).permutation(N).astype(np.int32)
-    cache = pkv.PagedKVCache(L, N, HKV, D, "f16", order, dev)
+    dt = args.dtype
+    cache = pkv.PagedKVCache(L, N, HKV, D, dt, order, dev)
     lib = C.load()
     sp = torch.cuda.current_stream().cuda_stream
     gen = torch.Generator(device=dev)
@@ -994,16 +996,17 @@ def prefill_bench(args, torch, pkv, C, workloads):
     flops = 4.0 * HQ * D * Bp * (T * (T + 1) / 2)
     achieved = flops / (float(np.mean(pre)) * 1e-6) / 1e12
     print(json.dumps({
-        "metric": "paged prefill tokens/s (4 x 2048-token prompts, causal, 32q/8kv d128 fp16)",
+        "metric": f"paged prefill tokens/s (4 x 2048-token prompts, causal, 32q/8kv d128 {'fp16' if dt == 'f16' else 'int8 pool'})",
         "value": round(Bp * T / (ms * 1e-3), 1), "unit": "tok/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16", "data": "synthetic",
+        "dtype": dt, "data": "synthetic",
         "config": {"workload": f"prefill step: {Bp} fresh prompts of {T} tokens appended into 16-token blocks "
-                               f"and attended causally, 32 q / 8 KV heads, head_dim 128, fp16, {L} layer pools",
+                               f"and attended causally, 32 q / 8 KV heads, head_dim 128, "
+                               f"{'fp16' if dt == 'f16' else 'int8 pool (quantised on append)'}, {L} layer pools",
                    "layers": L},
         "prefill_kernel_us": round(float(np.mean(pre)), 2),
         "prefill_kernel_us_p10_p90": [round(float(np.percentile(pre, 10)), 2), round(float(np.percentile(pre, 90)), 2)],
-        "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,4> (causal paged prefill)",
+        "roofline": {"bound": "mfma", "kernel": f"prefill_kernel<128,4,{'f16' if dt == 'f16' else 'i8'}> (causal paged prefill)",
                      "achieved": round(achieved, 1), "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_F16_MFMA_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": flops},
