@@ -799,7 +799,7 @@ def prefix_decode_bench(args, torch, pkv, C, workloads):
     tables_h, lens_h = cache.block_tables(seqs)
     max_blocks = tables_h.shape[1]
     ctx = int(lens_h.max())
-    plan = cache.plan_shared_prefix(seqs)
+    plan = cache.plan_shared_prefix(seqs, num_q_heads=HQ)
     tables_d = torch.from_numpy(tables_h).to(dev)
     lens_d = torch.from_numpy(lens_h).to(dev)
     q = torch.empty((L, nseq, HQ, D), dtype=torch.float16, device=dev).normal_(generator=gen)

@@ -79,6 +79,8 @@ def _dev_i32(a, device):
     t = torch.from_numpy(np.ascontiguousarray(a, np.int32))
     if t.numel() == 0:
         return torch.empty(t.shape, dtype=torch.int32, device=device)
+    if torch.device(device).type == "cpu":  # a host cache (host-side calls only): no pinned staging
+        return t.clone()
     return t.pin_memory().to(device, non_blocking=True)
 
 
@@ -318,10 +320,22 @@ class PagedKVCache:
         C.pkv_paged_prefill(a, _stream())
         return out
 
-    def plan_shared_prefix(self, seqs, min_blocks=1, max_members=C.PKV_MAX_SHARERS):
+    def plan_shared_prefix(self, seqs, min_blocks=1, max_members=None, num_q_heads=None):
         """Group the batch's sequences that share leading blocks so one decode
         reads those blocks once for all of them (the plan is tied to this
-        order of ``seqs`` and to the current block tables)."""
+        order of ``seqs`` and to the current block tables). A decode takes
+        groups of at most 128 query rows (members x query heads per KV head):
+        give the decode's ``num_q_heads`` and groups hold at most
+        ``128 // (num_q_heads // num_kv_heads)`` members (and at most 32);
+        else ``max_members`` (default 32, right up to 4 heads per KV head)."""
+        if max_members is None:
+            max_members = C.PKV_MAX_SHARERS
+            if num_q_heads is not None:
+                if num_q_heads < 1 or num_q_heads % self.num_kv_heads:
+                    raise ValueError(f"num_q_heads {num_q_heads} is not a multiple of {self.num_kv_heads}")
+                max_members = min(max_members, 128 // (num_q_heads // self.num_kv_heads))
+        elif num_q_heads is not None:
+            raise ValueError("give max_members or num_q_heads, not both")
         host, ng = C.pkv_plan_shared_prefix(self.handle, seqs, min_blocks, max_members)
         return PrefixPlan(host, ng, len(seqs), self.device)
 

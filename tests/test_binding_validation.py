@@ -103,3 +103,24 @@ def test_append_kv_rejects_a_sequence_named_twice(cache):
     # refused before any reservation: the allocator is untouched
     assert cache.num_free() == free
     assert cache.seq_len(a) == 0 and cache.seq_len(b) == 0
+
+
+def test_plan_members_follow_the_query_heads():
+    """A decode's shared-prefix work-groups hold 128 query rows: planned with
+    the decode's query heads, groups hold at most 128 // G members (32 at
+    most); planned without them, 32."""
+    c = pkv.PagedKVCache(1, 256, 2, 64, device="cpu")
+    root = c.create_seq()
+    c.reserve([root], [48])  # three full shared blocks
+    seqs = [root] + [c.fork(root) for _ in range(39)]
+    c.reserve(seqs, [5] * len(seqs))  # a private tail block each
+    sizes = lambda plan: sorted(len(members) for _, members in plan.groups())
+    assert sizes(c.plan_shared_prefix(seqs)) == [8, 32]
+    assert sizes(c.plan_shared_prefix(seqs, num_q_heads=16)) == [8, 16, 16]  # G = 8
+    assert sizes(c.plan_shared_prefix(seqs, num_q_heads=10)) == [15, 25]  # G = 5
+    assert sizes(c.plan_shared_prefix(seqs, max_members=20)) == [20, 20]
+    with pytest.raises(ValueError):
+        c.plan_shared_prefix(seqs, num_q_heads=3)
+    with pytest.raises(ValueError):
+        c.plan_shared_prefix(seqs, max_members=8, num_q_heads=16)
+    c.close()
