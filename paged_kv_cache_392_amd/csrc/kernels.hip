@@ -1745,16 +1745,18 @@ __device__ __forceinline__ void stream_k_role(const DecodeParams& prm, int g, in
 // role, so launches without a plan use GRID_PLAIN, which leaves it out.
 enum { GRID_PLAIN = 0, GRID_STREAM = 1, GRID_PLAN = 2 };
 
-// Work-groups per CU the decode kernels are built for (two waves per SIMD
-// or one). fp16 at eight query heads per KV head holds twice the value
-// accumulators; with its stream's tail written once per half it fits 256
-// VGPRs (219 on the plain grid) and the plain grid runs at two per CU (16 x
-// 8193 tokens, 64 q / 8 KV heads: 88.3-88.5 us against 91.0-91.3 at one).
-// The stream-K and plan grids keep one (the host holds them there with
-// dynamic LDS, see cap_per_cu_lds).
+// Work-groups per CU the decode kernels are built for (two waves per SIMD,
+// at most 256 VGPRs, or one). fp16 at eight query heads per KV head holds
+// twice the value accumulators; with its stream's tail written once per
+// half it fits 256 VGPRs (219 on the plain grid, 234 plan), and two per CU
+// beat one: 16 x 8193 tokens, 64 q / 8 KV heads, 88.3-88.5 us against
+// 91.0-91.3; the shared-prefix launch over 32 members of a 2048-token
+// prefix at 64 q / 8 KV heads, 27.5-27.7 us against 40.4-40.7. Its
+// stream-K grid measured no faster at two and is built for one (241 VGPRs)
+// and held there by the host (see cap_per_cu_lds).
 template <bool I8, int D, int G, int GRID>
 constexpr int decode_wgs_per_cu() {
-  return (I8 || G <= 4 || GRID == GRID_PLAIN) ? 2 : 1;
+  return (I8 || G <= 4 || GRID != GRID_STREAM) ? 2 : 1;
 }
 
 template <int D, int G, bool I8, int GRID>
@@ -2080,10 +2082,9 @@ Residency resident_wgs(const void* fn, size_t dyn_lds) {
 //     8192 tokens, same box: 45.1-45.4 us at two per CU against 47.0-47.2 at
 //     three, and 45.9-46.1 with the two-per-CU cut on CUs that could take a
 //     third);
-//   * fp16 at eight query heads per KV head on the stream-K and plan grids,
-//     cap 1 (their tails fit 256 VGPRs, but two per CU measured no faster:
-//     ragged 16 x U[128, 8193], 64 q / 8 KV heads, 57.1-57.4 us at two
-//     against 56.8-57.1 at one).
+//   * fp16 at eight query heads per KV head on the stream-K grid, cap 1
+//     (two per CU measured no faster: ragged 16 x U[128, 8193], 64 q / 8 KV
+//     heads, 57.1-57.4 us at two against 56.8-57.1 at one).
 // 0 where at most `cap` fit anyway. Per device and kernel.
 size_t cap_per_cu_lds(const void* fn, int cap) {
   static std::mutex mu;
@@ -2111,7 +2112,7 @@ size_t cap_per_cu_lds(const void* fn, int cap) {
 // per KV head, on `grid`).
 size_t decode_dyn_lds(const void* fn, bool i8, int kg, int grid) {
   if (i8) return cap_per_cu_lds(fn, 2);
-  return kg == 8 && grid != GRID_PLAIN ? cap_per_cu_lds(fn, 1) : 0;
+  return kg == 8 && grid == GRID_STREAM ? cap_per_cu_lds(fn, 1) : 0;
 }
 
 // Blocks per partition for one launch. Each partition is one work-group and
