@@ -70,6 +70,7 @@ def parse():
                     help="shape workload: comma-separated context lengths, one per sequence")
     ap.add_argument("--q-heads", type=int, default=32, help="shape workload")
     ap.add_argument("--kv-heads", type=int, default=8, help="shape workload")
+    ap.add_argument("--head-dim", type=int, choices=[64, 128], default=128, help="shape workload")
     ap.add_argument("--dtype", choices=["f16", "i8"], default="f16",
                     help="headline: the element type of the 32 layer pools (i8: the same step on int8 K/V, "
                          "each new token quantised on write inside the decode launch); shape workload")
@@ -746,6 +747,8 @@ def c3_decode_bench(args, torch, pkv, C, workloads):
 
 def shape_decode_bench(args, torch, pkv, C, workloads):
     """Decode-only step of any shape given on the command line."""
+    global D
+    D = args.head_dim
     if args.seed is None:
         args.seed = 7
     if args.context_list:
@@ -762,7 +765,7 @@ def shape_decode_bench(args, torch, pkv, C, workloads):
             + (f"{args.context_list} tokens" if args.context_list
                else f"U[{args.lengths[0]}, {args.lengths[1]}] tokens (seed {args.seed})" if args.lengths
                else f"{args.context} tokens")
-            + f", {args.q_heads} q heads / {args.kv_heads} KV heads, head_dim 128, {args.dtype}, "
+            + f", {args.q_heads} q heads / {args.kv_heads} KV heads, head_dim {D}, {args.dtype}, "
             f"{args.layers} layer pools")
     decode_only_bench(args, torch, pkv, C, lens, args.q_heads, args.kv_heads, args.dtype, order, args.seed,
                       f"paged decode HBM GB/s (% of peak), {args.dtype}, decode-only shape", desc)
